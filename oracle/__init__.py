@@ -1,0 +1,261 @@
+"""CPU oracle for the routed MoE FFN over GGUF block-quantized experts.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(``quantized_moe_ffn_amd``) never imports it, and the two share no code.
+
+This module is argument marshalling (numpy <-> ctypes) around ``moe_oracle.c``,
+which holds every step of the arithmetic.  The C file is built with gcc into
+``liboracle.so`` next to it (no fast-math, no FP contraction).
+
+Every function states the passage of the pages it follows; the pages name the
+method (routed top-k MoE, Q4_K / Q8_0 experts, SiLU-gated FFN, shared expert)
+without printing its equations, and the readings taken are listed at the top of
+``moe_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+Q8_0 = 8
+Q4_K = 12
+BLOCK_WEIGHTS = {Q4_K: 256, Q8_0: 32}
+BLOCK_BYTES = {Q4_K: 144, Q8_0: 34}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile moe_oracle.c with gcc (OpenMP, no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+               "-shared", "-Wall", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.orc_threads.restype = ctypes.c_int
+    lib.orc_fp16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.orc_fp16_to_f64.restype = ctypes.c_double
+    lib.orc_q4k_unpack.argtypes = [P, P, P, P, P, P]
+    lib.orc_q4k_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16, P, P, P, P]
+    lib.orc_q4k_dequant.argtypes = [P, i64, P]
+    lib.orc_q80_dequant.argtypes = [P, i64, P]
+    lib.orc_route_topk.argtypes = [P, i32, i32, i32, i32, P, P]
+    lib.orc_bucket.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+    lib.orc_quant_act_f32.argtypes = [P, i32, i32, P, P]
+    lib.orc_silu.argtypes = [ctypes.c_double]
+    lib.orc_silu.restype = ctypes.c_double
+    lib.orc_expert_ffn.argtypes = [P, P, P, i32, i32, i32, i64, i64, i64, i32, i32, i32,
+                                   P, P, i32, P, P]
+    lib.orc_combine.argtypes = [P, P, P, P, i32, i32, i32, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def threads() -> int:
+    """Number of OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_threads())
+
+
+def fp16_to_f64(bits) -> np.ndarray:
+    """IEEE binary16 bit patterns -> exact fp64 values (scale fields of both formats)."""
+    lib = _load()
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.orc_fp16_to_f64(int(v)) for v in b], dtype=np.float64)
+
+
+def q4k_unpack(block) -> dict:
+    """One 144-byte Q4_K super-block -> its fields (d, dmin bits; sc[8]; m[8]; q[256])."""
+    lib = _load()
+    blk = np.ascontiguousarray(np.frombuffer(bytes(block), dtype=np.uint8))
+    assert blk.size == 144
+    d = np.zeros(1, np.uint16)
+    dm = np.zeros(1, np.uint16)
+    sc = np.zeros(8, np.int32)
+    m = np.zeros(8, np.int32)
+    q = np.zeros(256, np.int32)
+    lib.orc_q4k_unpack(_ptr(blk), _ptr(d), _ptr(dm), _ptr(sc), _ptr(m), _ptr(q))
+    return {"d_bits": int(d[0]), "dmin_bits": int(dm[0]), "sc": sc, "m": m, "q": q}
+
+
+def q4k_pack(d_bits, dmin_bits, sc, m, q) -> np.ndarray:
+    """Fields -> one 144-byte Q4_K super-block (inverse of ``q4k_unpack``)."""
+    lib = _load()
+    sc = np.ascontiguousarray(sc, dtype=np.int32)
+    m = np.ascontiguousarray(m, dtype=np.int32)
+    q = np.ascontiguousarray(q, dtype=np.int32)
+    out = np.zeros(144, np.uint8)
+    lib.orc_q4k_pack(int(d_bits), int(dmin_bits), _ptr(sc), _ptr(m), _ptr(q), _ptr(out))
+    return out
+
+
+def q4k_dequant(blocks) -> np.ndarray:
+    """Q4_K blocks (uint8, any shape ending in a multiple of 144 bytes) -> fp64 weights."""
+    lib = _load()
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).ravel()
+    assert b.size % 144 == 0
+    n = b.size // 144
+    out = np.zeros(n * 256, np.float64)
+    lib.orc_q4k_dequant(_ptr(b), n, _ptr(out))
+    return out
+
+
+def q80_dequant(blocks) -> np.ndarray:
+    """Q8_0 blocks (uint8, a multiple of 34 bytes) -> fp64 weights."""
+    lib = _load()
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).ravel()
+    assert b.size % 34 == 0
+    n = b.size // 34
+    out = np.zeros(n * 32, np.float64)
+    lib.orc_q80_dequant(_ptr(b), n, _ptr(out))
+    return out
+
+
+def dequant(blocks, qtype: int) -> np.ndarray:
+    return q4k_dequant(blocks) if qtype == Q4_K else q80_dequant(blocks)
+
+
+def route_topk(logits, k: int, renorm: bool = True):
+    """Top-k expert selection + routing weights, fp64 weights (readings R-topk, R-softmax)."""
+    lib = _load()
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    assert lg.ndim == 2 and np.all(np.isfinite(lg)), "the oracle takes finite logits only"
+    T, E = lg.shape
+    assert 1 <= k <= E
+    idx = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float64)
+    lib.orc_route_topk(_ptr(lg), T, E, k, int(bool(renorm)), _ptr(idx), _ptr(w))
+    return idx, w
+
+
+def bucket(idx, E: int) -> dict:
+    """Per-expert bucketing of (token, slot) pairs, stable in pair id."""
+    lib = _load()
+    ix = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = ix.shape
+    assert ix.min() >= 0 and ix.max() < E
+    count = np.zeros(E, np.int32)
+    offset = np.zeros(E + 1, np.int32)
+    pair = np.zeros(T * k, np.int32)
+    active = np.zeros(max(1, min(E, T * k)), np.int32)
+    na = np.zeros(1, np.int32)
+    lib.orc_bucket(_ptr(ix), T, k, E, _ptr(count), _ptr(offset), _ptr(pair), _ptr(active), _ptr(na))
+    return {"count": count, "offset": offset, "pair": pair,
+            "active": active[: int(na[0])].copy(), "n_active": int(na[0])}
+
+
+def quantize_act(x):
+    """Per-token, per-256-block int8 activation quantisation evaluated in IEEE fp32."""
+    lib = _load()
+    xa = np.ascontiguousarray(x, dtype=np.float32)
+    T, H = xa.shape
+    assert H % 256 == 0
+    xq = np.zeros((T, H), np.int8)
+    xd = np.zeros((T, H // 256), np.float32)
+    lib.orc_quant_act_f32(_ptr(xa), T, H, _ptr(xq), _ptr(xd))
+    return xq, xd
+
+
+def silu(g: float) -> float:
+    return float(_load().orc_silu(float(g)))
+
+
+def expert_ffn(gate, up, down, qtypes, H: int, I: int, pair_expert, pair_token, x,
+               mode: int = 0) -> np.ndarray:
+    """Expert FFN for each (expert, token) pair, fp64 (reading R-ffn).
+
+    gate/up: uint8 [n_experts, I, row_bytes(H)]; down: uint8 [n_experts, H, row_bytes(I)].
+    qtypes = (gate, up, down) qtype ids.  mode 0 = fp activations; mode 1 = the
+    int8 path's quantisation points (x per token, h per pair, 256-wide blocks).
+    Returns y [n_pairs, H] fp64.
+    """
+    lib = _load()
+    g = np.ascontiguousarray(gate, dtype=np.uint8)
+    u = np.ascontiguousarray(up, dtype=np.uint8)
+    d = np.ascontiguousarray(down, dtype=np.uint8)
+    qg, qu, qd = qtypes
+    assert g.shape[1] == I and u.shape[1] == I and d.shape[1] == H
+    assert g.shape[2] == H // BLOCK_WEIGHTS[qg] * BLOCK_BYTES[qg]
+    assert u.shape[2] == H // BLOCK_WEIGHTS[qu] * BLOCK_BYTES[qu]
+    assert d.shape[2] == I // BLOCK_WEIGHTS[qd] * BLOCK_BYTES[qd]
+    pe = np.ascontiguousarray(pair_expert, dtype=np.int32)
+    pt = np.ascontiguousarray(pair_token, dtype=np.int32)
+    xa = np.ascontiguousarray(x, dtype=np.float32)
+    assert xa.shape[1] == H
+    assert pe.size == 0 or (pe.min() >= 0 and pe.max() < g.shape[0])
+    assert pt.size == 0 or (pt.min() >= 0 and pt.max() < xa.shape[0])
+    n = pe.size
+    y = np.zeros((n, H), np.float64)
+    if n:
+        lib.orc_expert_ffn(_ptr(g), _ptr(u), _ptr(d), qg, qu, qd,
+                           g.shape[1] * g.shape[2], u.shape[1] * u.shape[2], d.shape[1] * d.shape[2],
+                           H, I, n, _ptr(pe), _ptr(pt), int(mode), _ptr(xa), _ptr(y))
+    return y
+
+
+def combine(y_pair, w, y_shared=None, shared_scale=None) -> np.ndarray:
+    """Routing-weighted combine in slot order, plus the shared expert (reading R-combine)."""
+    lib = _load()
+    wa = np.ascontiguousarray(w, dtype=np.float64)
+    T, k = wa.shape
+    yp = np.ascontiguousarray(y_pair, dtype=np.float64)
+    H = yp.shape[1]
+    assert yp.shape[0] == T * k
+    ys = None if y_shared is None else np.ascontiguousarray(y_shared, dtype=np.float64)
+    ss = None if shared_scale is None else np.ascontiguousarray(shared_scale, dtype=np.float64)
+    out = np.zeros((T, H), np.float64)
+    lib.orc_combine(_ptr(yp), _ptr(wa), None if ys is None else _ptr(ys),
+                    None if ss is None else _ptr(ss), T, k, H, _ptr(out))
+    return out
+
+
+def moe_layer(logits, x, gate, up, down, qtypes, k: int, renorm: bool = True, mode: int = 0,
+              shared=None, shared_qtypes=None, shared_scale=None) -> dict:
+    """The whole hot path for one layer: route -> bucket -> expert FFN -> combine.
+
+    ``gate/up/down`` hold every expert the routing may touch, indexed by expert id.
+    ``shared`` = (gate, up, down) arrays with a leading dimension of 1, or None.
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    T, E = logits.shape
+    H = x.shape[1]
+    I = gate.shape[1]
+    idx, w = route_topk(logits, k, renorm)
+    b = bucket(idx, E)
+    pair_expert = idx.reshape(-1)
+    pair_token = np.repeat(np.arange(T, dtype=np.int32), k)
+    y_pair = expert_ffn(gate, up, down, qtypes, H, I, pair_expert, pair_token, x, mode)
+    y_sh = None
+    if shared is not None:
+        sg, su, sd = shared
+        y_sh = expert_ffn(sg, su, sd, shared_qtypes or qtypes, H, I,
+                          np.zeros(T, np.int32), np.arange(T, dtype=np.int32), x, mode)
+    out = combine(y_pair, w, y_sh, shared_scale)
+    res = {"idx": idx, "w": w, "y_pair": y_pair, "y_shared": y_sh, "out": out}
+    res.update(b)
+    return res

@@ -1,0 +1,161 @@
+"""Pins for the oracle's expert FFN and combine (CPU only).
+
+The pages name the SiLU-gated expert FFN only implicitly (Qwen-family MoE on the
+"Strata-Sage-A1.5-GGUF" card; 10 routed + 1 shared on the "Strata: a 125B MoE
+at 94 tok/s" article), so the oracle's FFN is pinned by constructions whose
+result is known in closed form (integer-exact layers where silu(g) = g exactly),
+by unit vectors that pick single weight columns, by scipy's logistic function,
+by a brute-force numpy evaluation on tiny shapes, and by invariants of the
+combine (one-hot weights, identical experts, relabelling, batch invariance).
+"""
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+from quantized_moe_ffn_amd import synth
+
+Q4K, Q80 = oracle.Q4_K, oracle.Q8_0
+
+
+def _q4k_rows(rows, cols, q_of_row, sc=1, m=0, d_bits=0x3C00, dmin_bits=0x0000):
+    """A Q4_K matrix whose row r has every quant equal to q_of_row(r)."""
+    nb = cols // 256
+    out = np.zeros((rows, nb * 144), np.uint8)
+    for r in range(rows):
+        blk = oracle.q4k_pack(d_bits, dmin_bits, np.full(8, sc), np.full(8, m), np.full(256, q_of_row(r)))
+        out[r] = np.tile(blk, nb)
+    return out
+
+
+def _dense(mat, qtype, cols):
+    return oracle.dequant(mat, qtype).reshape(mat.shape[0], cols)
+
+
+def test_silu_vs_scipy():
+    for g in [-800.0, -40.0, -3.5, -1e-3, 0.0, 1e-3, 0.7, 5.0, 36.0, 40.0, 900.0]:
+        assert oracle.silu(g) == pytest.approx(g * expit(g), rel=1e-15, abs=1e-300)
+    assert oracle.silu(40.0) == 40.0            # 1 + e^-40 rounds to 1 in fp64
+
+
+@pytest.mark.parametrize("H,I", [(256, 256), (512, 768)])
+def test_integer_exact_ffn_closed_form(H, I):
+    """Gate rows all 1, up row i all (i mod 16), down row o all (o mod 16), x = 1:
+    g = H (so silu(g) = g exactly), u_i = H*(i mod 16), h_i = H^2 (i mod 16),
+    y_o = (o mod 16) * H^2 * sum_i (i mod 16)."""
+    gate = _q4k_rows(I, H, lambda r: 1)[None]
+    up = _q4k_rows(I, H, lambda r: r % 16)[None]
+    down = _q4k_rows(H, I, lambda r: r % 16)[None]
+    x = np.ones((1, H), np.float32)
+    y = oracle.expert_ffn(gate, up, down, (Q4K, Q4K, Q4K), H, I, [0], [0], x, mode=0)
+    s = sum(i % 16 for i in range(I))
+    expect = np.array([(o % 16) * H * H * s for o in range(H)], np.float64)
+    assert np.array_equal(y[0], expect)
+
+
+def test_unit_vector_picks_columns():
+    """x = e_c makes g and u the c-th column of the dequantized gate/up matrices."""
+    H, I = 512, 256
+    g = synth.rng(21)
+    gate = synth.bank_np(g, Q4K, 1, I, H)
+    up = synth.bank_np(g, Q4K, 1, I, H)
+    down = synth.bank_np(g, Q4K, 1, H, I)
+    Wg, Wu, Wd = _dense(gate[0], Q4K, H), _dense(up[0], Q4K, H), _dense(down[0], Q4K, I)
+    for c in (0, 37, 300, 511):
+        x = np.zeros((1, H), np.float32)
+        x[0, c] = 1.0
+        y = oracle.expert_ffn(gate, up, down, (Q4K, Q4K, Q4K), H, I, [0], [0], x)
+        h = Wg[:, c] * expit(Wg[:, c]) * Wu[:, c]
+        assert np.allclose(y[0], Wd @ h, rtol=1e-12, atol=1e-12 * np.abs(Wd @ h).max())
+
+
+@pytest.mark.parametrize("qd", [Q4K, Q80])
+def test_brute_force_tiny(qd):
+    """Oracle vs a dense numpy evaluation of the same definition on a tiny layer."""
+    H, I, T = 256, 256, 3
+    g = synth.rng(22, qd)
+    gate = synth.bank_np(g, Q4K, 2, I, H)
+    up = synth.bank_np(g, Q4K, 2, I, H)
+    down = synth.bank_np(g, qd, 2, H, I)
+    x = synth.activations_np(g, T, H)
+    pe, pt = [1, 0, 1], [0, 1, 2]
+    y = oracle.expert_ffn(gate, up, down, (Q4K, Q4K, qd), H, I, pe, pt, x)
+    for p in range(3):
+        e, t = pe[p], pt[p]
+        Wg, Wu, Wd = _dense(gate[e], Q4K, H), _dense(up[e], Q4K, H), _dense(down[e], qd, I)
+        xv = x[t].astype(np.float64)
+        gg = Wg @ xv
+        ref = Wd @ (gg * expit(gg) * (Wu @ xv))
+        assert np.max(np.abs(y[p] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_int8_path_equals_fp_path_when_quantisation_is_exact():
+    """x = 127 everywhere quantizes exactly (id = 1, q = 127, d = 1); up rows alternate 0 / 1 so
+    every 256-block of h holds only 0 and its amax, which also quantize exactly: the int8-path
+    oracle must then equal the fp-path oracle bit for bit."""
+    H, I = 512, 512
+    gate = _q4k_rows(I, H, lambda r: 1)[None]
+    up = _q4k_rows(I, H, lambda r: r % 2)[None]
+    down = _q4k_rows(H, I, lambda r: (3 * r) % 16)[None]
+    x = np.full((1, H), 127.0, np.float32)
+    y0 = oracle.expert_ffn(gate, up, down, (Q4K, Q4K, Q4K), H, I, [0], [0], x, mode=0)
+    y1 = oracle.expert_ffn(gate, up, down, (Q4K, Q4K, Q4K), H, I, [0], [0], x, mode=1)
+    assert np.array_equal(y0, y1)
+    gsum = 127.0 * H
+    expect = np.array([((3 * o) % 16) * gsum * gsum * (I // 2) for o in range(H)])
+    assert np.array_equal(y0[0], expect)
+
+
+def test_int8_path_error_is_quantisation_sized():
+    H, I = 512, 512
+    g = synth.rng(23)
+    gate = synth.bank_np(g, Q4K, 1, I, H)
+    up = synth.bank_np(g, Q4K, 1, I, H)
+    down = synth.bank_np(g, Q4K, 1, H, I)
+    x = synth.activations_np(g, 2, H)
+    y0 = oracle.expert_ffn(gate, up, down, (Q4K,) * 3, H, I, [0, 0], [0, 1], x, mode=0)
+    y1 = oracle.expert_ffn(gate, up, down, (Q4K,) * 3, H, I, [0, 0], [0, 1], x, mode=1)
+    rel = np.abs(y1 - y0).max(axis=1) / np.abs(y0).max(axis=1)
+    assert np.all(rel > 1e-5) and np.all(rel < 1e-1)
+
+
+def test_combine_one_hot_and_shared():
+    g = np.random.default_rng(24)
+    T, k, H = 3, 4, 16
+    y = g.standard_normal((T * k, H))
+    w = np.zeros((T, k))
+    w[0, 2] = w[1, 0] = w[2, 3] = 1.0
+    out = oracle.combine(y, w)
+    assert np.array_equal(out, y[[2, 4, 11]])
+    ys = g.standard_normal((T, H))
+    out2 = oracle.combine(y, w, ys, np.array([1.0, 0.5, 2.0]))
+    assert np.array_equal(out2, y[[2, 4, 11]] + np.array([[1.0], [0.5], [2.0]]) * ys)
+
+
+def test_layer_identical_experts_give_single_expert_output():
+    """With every expert holding the same weights, routing weights sum to 1 and the layer
+    output equals one expert's output (up to fp64 rounding of the weighted sum)."""
+    H, I, E, k = 256, 256, 6, 3
+    g = synth.rng(25)
+    one = [synth.bank_np(g, Q4K, 1, I, H), synth.bank_np(g, Q4K, 1, I, H), synth.bank_np(g, Q4K, 1, H, I)]
+    banks = [np.repeat(b, E, axis=0) for b in one]
+    x = synth.activations_np(g, 2, H)
+    lg = synth.logits_np(g, 2, E)
+    r = oracle.moe_layer(lg, x, *banks, (Q4K,) * 3, k)
+    y1 = oracle.expert_ffn(*one, (Q4K,) * 3, H, I, [0, 0], [0, 1], x)
+    assert np.allclose(r["out"], y1, rtol=1e-14, atol=1e-14 * np.abs(y1).max())
+
+
+def test_layer_relabel_and_batch_invariance():
+    H, I, E, k, T = 256, 256, 8, 2, 4
+    g = synth.rng(26)
+    banks = [synth.bank_np(g, Q4K, E, I, H), synth.bank_np(g, Q4K, E, I, H), synth.bank_np(g, Q4K, E, H, I)]
+    x = synth.activations_np(g, T, H)
+    lg = synth.logits_np(g, T, E)
+    r = oracle.moe_layer(lg, x, *banks, (Q4K,) * 3, k)
+    perm = g.permutation(E)
+    r2 = oracle.moe_layer(lg[:, perm], x, *[b[perm] for b in banks], (Q4K,) * 3, k)
+    assert np.array_equal(r["out"], r2["out"])
+    for t in range(T):
+        rt = oracle.moe_layer(lg[t:t + 1], x[t:t + 1], *banks, (Q4K,) * 3, k)
+        assert np.array_equal(rt["out"][0], r["out"][t])

@@ -1,0 +1,157 @@
+"""Pins for the oracle's block-format decoding (CPU only).
+
+The pages name Q4_K and Q8_0 as expert formats ("Strata-Sage-A1.5-GGUF" card,
+round-1 flag table; "Strata v0.1.31" release notes, Unsloth UD-Q4_K_XL bullet:
+GPU dequantizers bit-exact with the reference dequantizer) but print no byte
+layout and no worked block.  These tests pin the oracle to things other than
+itself: numpy's own binary16 conversion over all 65,536 patterns, codec round
+trips (the layout is a bijection), and hand-worked blocks whose values follow
+in closed form from the fields they were built from.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.golden import load_block
+
+
+def test_fp16_exhaustive_vs_numpy():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.fp16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zeros too
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_q4k_unpack_pack_roundtrip_random_bytes():
+    g = np.random.default_rng(1)
+    for _ in range(300):
+        blk = g.integers(0, 256, 144, dtype=np.uint8)
+        f = oracle.q4k_unpack(blk.tobytes())
+        assert f["sc"].min() >= 0 and f["sc"].max() <= 63
+        assert f["m"].min() >= 0 and f["m"].max() <= 63
+        assert f["q"].min() >= 0 and f["q"].max() <= 15
+        back = oracle.q4k_pack(f["d_bits"], f["dmin_bits"], f["sc"], f["m"], f["q"])
+        assert np.array_equal(back, blk)
+
+
+def test_q4k_pack_unpack_roundtrip_random_fields():
+    g = np.random.default_rng(2)
+    for _ in range(300):
+        d, dm = (int(v) for v in g.integers(0, 65536, 2))
+        sc = g.integers(0, 64, 8)
+        m = g.integers(0, 64, 8)
+        q = g.integers(0, 16, 256)
+        f = oracle.q4k_unpack(oracle.q4k_pack(d, dm, sc, m, q).tobytes())
+        assert f["d_bits"] == d and f["dmin_bits"] == dm
+        assert np.array_equal(f["sc"], sc) and np.array_equal(f["m"], m) and np.array_equal(f["q"], q)
+
+
+def test_q4k_block_a_closed_form():
+    blk = load_block("q4k_block_a.txt")
+    f = oracle.q4k_unpack(blk.tobytes())
+    assert np.array_equal(f["sc"], np.arange(1, 9)) and np.array_equal(f["m"], np.arange(8))
+    assert np.array_equal(f["q"], np.arange(256) % 16)
+    w = oracle.q4k_dequant(blk)
+    i = np.arange(256)
+    j = i // 32
+    expect = (j + 1) * (i % 16) - 0.5 * j
+    assert np.array_equal(w, expect)
+    assert (w[0], w[33], w[100], w[255]) == (0.0, 1.5, 14.5, 116.5)
+    assert w.sum() == 8192.0
+
+
+def test_q4k_block_b_high_bits():
+    blk = load_block("q4k_block_b.txt")
+    f = oracle.q4k_unpack(blk.tobytes())
+    assert np.all(f["sc"] == 63) and np.all(f["m"] == 63) and np.all(f["q"] == 15)
+    w = oracle.q4k_dequant(blk)
+    assert np.all(w == 3717.0 / 4096.0)
+
+
+def test_q4k_block_c_subnormal_scale():
+    blk = load_block("q4k_block_c.txt")
+    w = oracle.q4k_dequant(blk)
+    assert np.all(w == 2.0 ** -24)
+
+
+def test_q4k_single_field_sensitivity():
+    """Each of the 16 scale/min fields moves only its own 32 weights (indexing pin)."""
+    base_sc = np.full(8, 10)
+    base_m = np.full(8, 3)
+    q = np.full(256, 7)
+    ref = oracle.q4k_dequant(oracle.q4k_pack(0x3C00, 0x3C00, base_sc, base_m, q))
+    for j in range(8):
+        sc = base_sc.copy()
+        sc[j] = 50
+        w = oracle.q4k_dequant(oracle.q4k_pack(0x3C00, 0x3C00, sc, base_m, q))
+        diff = np.nonzero(w != ref)[0]
+        assert np.array_equal(diff, np.arange(32 * j, 32 * j + 32))
+        assert np.all(w[diff] - ref[diff] == 40 * 7)
+        m = base_m.copy()
+        m[j] = 60
+        w = oracle.q4k_dequant(oracle.q4k_pack(0x3C00, 0x3C00, base_sc, m, q))
+        diff = np.nonzero(w != ref)[0]
+        assert np.array_equal(diff, np.arange(32 * j, 32 * j + 32))
+        assert np.all(ref[diff] - w[diff] == 57)
+
+
+def test_q80_block_closed_form():
+    blk = load_block("q80_block.txt")
+    w = oracle.q80_dequant(blk)
+    assert np.array_equal(w, (np.arange(32) - 16) / 4.0)
+    assert w.sum() == -4.0
+
+
+def test_q80_random_vs_numpy_views():
+    """Q8_0 value = fp16 scale x int8, checked through numpy's own dtype views."""
+    g = np.random.default_rng(3)
+    blk = g.integers(0, 256, (50, 34), dtype=np.uint8)
+    d = blk[:, 0:2].copy().view(np.float16).astype(np.float64)
+    q = blk[:, 2:].copy().view(np.int8).astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        expect = (d * q).ravel()
+    got = oracle.q80_dequant(blk)
+    finite = np.isfinite(expect)
+    assert np.array_equal(got[finite], expect[finite])
+
+
+@pytest.mark.parametrize("nb", [1, 3])
+def test_q4k_dequant_exact_value(nb):
+    """The oracle's fp64 weight equals d*sc*q - dmin*m evaluated exactly with fractions."""
+    from fractions import Fraction
+    g = np.random.default_rng(4)
+    blk = g.integers(0, 256, (nb, 144), dtype=np.uint8)
+    # keep scales finite
+    blk[:, 1] &= 0x7B
+    blk[:, 3] &= 0x7B
+    w = oracle.q4k_dequant(blk)
+    for b in range(nb):
+        f = oracle.q4k_unpack(blk[b].tobytes())
+        d = Fraction(float(np.uint16(f["d_bits"]).view(np.float16)))
+        dm = Fraction(float(np.uint16(f["dmin_bits"]).view(np.float16)))
+        for i in range(0, 256, 7):
+            j = i // 32
+            exact = d * int(f["sc"][j]) * int(f["q"][i]) - dm * int(f["m"][j])
+            assert Fraction(w[256 * b + i]) == exact
+
+
+def test_q4k_block_e_distinct_fields():
+    blk = load_block("q4k_block_e.txt")
+    sc = np.array([1, 2, 3, 4, 17, 34, 51, 60])
+    m = np.array([5, 6, 7, 8, 33, 49, 20, 63])
+    f = oracle.q4k_unpack(blk.tobytes())
+    assert np.array_equal(f["sc"], sc) and np.array_equal(f["m"], m)
+    q = np.zeros(256, np.int64)
+    for c in range(4):
+        for l in range(32):
+            q[64 * c + l] = (c + l) % 16
+            q[64 * c + 32 + l] = (3 * c + 2 * l + 1) % 16
+    assert np.array_equal(f["q"], q)
+    j = np.arange(256) // 32
+    assert np.array_equal(oracle.q4k_dequant(blk), (sc[j] * q - m[j]).astype(np.float64))
+    # and the packer reproduces the hand-worked bytes
+    assert np.array_equal(oracle.q4k_pack(0x3C00, 0x3C00, sc, m, q), blk)
