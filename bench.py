@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE FFN over Q4_K / Q8_0 experts on one MI355X.
+
+A step is one pass of the whole hot path (route -> [quantize] -> expert FFN ->
+combine) through every layer of a stack of distinct seeded synthetic layers
+resident in HBM, for one batch of fresh router logits and activations per
+layer.  Default workload: Sage-A1.5-like decode (1 token, hidden 2048, 256
+experts, top-8, intermediate 512, Q4_K gate/up/down, 40 layers).
+
+Prints ONE JSON line on stdout: MoE-layer tokens/s (whole job), the roofline of
+the dominant kernel call measured with HIP events on its own stream, and the CPU
+oracle timed on a bounded sample of the same workload.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    d = os.path.join(ROOT, "quantized_moe_ffn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(config: str):
+    """HBM bytes per launch of the dominant call from committed rocprofv3 counter runs, or None
+    when they were taken on other kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(config)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main() -> int:
+    from quantized_moe_ffn_amd import synth
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="sage_decode", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--layers", type=int, default=None, help="override the number of distinct layers")
+    ap.add_argument("--replays", type=int, default=8, help="distinct input sets cycled over the steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the MoE FFN path here is built and measured on a "
+              "single MI355X (--gpus %d requested; multi-GPU sharding is a design note, not built)"
+              % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import quantized_moe_ffn_amd as qm
+    from quantized_moe_ffn_amd import layers as qlayers
+
+    if not os.path.exists(qm.LIB_PATH):
+        from quantized_moe_ffn_amd import build as hb
+        hb.build()
+    qm.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = synth.WORKLOADS[args.config]
+    L = args.layers or w.layers
+    R = max(1, args.replays)
+    T, H, E, k, I = w.tokens, w.hidden, w.n_experts, w.top_k, w.inter
+    flags = qm.MOE_FFN_INT8 if w.int8_path else qm.MOE_FFN_DECODE
+
+    log("[bench] building %d layers of %s (%.2f GB of expert weights)"
+        % (L, w.name, L * (E * w.expert_bytes() + (w.expert_bytes() if w.shared else 0)) / 1e9))
+    t0 = time.time()
+    stack = [qlayers.make_layer(w, seed=0, index=l, device=dev) for l in range(L)]
+    torch.cuda.synchronize()
+    log("[bench] layers ready in %.1f s" % (time.time() - t0))
+
+    inputs = []
+    for r in range(R):
+        row = []
+        for l in range(L):
+            lg, x = qlayers.inputs_np(w, seed=0, index=l, replay=r)
+            row.append((torch.from_numpy(lg).to(dev), torch.from_numpy(x).to(dev)))
+        inputs.append(row)
+    bufs = qm.LayerBuffers(stack[0].layer, T, k, flags, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        row = inputs[s % R]
+        for l in range(L):
+            lg, x = row[l]
+            qm.forward(stack[l].layer, lg, x, k, bufs, flags=flags, stream=stream)
+
+    # unique experts per (replay, layer): algorithmic bytes of each layer's FFN call
+    uniq = np.zeros((R, L), np.int64)
+    for r in range(R):
+        for l in range(L):
+            lg, _ = inputs[r][l]
+            qm.moe_route_topk(lg, k, bufs.routing, True, bufs.route_ws, stream)
+            uniq[r, l] = int(bufs.routing.n_active.item())
+    qm.moe_check_device_errors()
+    per_expert = w.expert_bytes()
+    shared_bytes = w.expert_bytes() if w.shared else 0
+    bytes_rl = uniq * per_expert + shared_bytes           # weight bytes per layer call
+    act_bytes = T * H * 4 + T * k * 4 * 2 + T * H * 4     # x in, routing, out (small next to weights)
+
+    log("[bench] warmup %d steps" % args.warmup)
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    qm.moe_check_device_errors()
+
+    log("[bench] timing %d steps x %d layers" % (args.steps, L))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for s in range(args.steps):
+        step(args.warmup + s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    qm.moe_check_device_errors()
+    ms_per_step = ms_total / args.steps
+    tokens = T * L * args.steps
+    value = tokens / (ms_total / 1e3)
+    step_bytes = sum(int(bytes_rl[(args.warmup + s) % R].sum()) for s in range(args.steps))
+    log("[bench] %.3f ms/step (wall %.3f ms/step), %.0f layer-tokens/s, %.1f GB/s end to end"
+        % (ms_per_step, wall * 1e3 / args.steps, value, step_bytes / (ms_total / 1e3) / 1e9))
+
+    # dominant call: the expert FFN, timed per launch with events on its stream
+    log("[bench] timing the expert FFN call per launch")
+    n_launch, dur_ms, dom_bytes = 0, 0.0, 0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+    for r in range(R):
+        for l in range(L):
+            lg, x = inputs[r][l]
+            qm.moe_route_topk(lg, k, bufs.routing, True, bufs.route_ws, stream)
+            if flags == qm.MOE_FFN_INT8:
+                qm.moe_quantize_act(x, bufs.xq, bufs.xd, stream)
+            a, b = evs[l]
+            a.record(stream)
+            qm.moe_expert_ffn_q(stack[l].layer, bufs.routing, T, k, bufs.y_pair,
+                                x=x if flags == qm.MOE_FFN_DECODE else None,
+                                xq=bufs.xq if flags == qm.MOE_FFN_INT8 else None,
+                                xd=bufs.xd if flags == qm.MOE_FFN_INT8 else None, flags=flags,
+                                y_shared=bufs.y_shared, workspace=bufs.ffn_ws, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for l in range(L):
+            dur_ms += evs[l][0].elapsed_time(evs[l][1])
+            dom_bytes += int(bytes_rl[r, l])
+            n_launch += 1
+    qm.moe_check_device_errors()
+    avg_ms = dur_ms / n_launch
+    if w.int8_path:
+        ops = 2.0 * T * k * 3 * H * I + (2.0 * T * 3 * H * I if w.shared else 0.0)
+        achieved = ops / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profiles(w.name),
+                "kernel": "moe_expert_ffn_q (int8 path)", "ops_per_launch": ops,
+                "avg_launch_us": round(avg_ms * 1e3, 2)}
+    else:
+        achieved = dom_bytes / (dur_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(w.name),
+                "kernel": "moe_expert_ffn_q (decode path)",
+                "bytes_per_launch": round(dom_bytes / n_launch), "avg_launch_us": round(avg_ms * 1e3, 2)}
+    log("[bench] expert FFN call: %.2f us per launch, %s %s" % (avg_ms * 1e3, roof["achieved"], roof["unit"]))
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(w, stack, inputs, bufs, flags, k, args.cpu_seconds)
+
+    rec = {
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (decode), int8 TOPS (prefill)",
+        "value": round(value, 1),
+        "unit": "layer-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if w.int8_path else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "inter": I,
+                   "shared_expert": w.shared, "layers": L, "replays": R,
+                   "formats": {"gate": fmt(w.qt_gate), "up": fmt(w.qt_up), "down": fmt(w.qt_down)},
+                   "parallelism": "single GPU"},
+        "hbm_GBps_end_to_end": round(step_bytes / (ms_total / 1e3) / 1e9, 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_max_normwise_err": parity,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def fmt(qt):
+    return {8: "Q8_0", 12: "Q4_K"}[qt]
+
+
+def cpu_baseline(w, stack, inputs, bufs, flags, k, budget_s):
+    """The oracle (as it stands) on a bounded sample of the same workload, on this host's
+    cores; also checks the GPU outputs of the sampled tokens against it."""
+    import torch
+    import oracle
+    import quantized_moe_ffn_amd as qm
+    T = w.tokens
+    tok_sample = np.arange(T) if T <= 64 else np.linspace(0, T - 1, 16).round().astype(np.int64)
+    mode = 1 if w.int8_path else 0
+    spent, tokens_done, layers_done, errs = 0.0, 0, 0, []
+    for l, dl in enumerate(stack):
+        if spent >= budget_s:
+            break
+        lg_t, x_t = inputs[0][l]
+        qm.forward(dl.layer, lg_t, x_t, k, bufs, flags=flags)
+        torch.cuda.synchronize()
+        gpu_out = bufs.out.cpu().numpy()[tok_sample]
+        lg = lg_t.cpu().numpy()[tok_sample]
+        x = x_t.cpu().numpy()[tok_sample]
+        # copy back only the experts this sample touches (not timed)
+        idx_gpu = bufs.routing.idx.cpu().numpy()[tok_sample]
+        uniq = np.unique(idx_gpu)
+        sel = torch.as_tensor(uniq, device=dl.banks["gate"].device)
+        hb = {n: dl.banks[n].index_select(0, sel).cpu().numpy() for n in ("gate", "up", "down")}
+        remap = np.full(w.n_experts, -1, np.int64)
+        remap[uniq] = np.arange(len(uniq))
+        shared = None
+        if w.shared:
+            shared = tuple(dl.banks[n].cpu().numpy() for n in ("sh_gate", "sh_up", "sh_down"))
+        qt = (w.qt_gate, w.qt_up, w.qt_down)
+        t0 = time.perf_counter()
+        idx, wts = oracle.route_topk(lg, k)
+        oracle.bucket(idx, w.n_experts)
+        pe = remap[idx.reshape(-1)]
+        if np.any(pe < 0):      # the oracle chose an expert the GPU did not: parity failure
+            pe = np.maximum(pe, 0)
+            errs.append(float("inf"))
+        pt = np.repeat(np.arange(len(tok_sample)), k)
+        y = oracle.expert_ffn(hb["gate"], hb["up"], hb["down"], qt, w.hidden, w.inter, pe, pt, x, mode)
+        ys = None
+        if shared is not None:
+            ys = oracle.expert_ffn(*shared, qt, w.hidden, w.inter, np.zeros(len(tok_sample), np.int32),
+                                   np.arange(len(tok_sample), dtype=np.int32), x, mode)
+        out = oracle.combine(y, wts, ys)
+        spent += time.perf_counter() - t0
+        tokens_done += len(tok_sample)
+        layers_done += 1
+        den = np.abs(out).max(axis=1)
+        errs.append(float((np.abs(gpu_out - out).max(axis=1) / den).max()))
+        log("[bench] cpu oracle: layer %d done, %.1f s spent" % (l, spent))
+    cpu = {"value": round(tokens_done / spent, 3), "unit": "layer-tokens/s", "cores": oracle.threads(),
+           "kind": "oracle",
+           "sample": "%d layer(s) x %d token(s) of %s, route+bucket+FFN+combine in fp64 (%.1f s)"
+                     % (layers_done, len(tok_sample), w.name, spent)}
+    return cpu, (max(errs) if errs else None)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,195 @@
+/*
+ * moe.h — C ABI of libmoe: the routed mixture-of-experts FFN over GGUF
+ * block-quantized expert weights, on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the per-layer expert path the Strata pages keep returning to:
+ * router logits -> top-k expert selection -> per-expert token buckets -> expert
+ * FFN with the weights dequantized inside the dot products (gate and up
+ * projections, SiLU(gate)*up, down projection) -> routing-weighted combine, with
+ * an optional always-on shared expert.  Sources: "Strata-Sage-A1.5-GGUF" (model
+ * card: 256 experts / top-8, Q4_K down experts), "Strata: a 125B MoE at 94
+ * tok/s on a 12 GB Card" (sparsity table: 512 experts, 10 routed + 1 shared,
+ * hidden 2,560), "Strata v0.1.31" release notes (Unsloth UD-Q4_K_XL bullet:
+ * Q4_K / Q8_0 experts, dequantizers bit-exact, dot products within float
+ * rounding), "Strata - the details" ("How it works": routers and shared
+ * experts on the GPU; MTP verify windows of up to 3 drafts; prompt chunks).
+ *
+ * Conventions for every call
+ *  - Every array argument is a DEVICE pointer owned by the caller; nothing is
+ *    retained after the call returns.  Descriptor structs (moe_qmatrix,
+ *    moe_layer, moe_routing) live in HOST memory and are read during the call.
+ *  - Every call that takes a stream only enqueues work on it: no call
+ *    allocates or frees memory, and none synchronises (except
+ *    moe_check_device_errors, which is documented to).
+ *  - Arguments are validated before anything is enqueued.  On failure the call
+ *    returns a non-zero moe_status, enqueues nothing, and moe_last_error()
+ *    (per host thread) names the failed check and the numbers involved.
+ *  - Errors found by kernels (an expert id out of range in routing buffers
+ *    passed in, a non-finite router logit or activation) set a per-device
+ *    error word; the kernel then skips the offending item without touching
+ *    memory out of bounds.  moe_check_device_errors reports and clears it.
+ *  - Results are bitwise deterministic run to run, and a token's result does
+ *    not depend on which other tokens share its experts.
+ *  - All sizes are element counts unless named *_bytes.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1, /* a shape, pointer, alignment or flag check failed */
+    MOE_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement      */
+    MOE_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required       */
+    MOE_ERR_DEVICE = 4            /* a HIP call failed, or a kernel set the error word */
+} moe_status;
+
+/* Block formats, numbered as in GGUF.  The pages name both formats (the
+ * "Strata v0.1.31" Unsloth bullet; Q4_K down experts on the Sage-A1.5 card) and
+ * give no byte layout; the public GGUF layouts are used:
+ *   MOE_Q4_K: 144-byte super-block of 256 weights: fp16 d, fp16 dmin, 12 bytes
+ *             packing eight 6-bit scales and eight 6-bit mins, 128 bytes of
+ *             4-bit quants; w = d*sc*q - dmin*m per 32-weight sub-block.
+ *   MOE_Q8_0: 34-byte block of 32 weights: fp16 d, 32 int8 q; w = d*q. */
+enum { MOE_Q8_0 = 8, MOE_Q4_K = 12 };
+
+/* moe_route_topk flags */
+enum { MOE_ROUTE_RENORM = 1u }; /* weights = softmax over the k selected logits */
+
+/* moe_expert_ffn_q path selection */
+enum {
+    MOE_FFN_AUTO = 0u,   /* decode path for small batches, int8 path otherwise        */
+    MOE_FFN_DECODE = 1u, /* fp32 activations, weights dequantized in registers        */
+    MOE_FFN_INT8 = 2u    /* int8 activations (moe_quantize_act), grouped int8 MFMA GEMM */
+};
+
+/* One projection of an expert bank: n_experts matrices of rows x cols weights,
+ * each row a contiguous run of blocks (cols contiguous), rows back to back,
+ * experts expert_bytes apart.  row_bytes must equal cols/B*S for the format's
+ * block of B weights and S bytes; rows must be 16-byte aligned (Q4_K) or the
+ * row start 2-byte aligned (Q8_0); data must be 256-byte aligned. */
+typedef struct moe_qmatrix {
+    const void* data;
+    int32_t qtype;
+    int32_t rows;
+    int32_t cols;
+    int32_t reserved;
+    int64_t row_bytes;
+    int64_t expert_bytes;
+} moe_qmatrix;
+
+/* One MoE layer: routed banks gate/up [E][I][H] and down [E][H][I]; when
+ * has_shared != 0 the sh_* matrices hold the always-on shared expert (one
+ * expert each, same H and I). */
+typedef struct moe_layer {
+    int32_t n_experts; /* E */
+    int32_t hidden;    /* H, a multiple of 256 */
+    int32_t inter;     /* I, a multiple of 256 */
+    int32_t has_shared;
+    moe_qmatrix gate, up, down;
+    moe_qmatrix sh_gate, sh_up, sh_down;
+} moe_layer;
+
+/* Routing results, all device arrays written by moe_route_topk.
+ *   idx [T][k] int32   selected experts, slot j in descending logit order
+ *   w   [T][k] fp32    routing weights
+ *   count [E], offset [E+1] int32: pairs per expert and their exclusive sums
+ *   pair [T*k] int32   pair ids p = t*k + j grouped by expert (ascending expert,
+ *                      ascending p within an expert)
+ *   active [min(E, T*k)] int32  experts with count > 0, ascending
+ *   n_active [1] int32 */
+typedef struct moe_routing {
+    int32_t* idx;
+    float* w;
+    int32_t* count;
+    int32_t* offset;
+    int32_t* pair;
+    int32_t* active;
+    int32_t* n_active;
+} moe_routing;
+
+/* Bytes of device workspace moe_route_topk needs for T tokens, E experts, top-k. */
+size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k);
+
+/* Top-k expert selection from router logits plus per-expert bucketing.
+ * logits: fp32 [T][E].  Selection order: descending logit, ties to the lower
+ * expert index, IEEE comparison (-0 and +0 tie).  With MOE_ROUTE_RENORM the
+ * weights are the softmax over the k selected logits; without it, the softmax
+ * over all E logits taken at the k selected experts.
+ * Checks: 1 <= T; 1 <= k <= min(E, 16); E <= 1024; logits 4-byte aligned; every
+ * moe_routing pointer non-null; ws_bytes >= moe_route_workspace_bytes.
+ * A non-finite logit sets the device error word (results for that token are
+ * still written, ordered by the total order of the bit patterns). */
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, uint32_t flags,
+                          const moe_routing* r, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Per-token int8 activation quantisation, once per token and 256-wide block
+ * (the "one quantization per token" of the Sage-A1.5 card's round-2 table):
+ * amax = max|x|; amax == 0 gives d = 0 and q = 0; otherwise id = 127/amax
+ * (IEEE fp32, correctly rounded), q = rint(x*id) (ties to even) clamped to
+ * +-127, d = amax/127.  x fp32 [T][H] -> xq int8 [T][H], xd fp32 [T][H/256].
+ * Checks: T >= 1, H % 256 == 0, pointers non-null.  A non-finite x sets the
+ * device error word and that block is written as q = 0, d = 0 (codes stay
+ * finite, as the "Strata v0.1.39" fixes require of q8_1 activations). */
+moe_status moe_quantize_act(const float* x, int32_t T, int32_t H, int8_t* xq, float* xd,
+                            hipStream_t stream);
+
+/* Bytes of device workspace moe_expert_ffn_q needs. */
+size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t flags);
+
+/* Expert FFN for every routed (token, slot) pair, and for the shared expert.
+ *   y_pair[p] = W_down[e] * (silu(W_gate[e] x_t) .* (W_up[e] x_t)),  e = idx[p], t = p / k
+ *   y_shared[t] = the same with the shared expert's matrices (when has_shared).
+ * Weights are dequantized inside the dot products.  Decode path: x fp32 [T][H].
+ * Int8 path: xq/xd from moe_quantize_act; h is re-quantized per 256-wide block
+ * of I for the int8 down projection.  y_pair fp32 [T*k][H]; y_shared fp32
+ * [T][H] (required iff has_shared).  r must hold the result of moe_route_topk
+ * for the same T, k and E (read on the device: no host synchronisation).
+ * Checks: shapes consistent with L; H, I multiples of 256; qtypes supported
+ * (gate/up/down: Q4_K or Q8_0); alignment; workspace size. */
+moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T, int32_t k,
+                            const float* x, const int8_t* xq, const float* xd, uint32_t flags,
+                            float* y_pair, float* y_shared, void* workspace, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Routing-weighted combine:
+ *   out[t] = sum_{j<k} w[t][j] * y_pair[t*k+j]  (+ s_t * y_shared[t])
+ * summed in slot order, then the shared expert; s_t = shared_scale[t], or 1
+ * when shared_scale is NULL; y_shared may be NULL (no shared expert).
+ * All fp32; out [T][H].  No residual, norm or bias. */
+moe_status moe_combine(const float* y_pair, const float* w, const float* y_shared,
+                       const float* shared_scale, int32_t T, int32_t k, int32_t H, float* out,
+                       hipStream_t stream);
+
+/* Test hook: dequantize n_weights weights of contiguous blocks to fp32 with the
+ * same device unpacking helpers the FFN kernels use.  Each value is the exact
+ * d*sc*q - dmin*m (Q4_K) or d*q (Q8_0) rounded once to fp32.  n_weights must
+ * be a multiple of the block size. */
+moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, float* out,
+                         hipStream_t stream);
+
+/* Synchronises `stream`, then reads and clears the current device's error
+ * word.  Returns MOE_ERR_DEVICE (and a message naming the flags) if set. */
+moe_status moe_check_device_errors(hipStream_t stream);
+
+/* Message for the last failed call on this host thread ("" if none). */
+const char* moe_last_error(void);
+
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,85 @@
+// common.h — device helpers shared by the libmoe kernels (gfx950, wave64).
+//
+// Block formats (GGUF layouts; the pages name Q4_K and Q8_0 as expert formats,
+// "Strata v0.1.31" release notes, Unsloth UD-Q4_K_XL bullet, and the
+// "Strata-Sage-A1.5-GGUF" card's flag table, without a byte layout):
+//   Q4_K, 144 B / 256 weights:
+//     [0:2] d fp16 | [2:4] dmin fp16 | [4:16] s[12] | [16:144] qs[128]
+//     sub-block j (weights 32j..32j+31): j < 4: sc = s[j] & 63, m = s[j+4] & 63
+//       j >= 4: sc = (s[j+4] & 15) | (s[j-4] >> 6) << 4, m = (s[j+4] >> 4) | (s[j] >> 6) << 4
+//     qs[32c+l]: low nibble = weight 64c+l, high nibble = weight 64c+32+l
+//     w = d*sc*q - dmin*m
+//   Q8_0, 34 B / 32 weights: [0:2] d fp16 | [2:34] q int8;  w = d*q
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kQ8_0 = 8;
+constexpr int kQ4_K = 12;
+constexpr int kWave = 64;
+
+// Bits of the per-device error word.
+constexpr unsigned kErrExpertRange = 1u;   // an expert id outside [0, E)
+constexpr unsigned kErrPairRange = 2u;     // bucket offsets / pair ids outside their range
+constexpr unsigned kErrLogitNonFinite = 4u;
+constexpr unsigned kErrActNonFinite = 8u;
+constexpr unsigned kErrBarrierTimeout = 16u;
+
+extern __device__ unsigned int g_moe_err;
+
+__device__ __forceinline__ void raise_error(unsigned bits) { atomicOr(&g_moe_err, bits); }
+
+// IEEE binary16 bits -> fp32 (exact, subnormals included: v_cvt_f32_f16 with
+// fp16 denormals enabled, the HIP default).
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Q4_K header as four dwords: h0 = d | dmin << 16, h1 = s[0..3], h2 = s[4..7], h3 = s[8..11].
+struct Q4KHead {
+    uint32_t h0, h1, h2, h3;
+};
+
+__device__ __forceinline__ float q4k_d(const Q4KHead& h) { return f16_bits_to_f32(h.h0 & 0xFFFFu); }
+__device__ __forceinline__ float q4k_dmin(const Q4KHead& h) { return f16_bits_to_f32(h.h0 >> 16); }
+
+// 6-bit scale and min of sub-block j (0..7).
+__device__ __forceinline__ void q4k_scale_min(const Q4KHead& h, int j, int& sc, int& m) {
+    if (j < 4) {
+        sc = (h.h1 >> (8 * j)) & 63;
+        m = (h.h2 >> (8 * j)) & 63;
+    } else {
+        const int jj = j - 4;
+        sc = ((h.h3 >> (8 * jj)) & 15) | (((h.h1 >> (8 * jj + 6)) & 3) << 4);
+        m = ((h.h3 >> (8 * jj + 4)) & 15) | (((h.h2 >> (8 * jj + 6)) & 3) << 4);
+    }
+}
+
+// Quant of weight i (0..255) from the 128 quant bytes viewed as 32 dwords.
+__device__ __forceinline__ int q4k_quant(const uint32_t* qs32, int i) {
+    const int c = i >> 6, l = i & 31, hi = (i >> 5) & 1;
+    const int byte = 32 * c + l;
+    const uint32_t b = (qs32[byte >> 2] >> (8 * (byte & 3))) & 0xFFu;
+    return hi ? (int)(b >> 4) : (int)(b & 15u);
+}
+
+// Wave64 butterfly sum: every lane ends with the same total, summed in the
+// same tree order on every run (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace moe

@@ -1,0 +1,67 @@
+// kernels.h — internal launchers of libmoe (host side of the kernel files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kSmallPairs = 256;  // T*k up to this: routing + bucketing in one workgroup
+constexpr int kTilePairs = 256;   // tile of the large-batch counting sort
+
+struct RoutingPtrs {
+    int32_t* idx;
+    float* w;
+    int32_t* count;
+    int32_t* offset;
+    int32_t* pair;
+    int32_t* active;
+    int32_t* n_active;
+};
+
+// One projection of a bank, as the kernels see it.
+struct QMat {
+    const uint8_t* data;
+    int64_t row_bytes;
+    int64_t expert_bytes;
+    int qtype;
+};
+
+struct FfnArgs {
+    QMat gate, up, down;           // routed banks
+    QMat sgate, sup, sdown;        // shared expert (used when has_shared)
+    int has_shared;
+    int H, I, T, k, E;
+    const int32_t* count;
+    const int32_t* offset;
+    const int32_t* pair;
+    const int32_t* active;
+    const int32_t* n_active;
+    const float* x;                // [T][H] fp32 (decode path)
+    const int8_t* xq;              // [T][H] int8 (int8 path)
+    const float* xd;               // [T][H/256]
+    float* h;                      // workspace [T*k + T][I] fp32 (decode path)
+    int8_t* hq;                    // workspace [T*k + T][I] int8 (int8 path)
+    float* hd;                     // workspace [T*k + T][I/256]
+    float* y_pair;                 // [T*k][H]
+    float* y_shared;               // [T][H]
+    int n_slots;                   // min(E, T*k) routed expert slots
+};
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, const RoutingPtrs& r,
+                        void* ws, hipStream_t s);
+size_t route_workspace_bytes(int T, int E, int k);
+
+hipError_t launch_gateup(const FfnArgs& a, int xmode, hipStream_t s);
+hipError_t launch_down(const FfnArgs& a, int hmode, hipStream_t s);
+hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_int8(const FfnArgs& a, void* ws_extra, hipStream_t s);
+size_t ffn_int8_extra_bytes(int T, int k, int E, int H, int I);
+
+hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s);
+hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared,
+                          const float* shared_scale, int T, int k, int H, float* out, hipStream_t s);
+hipError_t launch_dequant(const void* blocks, int qtype, int64_t n_weights, float* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,7 @@
+// libmoe.hip — single translation unit of libmoe (one device error word,
+// one code object).  Each included file holds one stage of the path.
+#include "ffn_decode.hip"
+#include "route.hip"
+#include "quant.hip"
+#include "ffn_int8.hip"
+#include "moe_api.hip"

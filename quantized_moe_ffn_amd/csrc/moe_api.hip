@@ -1,0 +1,270 @@
+// moe_api.hip — the C ABI of libmoe (declared in include/moe.h): argument
+// validation, workspace layout and dispatch to the kernels.  Nothing here
+// allocates, frees or synchronises (except moe_check_device_errors).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status ok() {
+    g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
+moe_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MOE_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int blk_weights(int qt) { return qt == MOE_Q4_K ? 256 : 32; }
+int blk_bytes(int qt) { return qt == MOE_Q4_K ? 144 : 34; }
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxDim = 3584;   // H and I: LDS staging of kTokChunk rows of fp32 (< 64 KB)
+constexpr int kAutoDecodeMaxT = 64;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Validates one projection; rows x cols weights per expert, n_experts experts.
+moe_status check_qmatrix(const moe_qmatrix& m, const char* name, int rows, int cols, int n_experts) {
+    if (!m.data) return fail(MOE_ERR_INVALID_ARGUMENT, "%s.data is NULL", name);
+    if (m.qtype != MOE_Q4_K && m.qtype != MOE_Q8_0)
+        return fail(MOE_ERR_UNSUPPORTED, "%s.qtype = %d: supported are Q4_K (%d) and Q8_0 (%d)", name,
+                    m.qtype, MOE_Q4_K, MOE_Q8_0);
+    if (m.rows != rows || m.cols != cols)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s is %d x %d, expected %d x %d", name, m.rows, m.cols,
+                    rows, cols);
+    if (cols % blk_weights(m.qtype) != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s.cols = %d is not a multiple of the block size %d", name,
+                    cols, blk_weights(m.qtype));
+    const int64_t rb = (int64_t)cols / blk_weights(m.qtype) * blk_bytes(m.qtype);
+    if (m.row_bytes != rb)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s.row_bytes = %lld, expected %lld", name,
+                    (long long)m.row_bytes, (long long)rb);
+    if (n_experts > 1 && m.expert_bytes < (int64_t)rows * rb)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s.expert_bytes = %lld < rows*row_bytes = %lld", name,
+                    (long long)m.expert_bytes, (long long)rows * rb);
+    const size_t al = m.qtype == MOE_Q4_K ? 16 : 2;
+    if (!aligned(m.data, al) || (m.expert_bytes % (int64_t)al) != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "%s: data and expert_bytes must be %zu-byte aligned", name, al);
+    return MOE_OK;
+}
+
+moe::QMat to_qmat(const moe_qmatrix& m) {
+    return moe::QMat{(const uint8_t*)m.data, m.row_bytes, m.expert_bytes, m.qtype};
+}
+
+struct FfnWorkspace {
+    size_t h, hq, hd, total;
+};
+
+FfnWorkspace ffn_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
+    const size_t rows = (size_t)T * k + (L->has_shared ? T : 0);
+    FfnWorkspace w{};
+    w.h = 0;
+    size_t off = align_up(rows * L->inter * sizeof(float), 256);
+    w.hq = off;
+    w.hd = off;
+    if (path == MOE_FFN_INT8) {
+        off += align_up(rows * L->inter, 256);
+        w.hd = off;
+        off += align_up(rows * (L->inter / 256) * sizeof(float), 256);
+    }
+    w.total = off;
+    return w;
+}
+
+uint32_t resolve_path(uint32_t flags, int T) {
+    if (flags == MOE_FFN_AUTO) return T <= kAutoDecodeMaxT ? MOE_FFN_DECODE : MOE_FFN_INT8;
+    return flags;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_last_error; }
+
+size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k) {
+    if (T < 1 || E < 1 || k < 1) return 0;
+    return moe::route_workspace_bytes(T, E, k);
+}
+
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, uint32_t flags,
+                          const moe_routing* r, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!logits) return fail(MOE_ERR_INVALID_ARGUMENT, "logits is NULL");
+    if (!aligned(logits, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "logits must be 4-byte aligned");
+    if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d: need at least one token", T);
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d: need 1 <= E <= %d", E, kMaxExperts);
+    if (k < 1 || k > E || k > kMaxTopK)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d: need 1 <= k <= min(E = %d, %d)", k, E, kMaxTopK);
+    if (flags & ~(uint32_t)MOE_ROUTE_RENORM)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "flags = 0x%x: only MOE_ROUTE_RENORM is defined", flags);
+    if ((int64_t)T * k > (int64_t)1 << 30)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "T*k = %lld is too large", (long long)T * k);
+    if (!r || !r->idx || !r->w || !r->count || !r->offset || !r->pair || !r->active || !r->n_active)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_routing or one of its arrays is NULL");
+    const size_t need = moe::route_workspace_bytes(T, E, k);
+    if (need && (!workspace || ws_bytes < need))
+        return fail(MOE_ERR_WORKSPACE, "routing workspace: %zu bytes given, %zu needed", ws_bytes, need);
+    if (need && !aligned(workspace, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 4-byte aligned");
+    moe::RoutingPtrs rp{r->idx, r->w, r->count, r->offset, r->pair, r->active, r->n_active};
+    return from_hip(moe::launch_route(logits, T, E, k, (flags & MOE_ROUTE_RENORM) ? 1 : 0, rp, workspace, stream),
+                    "moe_route_topk launch");
+}
+
+moe_status moe_quantize_act(const float* x, int32_t T, int32_t H, int8_t* xq, float* xd, hipStream_t stream) {
+    if (!x || !xq || !xd) return fail(MOE_ERR_INVALID_ARGUMENT, "x, xq or xd is NULL");
+    if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d: need at least one token", T);
+    if (H < 256 || H % 256 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "H = %d: must be a positive multiple of 256", H);
+    if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xd, 4))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned, xq and xd 4-byte aligned");
+    return from_hip(moe::launch_quantize_act(x, T, H, xq, xd, stream), "moe_quantize_act launch");
+}
+
+size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t flags) {
+    if (!L || T < 1 || k < 1) return 0;
+    return ffn_ws_layout(L, T, k, resolve_path(flags, T)).total;
+}
+
+moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T, int32_t k, const float* x,
+                            const int8_t* xq, const float* xd, uint32_t flags, float* y_pair, float* y_shared,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!L) return fail(MOE_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
+    const int E = L->n_experts, H = L->hidden, I = L->inter;
+    if (E < 1 || E > kMaxExperts) return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts = %d: need 1..%d", E, kMaxExperts);
+    if (H < 256 || H % 256 || I < 256 || I % 256)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "hidden = %d, inter = %d: both must be positive multiples of 256", H, I);
+    if (H > kMaxDim || I > kMaxDim)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden = %d, inter = %d: this build supports up to %d", H, I, kMaxDim);
+    if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d: need at least one token", T);
+    if (k < 1 || k > E || k > kMaxTopK)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d: need 1 <= k <= min(E = %d, %d)", k, E, kMaxTopK);
+    moe_status st;
+    if ((st = check_qmatrix(L->gate, "gate", I, H, E)) != MOE_OK) return st;
+    if ((st = check_qmatrix(L->up, "up", I, H, E)) != MOE_OK) return st;
+    if ((st = check_qmatrix(L->down, "down", H, I, E)) != MOE_OK) return st;
+    if (L->has_shared) {
+        if ((st = check_qmatrix(L->sh_gate, "sh_gate", I, H, 1)) != MOE_OK) return st;
+        if ((st = check_qmatrix(L->sh_up, "sh_up", I, H, 1)) != MOE_OK) return st;
+        if ((st = check_qmatrix(L->sh_down, "sh_down", H, I, 1)) != MOE_OK) return st;
+        if (L->sh_gate.qtype != L->gate.qtype || L->sh_up.qtype != L->up.qtype || L->sh_down.qtype != L->down.qtype)
+            return fail(MOE_ERR_UNSUPPORTED, "the shared expert must use the routed experts' formats "
+                        "(gate %d/%d, up %d/%d, down %d/%d)", L->sh_gate.qtype, L->gate.qtype,
+                        L->sh_up.qtype, L->up.qtype, L->sh_down.qtype, L->down.qtype);
+        if (!y_shared) return fail(MOE_ERR_INVALID_ARGUMENT, "layer has a shared expert but y_shared is NULL");
+    }
+    if (!r || !r->count || !r->offset || !r->pair || !r->active || !r->n_active)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_routing or one of count/offset/pair/active/n_active is NULL");
+    if (!y_pair) return fail(MOE_ERR_INVALID_ARGUMENT, "y_pair is NULL");
+    if (flags != MOE_FFN_AUTO && flags != MOE_FFN_DECODE && flags != MOE_FFN_INT8)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8", flags);
+    const uint32_t path = resolve_path(flags, T);
+    if (path == MOE_FFN_DECODE && !x) return fail(MOE_ERR_INVALID_ARGUMENT, "decode path needs x (fp32 [T][H])");
+    if (path == MOE_FFN_INT8 && (!xq || !xd))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "int8 path needs xq and xd from moe_quantize_act");
+    if ((x && !aligned(x, 4)) || (xd && !aligned(xd, 4)) || !aligned(y_pair, 4) || (y_shared && !aligned(y_shared, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "fp32 arrays must be 4-byte aligned");
+    const FfnWorkspace wl = ffn_ws_layout(L, T, k, path);
+    if (!workspace || ws_bytes < wl.total)
+        return fail(MOE_ERR_WORKSPACE, "FFN workspace: %zu bytes given, %zu needed", ws_bytes, wl.total);
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+
+    moe::FfnArgs a{};
+    a.gate = to_qmat(L->gate);
+    a.up = to_qmat(L->up);
+    a.down = to_qmat(L->down);
+    a.has_shared = L->has_shared ? 1 : 0;
+    if (a.has_shared) {
+        a.sgate = to_qmat(L->sh_gate);
+        a.sup = to_qmat(L->sh_up);
+        a.sdown = to_qmat(L->sh_down);
+    }
+    a.H = H;
+    a.I = I;
+    a.T = T;
+    a.k = k;
+    a.E = E;
+    a.count = r->count;
+    a.offset = r->offset;
+    a.pair = r->pair;
+    a.active = r->active;
+    a.n_active = r->n_active;
+    a.x = x;
+    a.xq = xq;
+    a.xd = xd;
+    char* ws = (char*)workspace;
+    a.h = (float*)(ws + wl.h);
+    a.hq = (int8_t*)(ws + wl.hq);
+    a.hd = (float*)(ws + wl.hd);
+    a.y_pair = y_pair;
+    a.y_shared = y_shared;
+    a.n_slots = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
+    if (path == MOE_FFN_DECODE) return from_hip(moe::launch_ffn_decode(a, stream), "moe_expert_ffn_q (decode) launch");
+    return from_hip(moe::launch_ffn_int8(a, nullptr, stream), "moe_expert_ffn_q (int8) launch");
+}
+
+moe_status moe_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
+                       int32_t T, int32_t k, int32_t H, float* out, hipStream_t stream) {
+    if (!y_pair || !w || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "y_pair, w or out is NULL");
+    if (T < 1 || k < 1 || k > kMaxTopK || H < 1)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d, k = %d, H = %d: need T >= 1, 1 <= k <= %d, H >= 1", T, k, H,
+                    kMaxTopK);
+    if (shared_scale && !y_shared)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "shared_scale given without y_shared");
+    return from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, T, k, H, out, stream),
+                    "moe_combine launch");
+}
+
+moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, float* out, hipStream_t stream) {
+    if (!blocks || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "blocks or out is NULL");
+    if (qtype != MOE_Q4_K && qtype != MOE_Q8_0)
+        return fail(MOE_ERR_UNSUPPORTED, "qtype = %d: supported are Q4_K (%d) and Q8_0 (%d)", qtype, MOE_Q4_K, MOE_Q8_0);
+    if (n_weights < 0 || n_weights % blk_weights(qtype) != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "n_weights = %lld is not a multiple of the block size %d",
+                    (long long)n_weights, blk_weights(qtype));
+    if (!aligned(blocks, qtype == MOE_Q4_K ? 16 : 2))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "blocks must be %d-byte aligned", qtype == MOE_Q4_K ? 16 : 2);
+    if (n_weights == 0) return ok();
+    return from_hip(moe::launch_dequant(blocks, qtype, n_weights, out, stream), "moe_dequant_q launch");
+}
+
+moe_status moe_check_device_errors(hipStream_t stream) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return from_hip(e, "moe_check_device_errors: stream synchronize");
+    unsigned int word = 0, zero = 0;
+    e = hipMemcpyFromSymbol(&word, HIP_SYMBOL(moe::g_moe_err), sizeof(word), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return from_hip(e, "moe_check_device_errors: read error word");
+    if (word == 0) return ok();
+    e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_moe_err), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return from_hip(e, "moe_check_device_errors: clear error word");
+    return fail(MOE_ERR_DEVICE, "device error word 0x%x:%s%s%s%s%s", word,
+                (word & moe::kErrExpertRange) ? " expert id out of range;" : "",
+                (word & moe::kErrPairRange) ? " bucket offsets or pair ids out of range;" : "",
+                (word & moe::kErrLogitNonFinite) ? " non-finite router logit;" : "",
+                (word & moe::kErrActNonFinite) ? " non-finite activation;" : "",
+                (word & moe::kErrBarrierTimeout) ? " grid barrier timed out;" : "");
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// qblock.h — device-side unpacking of Q4_K and Q8_0 blocks, shared by the FFN
+// kernels and the dequantization test hook (so the hook exercises the exact
+// loads, nibble splits and scale decoding the FFN kernels use).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// A Q4_K "slice": 16 quant bytes of one super-block = 16 weights of sub-block
+// 2c (low nibbles) and 16 weights of sub-block 2c+1 (high nibbles), where the
+// slice index part = 2c + half (0..7) selects qs[32c + 16*half .. +16].
+//   low nibble  of byte i -> weight 64c + 16*half + i       (sub-block 2c)
+//   high nibble of byte i -> weight 64c + 32 + 16*half + i  (sub-block 2c+1)
+struct Q4KSlice {
+    uint32_t q[4];          // the 16 quant bytes
+    float d, dmin;          // super-block scales
+    int sc_lo, m_lo;        // sub-block 2c
+    int sc_hi, m_hi;        // sub-block 2c+1
+};
+
+__device__ __forceinline__ void q4k_load_slice(const uint8_t* __restrict__ blk, int part, Q4KSlice& s) {
+    const uint4 hv = *reinterpret_cast<const uint4*>(blk);
+    const uint4 qv = *reinterpret_cast<const uint4*>(blk + 16 + 16 * part);
+    const Q4KHead h{hv.x, hv.y, hv.z, hv.w};
+    s.q[0] = qv.x;
+    s.q[1] = qv.y;
+    s.q[2] = qv.z;
+    s.q[3] = qv.w;
+    s.d = q4k_d(h);
+    s.dmin = q4k_dmin(h);
+    const int c = part >> 1;
+    q4k_scale_min(h, 2 * c, s.sc_lo, s.m_lo);
+    q4k_scale_min(h, 2 * c + 1, s.sc_hi, s.m_hi);
+}
+
+// First weight index (within the super-block) of the low / high halves of a slice.
+__device__ __forceinline__ int q4k_slice_col_lo(int part) { return 64 * (part >> 1) + 16 * (part & 1); }
+__device__ __forceinline__ int q4k_slice_col_hi(int part) { return q4k_slice_col_lo(part) + 32; }
+
+__device__ __forceinline__ int q4k_slice_qlo(const Q4KSlice& s, int i) {
+    return (int)((s.q[i >> 2] >> (8 * (i & 3))) & 15u);
+}
+__device__ __forceinline__ int q4k_slice_qhi(const Q4KSlice& s, int i) {
+    return (int)((s.q[i >> 2] >> (8 * (i & 3) + 4)) & 15u);
+}
+
+// Q8_0 block: 2-byte aligned (34-byte blocks), read as 17 halfwords.
+struct Q80Block {
+    float d;
+    uint32_t q[8];  // 32 int8 quants, little-endian in 8 dwords
+};
+
+__device__ __forceinline__ void q80_load(const uint8_t* __restrict__ blk, Q80Block& b) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(blk);
+    b.d = f16_bits_to_f32(p[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b.q[i] = (uint32_t)p[1 + 2 * i] | ((uint32_t)p[2 + 2 * i] << 16);
+}
+
+__device__ __forceinline__ int q80_quant(const Q80Block& b, int i) {
+    return (int)(int8_t)((b.q[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+}
+
+}  // namespace moe

@@ -1,0 +1,281 @@
+// route.hip — top-k expert selection from router logits and per-expert bucketing.
+//
+// The router is a GPU stage on the pages ("Strata - the details", "How it works":
+// routers live in VRAM; the decode verify pass routes each token of a window).
+// Selection: descending logit, ties to the lower expert index, IEEE comparison
+// (-0 and +0 tie).  Weights: softmax over the k selected logits (renormalised),
+// or the plain softmax over all E taken at the selected slots.
+// Bucketing: pairs p = t*k + j grouped by expert, ascending p within an expert
+// (a stable counting sort), so every later stage is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Larger key <=> larger logit.  -0 is folded onto +0 so they tie; NaNs get a
+// place in the total order of bit patterns (and raise the error word).
+__device__ __forceinline__ uint32_t order_key(float v) {
+    uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ bool better(uint32_t ka, int ia, uint32_t kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// One wave selects the top-k of one token's E logits (E <= 64 * kMaxVpl).
+// Lane l owns experts l, l+64, ...  Returns, in lane j < k, the expert of slot j
+// and its weight; other lanes return -1 / 0.
+constexpr int kMaxVpl = 16;  // E <= 1024
+
+__device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool renorm, int& out_e,
+                          float& out_w) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t key[kMaxVpl];
+    bool bad = false;
+#pragma unroll
+    for (int v = 0; v < kMaxVpl; ++v) {
+        const int e = lane + kWave * v;
+        float x = (e < E) ? lg[e] : 0.0f;
+        bad |= (e < E) && !isfinite(x);
+        key[v] = (e < E) ? order_key(x) : 0u;
+    }
+    if (__any(bad)) {
+        if (lane == 0) raise_error(kErrLogitNonFinite);
+    }
+    uint32_t taken = 0;
+    int my_e = -1;
+    for (int j = 0; j < k; ++j) {
+        // best of this lane's remaining experts
+        uint32_t bk = 0;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int v = 0; v < kMaxVpl; ++v) {
+            const int e = lane + kWave * v;
+            if (e < E && !((taken >> v) & 1u) && better(key[v], e, bk, bi)) {
+                bk = key[v];
+                bi = e;
+            }
+        }
+        // butterfly arg-max over the wave
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint32_t ok = __shfl_xor(bk, off, kWave);
+            const int oi = __shfl_xor(bi, off, kWave);
+            if (better(ok, oi, bk, bi)) {
+                bk = ok;
+                bi = oi;
+            }
+        }
+        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+        if (lane == j) my_e = bi;
+    }
+    // weights
+    const float my_l = (lane < k) ? lg[my_e] : 0.0f;
+    const float top = __shfl(my_l, 0, kWave);
+    float sum;
+    if (renorm) {
+        const float ex = (lane < k) ? expf(my_l - top) : 0.0f;
+        sum = wave_sum(ex);
+        out_w = (lane < k) ? ex / sum : 0.0f;
+    } else {
+        float part = 0.0f;
+        for (int v = 0; v < kMaxVpl; ++v) {
+            const int e = lane + kWave * v;
+            if (e < E) part += expf(lg[e] - top);
+        }
+        sum = wave_sum(part);
+        out_w = (lane < k) ? expf(my_l - top) / sum : 0.0f;
+    }
+    out_e = my_e;
+}
+
+// Block-wide exclusive scan of n <= blockDim.x ints held one per thread.
+// Returns the exclusive prefix for this thread and writes the total.
+__device__ int block_exclusive_scan(int v, int* s_wave, int& total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int w = (lane < nwaves) ? s_wave[lane] : 0;
+        int wi = w;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(wi, off, kWave);
+            if (lane >= off) wi += o;
+        }
+        if (lane < nwaves) s_wave[lane] = wi - w;  // exclusive wave offsets
+        if (lane == nwaves - 1) s_wave[kWave] = wi;
+    }
+    __syncthreads();
+    const int res = s_wave[wave] + incl - v;
+    total = s_wave[kWave];
+    __syncthreads();
+    return res;
+}
+
+// ---------------------------------------------------------------------------
+// Small batches (T*k <= kSmallPairs): top-k and bucketing in one workgroup.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) route_small_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k, int renorm,
+                                                           RoutingPtrs r) {
+    __shared__ int s_idx[kSmallPairs];
+    __shared__ int s_count[1024];
+    __shared__ int s_off[1024];
+    __shared__ int s_wave[kWave + 1];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid & (kWave - 1);
+    const int nwaves = blockDim.x / kWave;
+    const int P = T * k;
+    for (int e = tid; e < E; e += blockDim.x) s_count[e] = 0;
+    for (int t = wave; t < T; t += nwaves) {
+        int e;
+        float w;
+        wave_topk(logits + (int64_t)t * E, E, k, renorm != 0, e, w);
+        if (lane < k) {
+            r.idx[t * k + lane] = e;
+            r.w[t * k + lane] = w;
+            s_idx[t * k + lane] = e;
+        }
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) atomicAdd(&s_count[s_idx[p]], 1);
+    __syncthreads();
+    // offsets and the active list: E <= 1024 = blockDim.x
+    int total_pairs, n_act;
+    const int c = (tid < E) ? s_count[tid] : 0;
+    const int off = block_exclusive_scan(c, s_wave, total_pairs);
+    const int apos = block_exclusive_scan((tid < E && c > 0) ? 1 : 0, s_wave, n_act);
+    if (tid < E) {
+        s_off[tid] = off;
+        r.count[tid] = c;
+        r.offset[tid] = off;
+        if (c > 0) r.active[apos] = tid;
+    }
+    if (tid == 0) {
+        r.offset[E] = total_pairs;
+        *r.n_active = n_act;
+    }
+    __syncthreads();
+    // stable placement: rank = earlier pairs of the same expert
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = s_idx[p];
+        int rank = 0;
+        for (int q = 0; q < p; ++q) rank += (s_idx[q] == e);
+        r.pair[s_off[e] + rank] = p;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large batches: one wave per token, then a tiled stable counting sort.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) route_tokens_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k, int renorm, int32_t* idx,
+                                                           float* w) {
+    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (t >= T) return;
+    int e;
+    float wt;
+    wave_topk(logits + (int64_t)t * E, E, k, renorm != 0, e, wt);
+    if (lane < k) {
+        idx[(int64_t)t * k + lane] = e;
+        w[(int64_t)t * k + lane] = wt;
+    }
+}
+
+// Per tile of kTilePairs pairs: histogram over experts and each pair's rank
+// among the earlier pairs of its expert inside the tile.
+__global__ void __launch_bounds__(kTilePairs) bucket_tile_kernel(const int32_t* __restrict__ idx, int P,
+                                                                 int E, int32_t* tile_hist,
+                                                                 int32_t* rank) {
+    __shared__ int s_e[kTilePairs];
+    __shared__ int s_h[1024];
+    const int tile = blockIdx.x, tid = threadIdx.x;
+    const int p = tile * kTilePairs + tid;
+    for (int e = tid; e < E; e += blockDim.x) s_h[e] = 0;
+    const int e = (p < P) ? idx[p] : -1;
+    s_e[tid] = e;
+    __syncthreads();
+    if (p < P) atomicAdd(&s_h[e], 1);
+    int rk = 0;
+    for (int q = 0; q < tid; ++q) rk += (s_e[q] == e);
+    if (p < P) rank[p] = rk;
+    __syncthreads();
+    for (int x = tid; x < E; x += blockDim.x) tile_hist[(int64_t)tile * E + x] = s_h[x];
+}
+
+// One workgroup: per-expert totals, offsets, tile bases and the active list.
+__global__ void __launch_bounds__(1024) bucket_scan_kernel(int n_tiles, int E, int P,
+                                                           int32_t* tile_hist, RoutingPtrs r) {
+    __shared__ int s_wave[kWave + 1];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int t = 0; t < n_tiles; ++t) {
+            const int h = tile_hist[(int64_t)t * E + e];
+            tile_hist[(int64_t)t * E + e] = run;
+            run += h;
+        }
+    }
+    int total, n_act;
+    const int off = block_exclusive_scan(e < E ? run : 0, s_wave, total);
+    const int apos = block_exclusive_scan((e < E && run > 0) ? 1 : 0, s_wave, n_act);
+    if (e < E) {
+        r.count[e] = run;
+        r.offset[e] = off;
+        if (run > 0) r.active[apos] = e;
+        for (int t = 0; t < n_tiles; ++t) tile_hist[(int64_t)t * E + e] += off;
+    }
+    if (e == 0) {
+        r.offset[E] = total;
+        *r.n_active = n_act;
+    }
+    (void)P;
+}
+
+__global__ void __launch_bounds__(256) bucket_scatter_kernel(const int32_t* __restrict__ idx, int P,
+                                                             int E, const int32_t* __restrict__ tile_base,
+                                                             const int32_t* __restrict__ rank,
+                                                             int32_t* pair) {
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= P) return;
+    const int tile = p / kTilePairs;
+    const int e = idx[p];
+    pair[tile_base[(int64_t)tile * E + e] + rank[p]] = p;
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, const RoutingPtrs& r,
+                        void* ws, hipStream_t s) {
+    const int P = T * k;
+    if (P <= kSmallPairs) {
+        route_small_kernel<<<1, 1024, 0, s>>>(logits, T, E, k, renorm, r);
+        return hipGetLastError();
+    }
+    const int n_tiles = (P + kTilePairs - 1) / kTilePairs;
+    int32_t* tile_hist = (int32_t*)ws;
+    int32_t* rank = tile_hist + (size_t)n_tiles * E;
+    route_tokens_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
+    bucket_tile_kernel<<<n_tiles, kTilePairs, 0, s>>>(r.idx, P, E, tile_hist, rank);
+    bucket_scan_kernel<<<1, 1024, 0, s>>>(n_tiles, E, P, tile_hist, r);
+    bucket_scatter_kernel<<<(P + 255) / 256, 256, 0, s>>>(r.idx, P, E, tile_hist, rank, r.pair);
+    return hipGetLastError();
+}
+
+size_t route_workspace_bytes(int T, int E, int k) {
+    const int64_t P = (int64_t)T * k;
+    if (P <= kSmallPairs) return 0;
+    const int64_t n_tiles = (P + kTilePairs - 1) / kTilePairs;
+    return (size_t)(n_tiles * E + P) * sizeof(int32_t);
+}
+
+}  // namespace moe

@@ -1,0 +1,317 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, through the C ABI.
+
+Exact: dequantized weights (bit for bit, as the "Strata v0.1.31" release notes
+require of GPU dequantizers), top-k indices, bucket lists, int8 activation codes.
+Toleranced: routing weights (1e-6), FFN outputs (2e-3 decode / 5e-3 int8 path,
+normwise per row).  Inputs are seeded synthetic layers with the workloads' shapes
+and value laws.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_moe_ffn_amd import synth
+
+from tests.gpu_helpers import TOL_DECODE, TOL_INT8, TOL_W, normwise_err, oracle_pairs, oracle_shared
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def qm():
+    import quantized_moe_ffn_amd as m
+    m.load_library()
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------- dequantization
+
+def _finite_scale_blocks(g, n, qt):
+    b = synth.q4k_blocks_np(g, n) if qt == oracle.Q4_K else synth.q80_blocks_np(g, n)
+    # random fp16 scale bit patterns, finite (subnormals included)
+    bits = g.integers(0, 0x7C00, size=(n, 2 if qt == oracle.Q4_K else 1), dtype=np.uint16)
+    bits |= (g.integers(0, 2, size=bits.shape, dtype=np.uint16) << 15)
+    b[:, : 2 * bits.shape[1]] = bits.view(np.uint8).reshape(n, -1)
+    return b
+
+
+@pytest.mark.parametrize("qt", [oracle.Q4_K, oracle.Q8_0])
+def test_dequant_bit_exact(qt):
+    m = qm()
+    from tests.golden import load_block
+    g = np.random.default_rng(100 + qt)
+    blocks = _finite_scale_blocks(g, 3000, qt)
+    if qt == oracle.Q4_K:
+        gold = np.stack([load_block(f) for f in ("q4k_block_a.txt", "q4k_block_b.txt", "q4k_block_c.txt",
+                                                  "q4k_block_e.txt")])
+    else:
+        gold = load_block("q80_block.txt")[None]
+    blocks = np.concatenate([gold, blocks])
+    n_w = blocks.shape[0] * oracle.BLOCK_WEIGHTS[qt]
+    _say("dequant", qt, blocks.shape)
+    dev = torch.from_numpy(blocks.copy()).to(DEV)
+    out = torch.empty(n_w, dtype=torch.float32, device=DEV)
+    m.moe_dequant_q(dev, qt, n_w, out)
+    m.moe_check_device_errors()
+    got = out.cpu().numpy()
+    ref = oracle.dequant(blocks, qt).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# --------------------------------------------------------------------------- routing
+
+def _route(m, logits_np, k, renorm=True):
+    T, E = logits_np.shape
+    r = m.Routing(T, E, k, DEV)
+    ws = torch.empty(max(1, m.moe_route_workspace_bytes(T, E, k)), dtype=torch.uint8, device=DEV)
+    lg = torch.from_numpy(np.ascontiguousarray(logits_np)).to(DEV)
+    m.moe_route_topk(lg, k, r, renorm, ws)
+    m.moe_check_device_errors()
+    return r
+
+
+def _check_routing(r, logits_np, k, renorm=True):
+    E = logits_np.shape[1]
+    idx, w = oracle.route_topk(logits_np, k, renorm)
+    b = oracle.bucket(idx, E)
+    assert np.array_equal(r.idx.cpu().numpy(), idx)
+    assert np.abs(r.w.cpu().numpy() - w).max() <= TOL_W
+    assert np.array_equal(r.count.cpu().numpy(), b["count"])
+    assert np.array_equal(r.offset.cpu().numpy(), b["offset"])
+    assert np.array_equal(r.pair.cpu().numpy(), b["pair"])
+    na = int(r.n_active.cpu().numpy()[0])
+    assert na == b["n_active"]
+    assert np.array_equal(r.active.cpu().numpy()[:na], b["active"])
+
+
+@pytest.mark.parametrize("T,E,k,zipf", [
+    (1, 8, 2, 0.0), (4, 8, 2, 0.0), (1, 256, 8, 0.0), (3, 256, 8, 0.0), (1, 512, 10, 0.0),
+    (32, 256, 8, 0.0), (33, 256, 8, 0.0), (1000, 300, 5, 0.0), (4096, 256, 8, 1.1), (2, 8, 8, 0.0),
+    (7, 1024, 16, 0.0), (5, 65, 1, 0.0),
+])
+def test_route_matches_oracle(T, E, k, zipf):
+    m = qm()
+    _say("route", T, E, k, zipf)
+    lg = synth.logits_np(synth.rng(200, T, E, k), T, E, zipf)
+    r = _route(m, lg, k)
+    _check_routing(r, lg, k)
+
+
+def test_route_ties_signed_zeros_and_plain_softmax():
+    m = qm()
+    g = np.random.default_rng(201)
+    lg = g.integers(-2, 3, size=(40, 64)).astype(np.float32)
+    lg[lg == 0] = np.where(g.random(np.count_nonzero(lg == 0)) < 0.5, -0.0, 0.0).astype(np.float32)
+    for k in (1, 3, 8, 16):
+        _say("route ties", k)
+        _check_routing(_route(m, lg, k), lg, k)
+    lg2 = synth.logits_np(synth.rng(202), 300, 128)   # large path, plain softmax
+    _check_routing(_route(m, lg2, 6, renorm=False), lg2, 6, renorm=False)
+
+
+# --------------------------------------------------------------------------- activation quantisation
+
+def test_quantize_act_bit_exact():
+    m = qm()
+    g = np.random.default_rng(300)
+    x = (g.standard_normal((37, 2048)) * g.uniform(1e-3, 1e3, (37, 1))).astype(np.float32)
+    x[3, 256:512] = 0.0
+    x[4, :256] = np.round(x[4, :256])
+    x[4, 0] = 127.0
+    x[4, 1:5] = [2.5, -2.5, 0.5, 3.5]
+    xt = torch.from_numpy(x).to(DEV)
+    xq = torch.empty((37, 2048), dtype=torch.int8, device=DEV)
+    xd = torch.empty((37, 8), dtype=torch.float32, device=DEV)
+    m.moe_quantize_act(xt, xq, xd)
+    m.moe_check_device_errors()
+    rq, rd = oracle.quantize_act(x)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint32), rd.view(np.uint32))
+
+
+def test_quantize_act_nonfinite_raises_error_word():
+    m = qm()
+    x = np.ones((2, 256), np.float32)
+    x[1, 7] = np.inf
+    xt = torch.from_numpy(x).to(DEV)
+    xq = torch.empty((2, 256), dtype=torch.int8, device=DEV)
+    xd = torch.empty((2, 1), dtype=torch.float32, device=DEV)
+    m.moe_quantize_act(xt, xq, xd)
+    with pytest.raises(m.MoeError, match="non-finite activation"):
+        m.moe_check_device_errors()
+    assert np.all(xq.cpu().numpy()[1] == 0) and xd.cpu().numpy()[1, 0] == 0.0
+    m.moe_check_device_errors()   # cleared
+
+
+# --------------------------------------------------------------------------- whole layer
+
+def _layer(name, **over):
+    from quantized_moe_ffn_amd import layers
+    w = synth.WORKLOADS[name]
+    if over:
+        w = synth.Workload(**{**w.__dict__, **over})
+    return layers.make_layer(w, seed=0, index=0, device=DEV), w
+
+
+def _run_layer(m, dl, logits, x, k, flags):
+    lg = torch.from_numpy(np.ascontiguousarray(logits)).to(DEV)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    bufs = m.forward(dl.layer, lg, xt, k, flags=flags)
+    m.moe_check_device_errors()
+    return bufs
+
+
+def _check_layer(m, dl, w, logits, x, bufs, mode, tol, token_subset=None):
+    k = w.top_k
+    T = x.shape[0]
+    idx, wts = oracle.route_topk(logits, k)
+    assert np.array_equal(bufs.routing.idx.cpu().numpy(), idx)
+    assert np.abs(bufs.routing.w.cpu().numpy() - wts).max() <= TOL_W
+    toks = np.arange(T) if token_subset is None else np.asarray(token_subset)
+    pe = idx[toks].reshape(-1)
+    pt = np.repeat(toks, k)
+    y_ref, hb = oracle_pairs(dl, pe, pt, x, mode)
+    pairs = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    y_got = bufs.y_pair.cpu().numpy()[pairs]
+    ep = normwise_err(y_got, y_ref)
+    ys = None
+    if w.shared:
+        ys = oracle_shared(dl, hb, toks, x, mode)
+        es = normwise_err(bufs.y_shared.cpu().numpy()[toks], ys)
+        assert es.max() <= tol, es.max()
+    out_ref = oracle.combine(y_ref, wts[toks], ys)
+    eo = normwise_err(bufs.out.cpu().numpy()[toks], out_ref)
+    _say("  y_pair err max %.3e  out err max %.3e" % (ep.max(), eo.max()))
+    assert ep.max() <= tol, ep.max()
+    assert eo.max() <= tol, eo.max()
+
+
+@pytest.mark.parametrize("name", ["tiny", "sage_decode", "mtp_window", "flash_next_decode"])
+def test_decode_layer_parity(name):
+    m = qm()
+    _say("decode layer", name)
+    dl, w = _layer(name)
+    from quantized_moe_ffn_amd import layers
+    for replay in range(3):
+        logits, x = layers.inputs_np(w, seed=0, index=0, replay=replay)
+        bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE)
+        _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
+
+
+@pytest.mark.parametrize("over", [dict(hidden=256, inter=768, n_experts=3, top_k=3, tokens=5),
+                                  dict(hidden=768, inter=256, n_experts=70, top_k=4, tokens=9, qt_down=oracle.Q8_0),
+                                  dict(hidden=512, inter=512, n_experts=16, top_k=2, tokens=1, qt_gate=oracle.Q8_0,
+                                       qt_up=oracle.Q8_0)])
+def test_decode_ragged_shapes(over):
+    m = qm()
+    _say("decode ragged", over)
+    dl, w = _layer("tiny", **over)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=1)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE)
+    _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
+
+
+def test_int8_path_tiny_full():
+    m = qm()
+    _say("int8 tiny T=96")
+    dl, w = _layer("tiny", tokens=96)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=2)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8)
+    xq, xd = oracle.quantize_act(x)
+    assert np.array_equal(bufs.xq.cpu().numpy(), xq)
+    _check_layer(m, dl, w, logits, x, bufs, 1, TOL_INT8)
+
+
+def test_int8_prefill_chunk_sampled():
+    m = qm()
+    _say("int8 prefill chunk T=4096 (sampled tokens)")
+    dl, w = _layer("prefill_chunk")
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=0)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8)
+    _check_routing(bufs.routing, logits, w.top_k)
+    toks = np.array([0, 1, 777, 2048, 4000, 4095])
+    _check_layer(m, dl, w, logits, x, bufs, 1, TOL_INT8, token_subset=toks)
+
+
+def test_integer_exact_layer_is_bitwise():
+    """Gate weights all 1/8, up row i all (i mod 4), down row o all (o mod 3), x = 1 (H = I = 256):
+    g = 32 (so silu(g) = g in fp32), h_i = 8192 (i mod 4), y_o = (o mod 3) * 8192 * 384.  Every
+    partial sum is an integer-valued float below 2^24, so the GPU result must equal the closed form
+    exactly, whatever the summation order."""
+    m = qm()
+    H, I = 256, 256
+    def rows(n, cols, q_of, d_bits=0x3C00):
+        nb = cols // 256
+        return np.stack([np.tile(oracle.q4k_pack(d_bits, 0, np.ones(8), np.zeros(8), np.full(256, q_of(r))), nb)
+                         for r in range(n)])
+    gate = rows(I, H, lambda r: 1, d_bits=0x3000)[None]     # d = 2^-3
+    up = rows(I, H, lambda r: r % 4)[None]
+    down = rows(H, I, lambda r: r % 3)[None]
+    mats = [m.QMatrix(torch.from_numpy(np.ascontiguousarray(a)).to(DEV), m.MOE_Q4_K, c)
+            for a, c in ((gate, H), (up, H), (down, I))]
+    layer = m.Layer(*mats)
+    x = torch.ones((1, H), dtype=torch.float32, device=DEV)
+    lg = torch.zeros((1, 1), dtype=torch.float32, device=DEV)
+    bufs = m.forward(layer, lg, x, 1, flags=m.MOE_FFN_DECODE)
+    m.moe_check_device_errors()
+    expect = np.array([(o % 3) * 8192 * 384 for o in range(H)], np.float32)
+    assert 2 * 8192 * 384 < 2 ** 24
+    assert np.array_equal(bufs.out.cpu().numpy()[0], expect)
+    assert np.array_equal(bufs.y_pair.cpu().numpy()[0], expect)
+
+
+def test_determinism_and_batch_invariance():
+    m = qm()
+    dl, w = _layer("mtp_window")
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=3)
+    a = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE).out.cpu().numpy()
+    b = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE).out.cpu().numpy()
+    assert np.array_equal(a, b)
+    for t in range(3):
+        one = _run_layer(m, dl, logits[t:t + 1], x[t:t + 1], w.top_k, m.MOE_FFN_DECODE).out.cpu().numpy()
+        assert np.array_equal(one[0], a[t])
+
+
+def test_corrupted_routing_sets_error_word():
+    """A routing buffer handed in with an expert id out of range is caught on the device:
+    the kernel skips the slot (no out-of-bounds access) and raises the error word."""
+    m = qm()
+    dl, w = _layer("tiny")
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=4)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE)
+    bufs.routing.active[0] = w.n_experts + 5
+    xt = torch.from_numpy(x).to(DEV)
+    m.moe_expert_ffn_q(dl.layer, bufs.routing, x.shape[0], w.top_k, bufs.y_pair, x=xt, flags=m.MOE_FFN_DECODE,
+                       workspace=bufs.ffn_ws)
+    with pytest.raises(m.MoeError, match="expert id out of range"):
+        m.moe_check_device_errors()
+    m.moe_check_device_errors()
+
+
+def test_combine_shared_scale_and_one_hot():
+    m = qm()
+    g = np.random.default_rng(500)
+    T, k, H = 3, 4, 512
+    y = g.standard_normal((T * k, H)).astype(np.float32)
+    wts = np.zeros((T, k), np.float32)
+    wts[0, 1] = wts[1, 3] = wts[2, 0] = 1.0
+    ys = g.standard_normal((T, H)).astype(np.float32)
+    sc = np.array([0.5, 1.0, 2.0], np.float32)
+    out = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    m.moe_combine(torch.from_numpy(y).to(DEV), torch.from_numpy(wts).to(DEV), out)
+    assert np.array_equal(out.cpu().numpy(), y[[1, 7, 8]])
+    m.moe_combine(torch.from_numpy(y).to(DEV), torch.from_numpy(wts).to(DEV), out, torch.from_numpy(ys).to(DEV),
+                  torch.from_numpy(sc).to(DEV))
+    ref = oracle.combine(y.astype(np.float64), wts.astype(np.float64), ys.astype(np.float64), sc.astype(np.float64))
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-6 * np.abs(ref).max()
