@@ -70,6 +70,7 @@ def main() -> int:
     ap.add_argument("--replays", type=int, default=8, help="distinct input sets cycled over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", choices=["on", "off"], default="on", help="replay each step as a HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -110,15 +111,15 @@ def main() -> int:
             row.append((torch.from_numpy(lg).to(dev), torch.from_numpy(x).to(dev)))
         inputs.append(row)
     bufs = qm.LayerBuffers(stack[0].layer, T, k, flags, device=dev)
-    stream = torch.cuda.current_stream()
 
-    def step(s):
-        row = inputs[s % R]
+    def run_replay(r, stream):
+        row = inputs[r]
         for l in range(L):
             lg, x = row[l]
             qm.forward(stack[l].layer, lg, x, k, bufs, flags=flags, stream=stream)
 
-    # unique experts per (replay, layer): algorithmic bytes of each layer's FFN call
+    # unique experts per (replay, layer): algorithmic bytes of each layer call
+    stream = torch.cuda.current_stream()
     uniq = np.zeros((R, L), np.int64)
     for r in range(R):
         for l in range(L):
@@ -128,8 +129,29 @@ def main() -> int:
     qm.moe_check_device_errors()
     per_expert = w.expert_bytes()
     shared_bytes = w.expert_bytes() if w.shared else 0
-    bytes_rl = uniq * per_expert + shared_bytes           # weight bytes per layer call
-    act_bytes = T * H * 4 + T * k * 4 * 2 + T * H * 4     # x in, routing, out (small next to weights)
+    bytes_rl = uniq * per_expert + shared_bytes           # expert weight bytes each layer call streams
+
+    graphs = None
+    if args.graph == "on":
+        log("[bench] capturing %d graphs of %d layer calls" % (R, L))
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graphs = []
+        with torch.cuda.stream(cap):
+            run_replay(0, cap)           # warm the allocator/library on the capture stream
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    run_replay(r, cap)
+                graphs.append(g)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+
+    def step(s):
+        if graphs is not None:
+            graphs[s % R].replay()
+        else:
+            run_replay(s % R, stream)
 
     log("[bench] warmup %d steps" % args.warmup)
     for s in range(args.warmup):
@@ -137,7 +159,7 @@ def main() -> int:
     torch.cuda.synchronize()
     qm.moe_check_device_errors()
 
-    log("[bench] timing %d steps x %d layers" % (args.steps, L))
+    log("[bench] timing %d steps x %d layers (graphs %s)" % (args.steps, L, args.graph))
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -152,49 +174,28 @@ def main() -> int:
     ms_per_step = ms_total / args.steps
     tokens = T * L * args.steps
     value = tokens / (ms_total / 1e3)
-    step_bytes = sum(int(bytes_rl[(args.warmup + s) % R].sum()) for s in range(args.steps))
-    log("[bench] %.3f ms/step (wall %.3f ms/step), %.0f layer-tokens/s, %.1f GB/s end to end"
-        % (ms_per_step, wall * 1e3 / args.steps, value, step_bytes / (ms_total / 1e3) / 1e9))
+    n_launch = L * args.steps
+    avg_us = ms_total * 1e3 / n_launch
+    dom_bytes = sum(int(bytes_rl[(args.warmup + s) % R].sum()) for s in range(args.steps))
+    log("[bench] %.3f ms/step (wall %.3f ms/step), %.0f layer-tokens/s, %.2f us per layer call"
+        % (ms_per_step, wall * 1e3 / args.steps, value, avg_us))
 
-    # dominant call: the expert FFN, timed per launch with events on its stream
-    log("[bench] timing the expert FFN call per launch")
-    n_launch, dur_ms, dom_bytes = 0, 0.0, 0
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-    for r in range(R):
-        for l in range(L):
-            lg, x = inputs[r][l]
-            qm.moe_route_topk(lg, k, bufs.routing, True, bufs.route_ws, stream)
-            if flags == qm.MOE_FFN_INT8:
-                qm.moe_quantize_act(x, bufs.xq, bufs.xd, stream)
-            a, b = evs[l]
-            a.record(stream)
-            qm.moe_expert_ffn_q(stack[l].layer, bufs.routing, T, k, bufs.y_pair,
-                                x=x if flags == qm.MOE_FFN_DECODE else None,
-                                xq=bufs.xq if flags == qm.MOE_FFN_INT8 else None,
-                                xd=bufs.xd if flags == qm.MOE_FFN_INT8 else None, flags=flags,
-                                y_shared=bufs.y_shared, workspace=bufs.ffn_ws, stream=stream)
-            b.record(stream)
-        torch.cuda.synchronize()
-        for l in range(L):
-            dur_ms += evs[l][0].elapsed_time(evs[l][1])
-            dom_bytes += int(bytes_rl[r, l])
-            n_launch += 1
-    qm.moe_check_device_errors()
-    avg_ms = dur_ms / n_launch
+    # dominant call: the layer call (moe_forward), whose average duration is the
+    # timed region divided by the number of calls in it
     if w.int8_path:
         ops = 2.0 * T * k * 3 * H * I + (2.0 * T * 3 * H * I if w.shared else 0.0)
-        achieved = ops / (avg_ms / 1e3) / 1e12
+        achieved = ops / (avg_us / 1e6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profiles(w.name),
-                "kernel": "moe_expert_ffn_q (int8 path)", "ops_per_launch": ops,
-                "avg_launch_us": round(avg_ms * 1e3, 2)}
+                "kernel": "moe_forward (int8 path: route, quantize, gate/up, requantize, down, combine)",
+                "ops_per_launch": ops, "avg_launch_us": round(avg_us, 3)}
     else:
-        achieved = dom_bytes / (dur_ms / 1e3) / 1e9
+        achieved = dom_bytes / (ms_total / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(w.name),
-                "kernel": "moe_expert_ffn_q (decode path)",
-                "bytes_per_launch": round(dom_bytes / n_launch), "avg_launch_us": round(avg_ms * 1e3, 2)}
-    log("[bench] expert FFN call: %.2f us per launch, %s %s" % (avg_ms * 1e3, roof["achieved"], roof["unit"]))
+                "kernel": "moe_forward (decode: route+gate/up+SiLU kernel, down+combine kernel)",
+                "bytes_per_launch": round(dom_bytes / n_launch), "avg_launch_us": round(avg_us, 3)}
+    log("[bench] layer call: %.2f us, %s %s" % (avg_us, roof["achieved"], roof["unit"]))
 
     cpu = None
     parity = None
@@ -217,8 +218,8 @@ def main() -> int:
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "inter": I,
                    "shared_expert": w.shared, "layers": L, "replays": R,
                    "formats": {"gate": fmt(w.qt_gate), "up": fmt(w.qt_up), "down": fmt(w.qt_down)},
-                   "parallelism": "single GPU"},
-        "hbm_GBps_end_to_end": round(step_bytes / (ms_total / 1e3) / 1e9, 1),
+                   "parallelism": "single GPU", "graphs": args.graph},
+        "hbm_GBps_end_to_end": round(dom_bytes / (ms_total / 1e3) / 1e9, 1),
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity_max_normwise_err": parity,
@@ -242,10 +243,12 @@ def cpu_baseline(w, stack, inputs, bufs, flags, k, budget_s):
     tok_sample = np.arange(T) if T <= 64 else np.linspace(0, T - 1, 16).round().astype(np.int64)
     mode = 1 if w.int8_path else 0
     spent, tokens_done, layers_done, errs = 0.0, 0, 0, []
-    for l, dl in enumerate(stack):
+    items = [(r, l) for r in range(len(inputs)) for l in range(len(stack))]
+    for r, l in items:
+        dl = stack[l]
         if spent >= budget_s:
             break
-        lg_t, x_t = inputs[0][l]
+        lg_t, x_t = inputs[r][l]
         qm.forward(dl.layer, lg_t, x_t, k, bufs, flags=flags)
         torch.cuda.synchronize()
         gpu_out = bufs.out.cpu().numpy()[tok_sample]
@@ -281,10 +284,11 @@ def cpu_baseline(w, stack, inputs, bufs, flags, k, budget_s):
         layers_done += 1
         den = np.abs(out).max(axis=1)
         errs.append(float((np.abs(gpu_out - out).max(axis=1) / den).max()))
-        log("[bench] cpu oracle: layer %d done, %.1f s spent" % (l, spent))
+        if layers_done % 20 == 0:
+            log("[bench] cpu oracle: %d layer calls done, %.1f s spent" % (layers_done, spent))
     cpu = {"value": round(tokens_done / spent, 3), "unit": "layer-tokens/s", "cores": oracle.threads(),
            "kind": "oracle",
-           "sample": "%d layer(s) x %d token(s) of %s, route+bucket+FFN+combine in fp64 (%.1f s)"
+           "sample": "%d layer call(s) x %d token(s) of %s, route+bucket+FFN+combine in fp64 (%.1f s)"
                      % (layers_done, len(tok_sample), w.name, spent)}
     return cpu, (max(errs) if errs else None)
 

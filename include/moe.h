@@ -172,6 +172,27 @@ moe_status moe_combine(const float* y_pair, const float* w, const float* y_share
                        const float* shared_scale, int32_t T, int32_t k, int32_t H, float* out,
                        hipStream_t stream);
 
+/* Bytes of device workspace moe_forward needs (for the path ffn_flags selects). */
+size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t ffn_flags);
+
+/* The whole layer: routing (as moe_route_topk, results written to r), expert
+ * FFN (as moe_expert_ffn_q, from fp32 x; on the int8 path x is quantized with
+ * moe_quantize_act's rule into the workspace) and combine (as moe_combine),
+ * enqueued on one stream.  For decode batches (T <= 4, T*k <= 64, Q4_K
+ * gate/up with H/256 in {1,2,4,8,10}, down rows of 8, 16 or 32 32-weight
+ * blocks, 16-byte aligned banks) the layer runs as two kernels: routing fused
+ * into the gate/up kernel (recomputed per workgroup) and the combine fused
+ * into the down kernel (formed in slot order in LDS); other shapes run the
+ * separate stages.  Same results contract as the three calls (bitwise
+ * deterministic; combine in slot order).  y_pair [T*k][H] is always written;
+ * y_shared [T][H] is required iff the layer has a shared expert;
+ * shared_scale [T] or NULL.  x must be 16-byte aligned.  Checks: those of
+ * moe_route_topk and moe_expert_ffn_q; ws_bytes >= moe_forward_workspace_bytes. */
+moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
+                       uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
+                       float* y_shared, const float* shared_scale, float* out, void* workspace,
+                       size_t ws_bytes, hipStream_t stream);
+
 /* Test hook: dequantize n_weights weights of contiguous blocks to fp32 with the
  * same device unpacking helpers the FFN kernels use.  Each value is the exact
  * d*sc*q - dmin*m (Q4_K) or d*q (Q8_0) rounded once to fp32.  n_weights must

@@ -7,9 +7,10 @@ kernels.  There is no CPU fallback: if ``libmoe.so`` is missing or cannot be
 loaded, the first call raises.
 
 Entry points keep the C names: ``moe_route_topk``, ``moe_quantize_act``,
-``moe_expert_ffn_q``, ``moe_combine``, ``moe_dequant_q``,
+``moe_expert_ffn_q``, ``moe_combine``, ``moe_forward``, ``moe_dequant_q``,
 ``moe_check_device_errors``, ``moe_last_error``, ``moe_abi_version``,
-``moe_route_workspace_bytes``, ``moe_ffn_workspace_bytes``.
+``moe_route_workspace_bytes``, ``moe_ffn_workspace_bytes``,
+``moe_forward_workspace_bytes``.
 """
 from __future__ import annotations
 
@@ -33,7 +34,7 @@ BLOCK_BYTES = {MOE_Q4_K: 144, MOE_Q8_0: 34}
 EXPORTS = (
     "moe_abi_version", "moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
     "moe_quantize_act", "moe_ffn_workspace_bytes", "moe_expert_ffn_q", "moe_combine",
-    "moe_dequant_q", "moe_check_device_errors",
+    "moe_dequant_q", "moe_check_device_errors", "moe_forward_workspace_bytes", "moe_forward",
 )
 
 
@@ -91,6 +92,11 @@ def load_library(path: str = LIB_PATH):
     lib.moe_combine.restype = st
     lib.moe_dequant_q.argtypes = [P, i32, i64, P, P]
     lib.moe_dequant_q.restype = st
+    lib.moe_forward_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer), i32, i32, u32]
+    lib.moe_forward_workspace_bytes.restype = sz
+    lib.moe_forward.argtypes = [ctypes.POINTER(moe_layer), P, P, i32, i32, u32, u32, ctypes.POINTER(moe_routing),
+                                P, P, P, P, P, sz, P]
+    lib.moe_forward.restype = st
     lib.moe_check_device_errors.argtypes = [P]
     lib.moe_check_device_errors.restype = st
     _lib = lib
@@ -224,6 +230,21 @@ def moe_dequant_q(blocks, qtype: int, n_weights: int, out, stream=None):
            "moe_dequant_q")
 
 
+def moe_forward_workspace_bytes(layer: Layer, T: int, k: int, flags: int = MOE_FFN_AUTO) -> int:
+    return int(load_library().moe_forward_workspace_bytes(ctypes.byref(layer.struct()), T, k, flags))
+
+
+def moe_forward(layer: Layer, logits, x, k: int, routing: Routing, y_pair, out, y_shared=None, shared_scale=None,
+                renorm: bool = True, flags: int = MOE_FFN_AUTO, workspace=None, stream=None):
+    T = x.shape[0]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().moe_forward(ctypes.byref(layer.struct()), _ptr(logits), _ptr(x), T, k,
+                                    MOE_ROUTE_RENORM if renorm else 0, flags, ctypes.byref(routing.struct()),
+                                    _ptr(y_pair), _ptr(y_shared), _ptr(shared_scale), _ptr(out), _ptr(workspace),
+                                    nbytes, _stream(stream))
+    _check(st, "moe_forward")
+
+
 def moe_check_device_errors(stream=None):
     _check(load_library().moe_check_device_errors(_stream(stream)), "moe_check_device_errors")
 
@@ -247,14 +268,22 @@ class LayerBuffers:
         self.xq = torch.empty((T, H), dtype=torch.int8, device=device)
         self.xd = torch.empty((T, H // 256), dtype=torch.float32, device=device)
         self.out = torch.empty((T, H), dtype=torch.float32, device=device)
+        fwd = moe_forward_workspace_bytes(layer, T, k, flags)
+        self.fwd_ws = torch.empty(max(fwd, 256), dtype=torch.uint8, device=device)
 
 
 def forward(layer: Layer, logits, x, k: int, bufs: LayerBuffers | None = None, flags: int = MOE_FFN_AUTO,
-            renorm: bool = True, shared_scale=None, stream=None) -> LayerBuffers:
-    """route -> (quantize) -> expert FFN -> combine, all enqueued on one stream."""
+            renorm: bool = True, shared_scale=None, stream=None, fused: bool = True) -> LayerBuffers:
+    """The whole layer on one stream.  fused=True: one moe_forward call (two kernels
+    for decode batches); fused=False: the separate calls route -> (quantize) ->
+    expert FFN -> combine."""
     T = x.shape[0]
     if bufs is None:
         bufs = LayerBuffers(layer, T, k, flags, device=x.device)
+    if fused:
+        moe_forward(layer, logits, x, k, bufs.routing, bufs.y_pair, bufs.out, bufs.y_shared, shared_scale, renorm,
+                    flags, bufs.fwd_ws, stream)
+        return bufs
     path = flags if flags != MOE_FFN_AUTO else (MOE_FFN_DECODE if T <= 64 else MOE_FFN_INT8)
     moe_route_topk(logits, k, bufs.routing, renorm, bufs.route_ws, stream)
     if path == MOE_FFN_INT8:

@@ -66,18 +66,62 @@ __device__ __forceinline__ int q4k_quant(const uint32_t* qs32, int i) {
     return hi ? (int)(b >> 4) : (int)(b & 15u);
 }
 
-// Wave64 butterfly sum: every lane ends with the same total, summed in the
-// same tree order on every run (deterministic).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+// DPP lane moves (no LDS round trip).  Lanes outside row_mask, or whose
+// source is invalid, read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+}
+
+// Sum over aligned segments of SEG lanes (SEG in 4..64), in a fixed order:
+// quad swaps, then half-row and row mirrors, then row broadcasts.  The segment
+// total is valid in every lane for SEG <= 16, in the odd 16-lane row of each
+// 32-lane half for SEG == 32, and in lanes 48..63 for SEG == 64; lane
+// (segment end - 1) always holds it.
+template <int SEG>
+__device__ __forceinline__ float segment_sum(float v) {
+    static_assert(SEG == 4 || SEG == 8 || SEG == 16 || SEG == 32 || SEG == 64, "segment size");
+    v += dpp_f<0xB1>(v);                       // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);                       // quad_perm [2,3,0,1]
+    if constexpr (SEG >= 8) v += dpp_f<0x141>(v);        // row_half_mirror
+    if constexpr (SEG >= 16) v += dpp_f<0x140>(v);       // row_mirror
+    if constexpr (SEG >= 32) v += dpp_f<0x142, 0xA>(v);  // row_bcast15 into rows 1, 3
+    if constexpr (SEG >= 64) v += dpp_f<0x143, 0xC>(v);  // row_bcast31 into rows 2, 3
     return v;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Wave64 maximum of unsigned values, the same value in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u<0xB1>(v));
+    v = max(v, dpp_u<0x4E>(v));
+    v = max(v, dpp_u<0x141>(v));
+    v = max(v, dpp_u<0x140>(v));
+    v = max(v, dpp_u<0x142, 0xA>(v));
+    v = max(v, dpp_u<0x143, 0xC>(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Wave64 sum, the same value in every lane, in a fixed order (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+    v = segment_sum<64>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
     return v;
+}
+
+// Byte N of a dword as fp32 (one v_cvt_f32_ubyteN).
+template <int N>
+__device__ __forceinline__ float ubyte_f32(uint32_t v) {
+    return (float)((v >> (8 * N)) & 0xFFu);
 }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }

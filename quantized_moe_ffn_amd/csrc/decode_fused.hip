@@ -1,0 +1,621 @@
+// decode_fused.hip — the decode-sized layer (T <= 4 tokens) in two kernels:
+//
+//   K1 route + gate/up + SiLU: every workgroup recomputes the top-k of the (at
+//      most 4) tokens from the router logits (one wave per token), derives the
+//      expert buckets in LDS, then streams its tile of gate and up rows of one
+//      expert and writes h = silu(W_gate x) * (W_up x) for the tokens routed to
+//      it.  Workgroup 0 also writes the routing results (idx, w, count, offset,
+//      pair, active, n_active).
+//   K2 down + combine: a workgroup owns a tile of output rows for EVERY expert
+//      of the layer (waves split the experts), so the routing-weighted sum over
+//      the k slots (plus the shared expert) is formed in LDS in slot order and
+//      written once: no float atomics, bitwise deterministic.
+//
+// Two launches per layer instead of four: on MI355X a small kernel costs a few
+// microseconds of launch and drain, as much as streaming the ~14 MB of experts
+// one Sage-A1.5-sized token touches ("Strata-Sage-A1.5-GGUF": 256 experts,
+// top-8; Flash-Next, "Strata: a 125B MoE at 94 tok/s": 10 routed + 1 shared of
+// 512).  The pages' own decode work moved the same way: fewer launches and
+// host round trips in the verify pass ("Strata v0.1.39" release notes, Decode
+// #646), register reductions in the decode chain ("Strata-Sage-A1.5-GGUF"
+// round-2 table).
+//
+// Weight streaming (K1): a "slice" is 16 quant bytes of a Q4_K super-block =
+// 16 weights of sub-block 2c (low nibbles) and 16 of sub-block 2c+1 (high
+// nibbles).  A unit of W waves covers P rows x (8*NB) slices per pass with
+// 64*W == P*8*NB, so every lane keeps the same 32 columns for the whole kernel
+// and holds those activations in registers (no LDS traffic for x).  Per slice a
+// lane issues two 16-byte loads (super-block header + quants), decodes the two
+// 6-bit scale/min pairs it needs and applies them once per 16 weights:
+//   partial = d*(sc_lo*S_lo + sc_hi*S_hi) - dmin*(m_lo*X_lo + m_hi*X_hi).
+#include "common.h"
+#include "kernels.h"
+#include "qblock.h"
+
+namespace moe {
+
+constexpr int kDecMaxT = 4;      // tokens handled by the fused decode path
+constexpr int kDecMaxPairs = 64; // T*k
+
+template <int A, int B>
+struct Gcd {
+    static constexpr int value = Gcd<B, A % B>::value;
+};
+template <int A>
+struct Gcd<A, 0> {
+    static constexpr int value = A;
+};
+
+// Routing of up to kDecMaxT tokens, computed redundantly by every workgroup.
+// Expert slots u = 0 .. n_uniq-1 each own the pairs pair[uoff[u] .. uoff[u+1]).
+// For one token the slots are the k selections in slot order (pair u = u); for
+// several tokens they are the distinct experts in ascending order.
+struct DecRoute {
+    int sel[kDecMaxPairs];       // expert of pair p = t*k + j (slot order)
+    float w[kDecMaxPairs];
+    int pair[kDecMaxPairs];
+    int uniq[kDecMaxPairs];
+    int uoff[kDecMaxPairs + 1];
+    int n_uniq;
+};
+
+// Waves 0..T-1 select the top-k of token t; wave 0 then builds the slots.
+// Ends with __syncthreads().
+template <int V>
+__device__ __forceinline__ void dec_route(const float* __restrict__ logits, int T, int E, int k, int renorm, DecRoute& R) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    int e = -1;
+    float w = 0.f;
+    if (wave < T) {
+        wave_topk<V>(logits + (int64_t)wave * E, E, k, renorm != 0, e, w);
+        if (lane < k) {
+            R.sel[wave * k + lane] = e;
+            R.w[wave * k + lane] = w;
+        }
+    }
+    if (T == 1) {
+        if (wave == 0) {
+            if (lane < k) {
+                R.uniq[lane] = e;
+                R.uoff[lane] = lane;
+                R.pair[lane] = lane;
+            }
+            if (lane == 0) {
+                R.n_uniq = k;
+                R.uoff[k] = k;
+            }
+        }
+        __syncthreads();
+        return;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int P = T * k;
+        const int ep = lane < P ? R.sel[lane] : 0x7FFFFFFF;
+        int below, same_before, ubelow, n_uniq;
+        bool first;
+        wave_buckets(ep, P, below, same_before, first, ubelow, n_uniq);
+        if (lane < P) {
+            R.pair[below + same_before] = lane;
+            if (first) {
+                R.uniq[ubelow] = ep;
+                R.uoff[ubelow] = below;
+            }
+        }
+        if (lane == 0) {
+            R.n_uniq = n_uniq;
+            R.uoff[n_uniq] = P;
+        }
+    }
+    __syncthreads();
+}
+
+// Workgroup 0 of K1 publishes the routing results in the layout moe_route_topk
+// writes (active experts ascending, pairs grouped by expert).
+__device__ __forceinline__ void dec_publish(const DecRoute& R, int T, int E, int k, const RoutingPtrs& r) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int P = T * k;
+    if (wave == 0) {
+        const int ep = lane < P ? R.sel[lane] : 0x7FFFFFFF;
+        int below, same_before, ubelow, n_uniq;
+        bool first;
+        wave_buckets(ep, P, below, same_before, first, ubelow, n_uniq);
+        if (lane < P) {
+            r.idx[lane] = ep;
+            r.w[lane] = R.w[lane];
+            r.pair[below + same_before] = lane;
+            if (first) r.active[ubelow] = ep;
+        }
+        if (lane == 0) *r.n_active = n_uniq;
+    }
+    for (int x = threadIdx.x; x <= E; x += blockDim.x) {
+        int below = 0, cnt = 0;
+        for (int q = 0; q < P; ++q) {
+            below += (R.sel[q] < x);
+            cnt += (R.sel[q] == x);
+        }
+        r.offset[x] = below;
+        if (x < E) r.count[x] = cnt;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K1: route + gate/up + SiLU.
+// ---------------------------------------------------------------------------
+template <int NB, int PASSES>
+struct K1Shape {
+    static constexpr int G = Gcd<NB, 8>::value;
+    static constexpr int W = NB / G;                       // waves per unit
+    static constexpr int P = 8 / G;                        // rows per pass per unit
+    static constexpr int UNITS = (4 + W - 1) / W;          // at least 4 waves (one per token)
+    static constexpr int THREADS = 64 * W * UNITS;
+    static constexpr int SLICES = 8 * NB;                  // slices per row
+    static constexpr int ROWS = P * UNITS * PASSES;        // rows of the tile
+    static constexpr bool IN_WAVE = (W == 1);              // a row's slices live in one wave
+    static constexpr int GROUPS = IN_WAVE ? 1 : SLICES / 16;  // 16-lane groups per row otherwise
+};
+
+// Dot products of one slice (16 quant bytes + its super-block header) with the
+// lane's activations of nt tokens: acc[t] = sum over the slice's 32 weights.
+template <int TT>
+__device__ __forceinline__ void q4k_slice_dot(const uint4 hv, const uint4 qv, int part, int nt,
+                                              const float (&xl)[TT][16], const float (&xh)[TT][16],
+                                              const float (&sxl)[TT], const float (&sxh)[TT], float (&acc)[TT]) {
+    const Q4KHead hd{hv.x, hv.y, hv.z, hv.w};
+    int sc_lo, m_lo, sc_hi, m_hi;
+    q4k_scale_min(hd, 2 * (part >> 1), sc_lo, m_lo);
+    q4k_scale_min(hd, 2 * (part >> 1) + 1, sc_hi, m_hi);
+    const float d = q4k_d(hd), dmin = q4k_dmin(hd);
+    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+    float ql[16], qh[16];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+        const uint32_t lo = qw[i4] & 0x0F0F0F0Fu, hi = (qw[i4] >> 4) & 0x0F0F0F0Fu;
+        ql[4 * i4 + 0] = ubyte_f32<0>(lo);
+        ql[4 * i4 + 1] = ubyte_f32<1>(lo);
+        ql[4 * i4 + 2] = ubyte_f32<2>(lo);
+        ql[4 * i4 + 3] = ubyte_f32<3>(lo);
+        qh[4 * i4 + 0] = ubyte_f32<0>(hi);
+        qh[4 * i4 + 1] = ubyte_f32<1>(hi);
+        qh[4 * i4 + 2] = ubyte_f32<2>(hi);
+        qh[4 * i4 + 3] = ubyte_f32<3>(hi);
+    }
+    const float dsl = d * (float)sc_lo, dsh = d * (float)sc_hi;
+    const float mml = dmin * (float)m_lo, mmh = dmin * (float)m_hi;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        acc[t] = 0.f;
+        if (t < nt) {
+            float slo = 0.f, shi = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                slo = fmaf(ql[j], xl[t][j], slo);
+                shi = fmaf(qh[j], xh[t][j], shi);
+            }
+            acc[t] = dsl * slo + dsh * shi - (mml * sxl[t] + mmh * sxh[t]);
+        }
+    }
+}
+
+template <int TT>
+__device__ __forceinline__ void unpack_f4(const float4 (&v)[4], float (&o)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[4 * i] = v[i].x;
+        o[4 * i + 1] = v[i].y;
+        o[4 * i + 2] = v[i].z;
+        o[4 * i + 3] = v[i].w;
+    }
+}
+
+template <int NB, int PASSES, int TT, int V>
+__global__ void __launch_bounds__((K1Shape<NB, PASSES>::THREADS)) dec_gateup_kernel(DecArgs a) {
+    using S = K1Shape<NB, PASSES>;
+    static_assert(S::IN_WAVE || S::UNITS == 1, "rows spanning waves need a single unit");
+    __shared__ DecRoute R;
+    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * TT * S::P * S::GROUPS)];
+    __shared__ int s_tok[kDecMaxT], s_hrow[kDecMaxT], s_nt;
+
+    dec_route<V>(a.logits, a.T, a.E, a.k, a.renorm, R);
+    if (blockIdx.x == 0 && blockIdx.y == 0) dec_publish(R, a.T, a.E, a.k, a.r);
+
+    // expert slot of this workgroup
+    const int slot = blockIdx.y;
+    const bool shared = a.has_shared && slot == a.T * a.k;
+    if (!shared && slot >= R.n_uniq) return;
+    const int e = shared ? 0 : R.uniq[slot];
+    const QMat G = shared ? a.sgate : a.gate;
+    const QMat U = shared ? a.sup : a.up;
+    if (threadIdx.x == 0) {
+        int nt = 0;
+        if (shared) {
+            for (int t = 0; t < a.T; ++t) {
+                s_tok[nt] = t;
+                s_hrow[nt] = a.T * a.k + t;
+                ++nt;
+            }
+        } else {
+            for (int q = R.uoff[slot]; q < R.uoff[slot + 1]; ++q) {
+                s_tok[nt] = R.pair[q] / a.k;
+                s_hrow[nt] = R.pair[q];
+                ++nt;
+            }
+        }
+        s_nt = nt;
+    }
+    __syncthreads();
+    const int nt = s_nt;
+
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int unit = wave / S::W;
+    const int f = (wave % S::W) * kWave + lane;         // flat lane inside the unit
+    const int rr = f / S::SLICES;                        // row inside the pass
+    const int sl = f % S::SLICES;
+    const int b = sl >> 3, part = sl & 7;
+    const int clo = 256 * b + q4k_slice_col_lo(part);
+    const int chi = 256 * b + q4k_slice_col_hi(part);
+    const int row0 = blockIdx.x * S::ROWS;
+
+    // every load of the tile first: weights of all passes, then the activations
+    const uint8_t* Gb = G.data + (int64_t)e * G.expert_bytes + (int64_t)b * 144;
+    const uint8_t* Ub = U.data + (int64_t)e * U.expert_bytes + (int64_t)b * 144;
+    uint4 hg[PASSES], qg[PASSES], hu[PASSES], qu[PASSES];
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int i = row0 + (ps * S::UNITS + unit) * S::P + rr;
+        const int ic = i < a.I ? i : a.I - 1;   // clamp: rows past I load a valid row and are not stored
+        const uint8_t* gr = Gb + (int64_t)ic * G.row_bytes;
+        const uint8_t* ur = Ub + (int64_t)ic * U.row_bytes;
+        hg[ps] = *reinterpret_cast<const uint4*>(gr);
+        qg[ps] = *reinterpret_cast<const uint4*>(gr + 16 + 16 * part);
+        hu[ps] = *reinterpret_cast<const uint4*>(ur);
+        qu[ps] = *reinterpret_cast<const uint4*>(ur + 16 + 16 * part);
+    }
+    float4 xl4[TT][4], xh4[TT][4];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        if (t < nt) {
+            const float4* pl = reinterpret_cast<const float4*>(a.x + (int64_t)s_tok[t] * a.H + clo);
+            const float4* ph = reinterpret_cast<const float4*>(a.x + (int64_t)s_tok[t] * a.H + chi);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                xl4[t][v] = pl[v];
+                xh4[t][v] = ph[v];
+            }
+        }
+    }
+    float xl[TT][16], xh[TT][16], sxl[TT], sxh[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        sxl[t] = sxh[t] = 0.f;
+        if (t < nt) {
+            unpack_f4<TT>(xl4[t], xl[t]);
+            unpack_f4<TT>(xh4[t], xh[t]);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                sxl[t] += xl[t][j];
+                sxh[t] += xh[t][j];
+            }
+        }
+    }
+
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int i = row0 + (ps * S::UNITS + unit) * S::P + rr;
+        float pg[TT], pu[TT];
+        q4k_slice_dot<TT>(hg[ps], qg[ps], part, nt, xl, xh, sxl, sxh, pg);
+        q4k_slice_dot<TT>(hu[ps], qu[ps], part, nt, xl, xh, sxl, sxh, pu);
+        if constexpr (S::IN_WAVE) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                pg[t] = segment_sum<S::SLICES>(pg[t]);
+                pu[t] = segment_sum<S::SLICES>(pu[t]);
+            }
+            if (sl == S::SLICES - 1 && i < a.I) {
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+                    if (t < nt) a.h[(int64_t)s_hrow[t] * a.I + i] = silu_f32(pg[t]) * pu[t];
+            }
+        } else {
+            // a row spans several waves: sums of 16-lane groups, then the row's groups in order
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                pg[t] = segment_sum<16>(pg[t]);
+                pu[t] = segment_sum<16>(pu[t]);
+            }
+            if (ps > 0) __syncthreads();
+            if ((lane & 15) == 15) {
+                const int grp = sl >> 4;
+#pragma unroll
+                for (int t = 0; t < TT; ++t) {
+                    s_part[((2 * t + 0) * S::P + rr) * S::GROUPS + grp] = pg[t];
+                    s_part[((2 * t + 1) * S::P + rr) * S::GROUPS + grp] = pu[t];
+                }
+            }
+            __syncthreads();
+            const int job = threadIdx.x;   // one thread per (token, row)
+            if (job < nt * S::P) {
+                const int t = job / S::P, r2 = job % S::P;
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int q = 0; q < S::GROUPS; ++q) {
+                    g += s_part[((2 * t + 0) * S::P + r2) * S::GROUPS + q];
+                    u += s_part[((2 * t + 1) * S::P + r2) * S::GROUPS + q];
+                }
+                const int i2 = row0 + ps * S::P + r2;
+                if (i2 < a.I) a.h[(int64_t)s_hrow[t] * a.I + i2] = silu_f32(g) * u;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K2: down + combine.  A "slice" of a down row is 16 quant bytes of a Q4_K
+// super-block (32 weights) or one 34-byte Q8_0 block (32 weights); NS slices
+// per row, 64/NS rows per wave pass, PASSES passes per workgroup.  Every wave
+// covers all the workgroup's rows for up to SMAX expert slots at a time, with
+// every weight and activation load of those slots in flight together.
+// ---------------------------------------------------------------------------
+constexpr int kK2Passes = 2;
+
+template <int TT>
+struct K2Slots {
+    static constexpr int value = TT == 1 ? 2 : 1;   // slots per wave in flight (register budget)
+};
+
+template <int QD, int NS, int TT, int V>
+__global__ void __launch_bounds__(512) dec_down_kernel(DecArgs a) {
+    constexpr int RP = kWave / NS;              // rows per wave pass
+    constexpr int RO = RP * kK2Passes;          // output rows of the workgroup
+    constexpr int SM = K2Slots<TT>::value;
+    __shared__ DecRoute R;
+    __shared__ float s_y[(kDecMaxPairs + kDecMaxT) * RO];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int nwaves = blockDim.x / kWave;
+    const int T = a.T, k = a.k, P = T * k;
+    const int o0 = blockIdx.x * RO;
+
+    dec_route<V>(a.logits, T, a.E, k, a.renorm, R);
+    const int n_slots = R.n_uniq + (a.has_shared ? 1 : 0);
+    const int rr = lane / NS, sl = lane % NS;
+    int c_lo, c_hi;
+    if constexpr (QD == kQ4_K) {
+        c_lo = 256 * (sl >> 3) + q4k_slice_col_lo(sl & 7);
+        c_hi = 256 * (sl >> 3) + q4k_slice_col_hi(sl & 7);
+    } else {
+        c_lo = 32 * sl;
+        c_hi = 32 * sl + 16;
+    }
+
+    for (int base = wave; base < n_slots; base += nwaves * SM) {
+        int np[SM], hrow[SM][TT];
+        bool shared[SM], live[SM];
+        const uint8_t* Db[SM];
+        int64_t rowb[SM];
+#pragma unroll
+        for (int m = 0; m < SM; ++m) {
+            const int u = base + m * nwaves;
+            live[m] = u < n_slots;
+            shared[m] = live[m] && a.has_shared && u == R.n_uniq;
+            const int e = (!live[m] || shared[m]) ? 0 : R.uniq[u];
+            const QMat D = shared[m] ? a.sdown : a.down;
+            Db[m] = D.data + (int64_t)e * D.expert_bytes;
+            rowb[m] = D.row_bytes;
+            const int q0 = shared[m] ? 0 : (live[m] ? R.uoff[u] : 0);
+            np[m] = !live[m] ? 0 : (shared[m] ? T : R.uoff[u + 1] - q0);
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+                hrow[m][t] = t < np[m] ? (shared[m] ? P + t : R.pair[q0 + t]) : 0;
+        }
+        // all weight loads, then the h loads
+        uint4 w0[SM][kK2Passes], w1[SM][kK2Passes];
+        uint32_t w2[SM][kK2Passes];
+#pragma unroll
+        for (int m = 0; m < SM; ++m) {
+#pragma unroll
+            for (int ps = 0; ps < kK2Passes; ++ps) {
+                w0[m][ps] = make_uint4(0, 0, 0, 0);
+                w1[m][ps] = make_uint4(0, 0, 0, 0);
+                w2[m][ps] = 0;
+                if (!live[m]) continue;
+                const int o = o0 + ps * RP + rr;
+                const int oc = o < a.H ? o : a.H - 1;
+                const uint8_t* row = Db[m] + (int64_t)oc * rowb[m];
+                if constexpr (QD == kQ4_K) {
+                    const uint8_t* blk = row + (int64_t)(sl >> 3) * 144;
+                    w0[m][ps] = *reinterpret_cast<const uint4*>(blk);
+                    w1[m][ps] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (sl & 7));
+                } else {
+                    // 34-byte block at a 2-byte aligned offset: 36 bytes from the dword below it
+                    const uint8_t* blk = row + (int64_t)sl * 34;
+                    const uint32_t* dw = reinterpret_cast<const uint32_t*>((uintptr_t)blk & ~(uintptr_t)3);
+                    w0[m][ps] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+                    w1[m][ps] = make_uint4(dw[4], dw[5], dw[6], dw[7]);
+                    w2[m][ps] = dw[8];
+                }
+            }
+        }
+        float4 hl4[SM][TT][4], hh4[SM][TT][4];
+#pragma unroll
+        for (int m = 0; m < SM; ++m) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                if (t < np[m]) {
+                    const float4* pl = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m][t] * a.I + c_lo);
+                    const float4* ph = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m][t] * a.I + c_hi);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        hl4[m][t][v] = pl[v];
+                        hh4[m][t][v] = ph[v];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < SM; ++m) {
+            if (!live[m]) continue;
+            float hl[TT][16], hh[TT][16], shl[TT], shh[TT];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                shl[t] = shh[t] = 0.f;
+                if (t < np[m]) {
+                    unpack_f4<TT>(hl4[m][t], hl[t]);
+                    unpack_f4<TT>(hh4[m][t], hh[t]);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        shl[t] += hl[t][j];
+                        shh[t] += hh[t][j];
+                    }
+                }
+            }
+#pragma unroll
+            for (int ps = 0; ps < kK2Passes; ++ps) {
+                float acc[TT];
+                if constexpr (QD == kQ4_K) {
+                    q4k_slice_dot<TT>(w0[m][ps], w1[m][ps], sl & 7, np[m], hl, hh, shl, shh, acc);
+                } else {
+                    const uint32_t dw[9] = {w0[m][ps].x, w0[m][ps].y, w0[m][ps].z, w0[m][ps].w,
+                                            w1[m][ps].x, w1[m][ps].y, w1[m][ps].z, w1[m][ps].w, w2[m][ps]};
+                    const bool odd = (sl & 1) != 0;   // 34*sl is 2 mod 4 exactly for odd sl (rows 4-byte aligned)
+                    const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
+                    const float d = f16_bits_to_f32(odd ? (dw[0] >> 16) : (dw[0] & 0xFFFFu));
+                    float qf[32];
+#pragma unroll
+                    for (int i4 = 0; i4 < 8; ++i4) {
+                        const uint32_t q4 = __builtin_amdgcn_perm(dw[i4 + 1], dw[i4], sel) ^ 0x80808080u;  // q + 128
+                        qf[4 * i4 + 0] = ubyte_f32<0>(q4);
+                        qf[4 * i4 + 1] = ubyte_f32<1>(q4);
+                        qf[4 * i4 + 2] = ubyte_f32<2>(q4);
+                        qf[4 * i4 + 3] = ubyte_f32<3>(q4);
+                    }
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        acc[t] = 0.f;
+                        if (t < np[m]) {
+                            float s0 = 0.f;
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) {
+                                s0 = fmaf(qf[j], hl[t][j], s0);
+                                s0 = fmaf(qf[16 + j], hh[t][j], s0);
+                            }
+                            acc[t] = d * (s0 - 128.0f * (shl[t] + shh[t]));
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < TT; ++t) acc[t] = segment_sum<NS>(acc[t]);
+                if (sl == NS - 1) {
+                    const int r = ps * RP + rr;
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        if (t < np[m]) {
+                            const int yrow = shared[m] ? (kDecMaxPairs + t) : hrow[m][t];
+                            s_y[yrow * RO + r] = acc[t];
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // combine in slot order, then the shared expert; also publish y_pair / y_shared
+    for (int job = threadIdx.x; job < T * RO; job += blockDim.x) {
+        const int t = job / RO, r = job % RO, o = o0 + r;
+        if (o >= a.H) continue;
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const float y = s_y[(t * k + j) * RO + r];
+            acc = fmaf(R.w[t * k + j], y, acc);
+            if (a.y_pair) a.y_pair[(int64_t)(t * k + j) * a.H + o] = y;
+        }
+        if (a.has_shared) {
+            const float ys = s_y[(kDecMaxPairs + t) * RO + r];
+            acc = fmaf(a.shared_scale ? a.shared_scale[t] : 1.0f, ys, acc);
+            if (a.y_shared) a.y_shared[(int64_t)t * a.H + o] = ys;
+        }
+        a.out[(int64_t)t * a.H + o] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int NB, int PASSES, int V>
+hipError_t launch_k1v(const DecArgs& a, hipStream_t s) {
+    using S = K1Shape<NB, PASSES>;
+    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, a.T * a.k + (a.has_shared ? 1 : 0));
+    if (a.T == 1)
+        dec_gateup_kernel<NB, PASSES, 1, V><<<grid, S::THREADS, 0, s>>>(a);
+    else
+        dec_gateup_kernel<NB, PASSES, kDecMaxT, V><<<grid, S::THREADS, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int NB, int PASSES>
+hipError_t launch_k1(const DecArgs& a, hipStream_t s) {
+    const int vpl = topk_vpl(a.E);
+    if (vpl == 4) return launch_k1v<NB, PASSES, 4>(a, s);
+    if (vpl == 8) return launch_k1v<NB, PASSES, 8>(a, s);
+    return launch_k1v<NB, PASSES, 16>(a, s);
+}
+
+template <int QD, int NS, int V>
+hipError_t launch_k2v(const DecArgs& a, hipStream_t s) {
+    constexpr int RO = (kWave / NS) * kK2Passes;
+    const int slots = a.T * a.k + (a.has_shared ? 1 : 0);
+    const int sm = a.T == 1 ? K2Slots<1>::value : K2Slots<kDecMaxT>::value;
+    int waves = (slots + sm - 1) / sm;
+    waves = waves < 4 ? 4 : (waves > 8 ? 8 : waves);   // at least one wave per token, at most 512 threads
+    if (a.T == 1)
+        dec_down_kernel<QD, NS, 1, V><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
+    else
+        dec_down_kernel<QD, NS, kDecMaxT, V><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int QD, int NS>
+hipError_t launch_k2(const DecArgs& a, hipStream_t s) {
+    const int vpl = topk_vpl(a.E);
+    if (vpl == 4) return launch_k2v<QD, NS, 4>(a, s);
+    if (vpl == 8) return launch_k2v<QD, NS, 8>(a, s);
+    return launch_k2v<QD, NS, 16>(a, s);
+}
+
+}  // namespace
+
+// Shapes the fused decode path covers: Q4_K gate/up with H/256 in {1, 2, 4, 8,
+// 10}; down Q4_K or Q8_0 with 8, 16 or 32 slices of 32 weights per row
+// (I = 256, 512 or 1024); T <= 4, T*k <= 64.
+bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd) {
+    if (T < 1 || T > kDecMaxT || T * k > kDecMaxPairs) return false;
+    if (qg != kQ4_K || qu != kQ4_K) return false;
+    const int nb = H / 256;
+    if (!(nb == 1 || nb == 2 || nb == 4 || nb == 8 || nb == 10)) return false;
+    const int ns = (qd == kQ4_K) ? 8 * (I / 256) : I / 32;
+    return ns == 8 || ns == 16 || ns == 32;
+}
+
+hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s) {
+    hipError_t e;
+    switch (a.H / 256) {
+        case 1: e = launch_k1<1, 1>(a, s); break;
+        case 2: e = launch_k1<2, 1>(a, s); break;
+        case 4: e = launch_k1<4, 2>(a, s); break;
+        case 8: e = launch_k1<8, 2>(a, s); break;
+        default: e = launch_k1<10, 2>(a, s); break;
+    }
+    if (e != hipSuccess) return e;
+    const int ns = (a.down.qtype == kQ4_K) ? 8 * (a.I / 256) : a.I / 32;
+    if (a.down.qtype == kQ4_K) {
+        if (ns == 8) return launch_k2<kQ4_K, 8>(a, s);
+        if (ns == 16) return launch_k2<kQ4_K, 16>(a, s);
+        return launch_k2<kQ4_K, 32>(a, s);
+    }
+    if (ns == 8) return launch_k2<kQ8_0, 8>(a, s);
+    if (ns == 16) return launch_k2<kQ8_0, 16>(a, s);
+    return launch_k2<kQ8_0, 32>(a, s);
+}
+
+}  // namespace moe

@@ -49,6 +49,24 @@ struct FfnArgs {
     int n_slots;                   // min(E, T*k) routed expert slots
 };
 
+// The two-kernel decode layer (route + gate/up + SiLU; down + combine).
+struct DecArgs {
+    const float* logits;  // [T][E]
+    const float* x;       // [T][H]
+    QMat gate, up, down, sgate, sup, sdown;
+    int has_shared;
+    int T, E, k, H, I, renorm;
+    RoutingPtrs r;
+    float* h;             // [T*k + T][I]
+    float* y_pair;        // [T*k][H] or null
+    float* y_shared;      // [T][H] or null
+    const float* shared_scale;
+    float* out;           // [T][H]
+};
+
+bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd);
+hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s);
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, const RoutingPtrs& r,
                         void* ws, hipStream_t s);
 size_t route_workspace_bytes(int T, int E, int k);

@@ -4,4 +4,5 @@
 #include "route.hip"
 #include "quant.hip"
 #include "ffn_int8.hip"
+#include "decode_fused.hip"
 #include "moe_api.hip"

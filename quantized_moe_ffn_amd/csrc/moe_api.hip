@@ -92,9 +92,89 @@ FfnWorkspace ffn_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
     return w;
 }
 
+struct ForwardWorkspace {
+    size_t route, ffn, xq, xd, total;
+};
+
+ForwardWorkspace forward_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
+    ForwardWorkspace w{};
+    size_t off = 0;
+    w.route = off;
+    off += align_up(moe::route_workspace_bytes(T, L->n_experts, k), 256);
+    w.ffn = off;
+    off += align_up(ffn_ws_layout(L, T, k, path).total, 256);
+    w.xq = off;
+    off += align_up((size_t)T * L->hidden, 256);
+    w.xd = off;
+    off += align_up((size_t)T * (L->hidden / 256) * sizeof(float), 256);
+    w.total = off;
+    return w;
+}
+
 uint32_t resolve_path(uint32_t flags, int T) {
     if (flags == MOE_FFN_AUTO) return T <= kAutoDecodeMaxT ? MOE_FFN_DECODE : MOE_FFN_INT8;
     return flags;
+}
+
+moe_status validate_layer(const moe_layer* L, int32_t T, int32_t k, const float* y_shared) {
+    if (!L) return fail(MOE_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
+    const int E = L->n_experts, H = L->hidden, I = L->inter;
+    if (E < 1 || E > kMaxExperts) return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts = %d: need 1..%d", E, kMaxExperts);
+    if (H < 256 || H % 256 || I < 256 || I % 256)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "hidden = %d, inter = %d: both must be positive multiples of 256", H, I);
+    if (H > kMaxDim || I > kMaxDim)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden = %d, inter = %d: this build supports up to %d", H, I, kMaxDim);
+    if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d: need at least one token", T);
+    if (k < 1 || k > E || k > kMaxTopK)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d: need 1 <= k <= min(E = %d, %d)", k, E, kMaxTopK);
+    if ((int64_t)T * k > (int64_t)1 << 30)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "T*k = %lld is too large", (long long)T * k);
+    moe_status st;
+    if ((st = check_qmatrix(L->gate, "gate", I, H, E)) != MOE_OK) return st;
+    if ((st = check_qmatrix(L->up, "up", I, H, E)) != MOE_OK) return st;
+    if ((st = check_qmatrix(L->down, "down", H, I, E)) != MOE_OK) return st;
+    if (L->has_shared) {
+        if ((st = check_qmatrix(L->sh_gate, "sh_gate", I, H, 1)) != MOE_OK) return st;
+        if ((st = check_qmatrix(L->sh_up, "sh_up", I, H, 1)) != MOE_OK) return st;
+        if ((st = check_qmatrix(L->sh_down, "sh_down", H, I, 1)) != MOE_OK) return st;
+        if (L->sh_gate.qtype != L->gate.qtype || L->sh_up.qtype != L->up.qtype || L->sh_down.qtype != L->down.qtype)
+            return fail(MOE_ERR_UNSUPPORTED, "the shared expert must use the routed experts' formats "
+                        "(gate %d/%d, up %d/%d, down %d/%d)", L->sh_gate.qtype, L->gate.qtype,
+                        L->sh_up.qtype, L->up.qtype, L->sh_down.qtype, L->down.qtype);
+        if (!y_shared) return fail(MOE_ERR_INVALID_ARGUMENT, "layer has a shared expert but y_shared is NULL");
+    }
+    return MOE_OK;
+}
+
+void fill_ffn_args(moe::FfnArgs& a, const moe_layer* L, int T, int k) {
+    a.gate = to_qmat(L->gate);
+    a.up = to_qmat(L->up);
+    a.down = to_qmat(L->down);
+    a.has_shared = L->has_shared ? 1 : 0;
+    if (a.has_shared) {
+        a.sgate = to_qmat(L->sh_gate);
+        a.sup = to_qmat(L->sh_up);
+        a.sdown = to_qmat(L->sh_down);
+    }
+    a.H = L->hidden;
+    a.I = L->inter;
+    a.T = T;
+    a.k = k;
+    a.E = L->n_experts;
+    a.n_slots = (int)((int64_t)T * k < a.E ? (int64_t)T * k : a.E);
+}
+
+bool aligned16_bank(const moe_qmatrix& m) { return aligned(m.data, 16) && (m.expert_bytes % 16) == 0; }
+
+// The two-kernel decode path applies: shapes it is built for, 16-byte aligned
+// banks and activations, and the decode arithmetic selected.
+bool use_fused_decode(const moe_layer* L, int T, int k, const float* x, uint32_t path) {
+    if (path != MOE_FFN_DECODE || !aligned(x, 16)) return false;
+    if (!moe::dec_fused_supported(T, k, L->hidden, L->inter, L->gate.qtype, L->up.qtype, L->down.qtype)) return false;
+    if (!aligned16_bank(L->gate) || !aligned16_bank(L->up) || !aligned16_bank(L->down)) return false;
+    if (L->has_shared && (!aligned16_bank(L->sh_gate) || !aligned16_bank(L->sh_up) || !aligned16_bank(L->sh_down)))
+        return false;
+    return true;
 }
 
 }  // namespace
@@ -148,33 +228,12 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_
     return ffn_ws_layout(L, T, k, resolve_path(flags, T)).total;
 }
 
+
 moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T, int32_t k, const float* x,
                             const int8_t* xq, const float* xd, uint32_t flags, float* y_pair, float* y_shared,
                             void* workspace, size_t ws_bytes, hipStream_t stream) {
-    if (!L) return fail(MOE_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
-    const int E = L->n_experts, H = L->hidden, I = L->inter;
-    if (E < 1 || E > kMaxExperts) return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts = %d: need 1..%d", E, kMaxExperts);
-    if (H < 256 || H % 256 || I < 256 || I % 256)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "hidden = %d, inter = %d: both must be positive multiples of 256", H, I);
-    if (H > kMaxDim || I > kMaxDim)
-        return fail(MOE_ERR_UNSUPPORTED, "hidden = %d, inter = %d: this build supports up to %d", H, I, kMaxDim);
-    if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d: need at least one token", T);
-    if (k < 1 || k > E || k > kMaxTopK)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d: need 1 <= k <= min(E = %d, %d)", k, E, kMaxTopK);
-    moe_status st;
-    if ((st = check_qmatrix(L->gate, "gate", I, H, E)) != MOE_OK) return st;
-    if ((st = check_qmatrix(L->up, "up", I, H, E)) != MOE_OK) return st;
-    if ((st = check_qmatrix(L->down, "down", H, I, E)) != MOE_OK) return st;
-    if (L->has_shared) {
-        if ((st = check_qmatrix(L->sh_gate, "sh_gate", I, H, 1)) != MOE_OK) return st;
-        if ((st = check_qmatrix(L->sh_up, "sh_up", I, H, 1)) != MOE_OK) return st;
-        if ((st = check_qmatrix(L->sh_down, "sh_down", H, I, 1)) != MOE_OK) return st;
-        if (L->sh_gate.qtype != L->gate.qtype || L->sh_up.qtype != L->up.qtype || L->sh_down.qtype != L->down.qtype)
-            return fail(MOE_ERR_UNSUPPORTED, "the shared expert must use the routed experts' formats "
-                        "(gate %d/%d, up %d/%d, down %d/%d)", L->sh_gate.qtype, L->gate.qtype,
-                        L->sh_up.qtype, L->up.qtype, L->sh_down.qtype, L->down.qtype);
-        if (!y_shared) return fail(MOE_ERR_INVALID_ARGUMENT, "layer has a shared expert but y_shared is NULL");
-    }
+    moe_status st = validate_layer(L, T, k, y_shared);
+    if (st != MOE_OK) return st;
     if (!r || !r->count || !r->offset || !r->pair || !r->active || !r->n_active)
         return fail(MOE_ERR_INVALID_ARGUMENT, "moe_routing or one of count/offset/pair/active/n_active is NULL");
     if (!y_pair) return fail(MOE_ERR_INVALID_ARGUMENT, "y_pair is NULL");
@@ -192,20 +251,7 @@ moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T,
     if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
 
     moe::FfnArgs a{};
-    a.gate = to_qmat(L->gate);
-    a.up = to_qmat(L->up);
-    a.down = to_qmat(L->down);
-    a.has_shared = L->has_shared ? 1 : 0;
-    if (a.has_shared) {
-        a.sgate = to_qmat(L->sh_gate);
-        a.sup = to_qmat(L->sh_up);
-        a.sdown = to_qmat(L->sh_down);
-    }
-    a.H = H;
-    a.I = I;
-    a.T = T;
-    a.k = k;
-    a.E = E;
+    fill_ffn_args(a, L, T, k);
     a.count = r->count;
     a.offset = r->offset;
     a.pair = r->pair;
@@ -220,9 +266,98 @@ moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T,
     a.hd = (float*)(ws + wl.hd);
     a.y_pair = y_pair;
     a.y_shared = y_shared;
-    a.n_slots = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
     if (path == MOE_FFN_DECODE) return from_hip(moe::launch_ffn_decode(a, stream), "moe_expert_ffn_q (decode) launch");
     return from_hip(moe::launch_ffn_int8(a, nullptr, stream), "moe_expert_ffn_q (int8) launch");
+}
+
+size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t ffn_flags) {
+    if (!L || T < 1 || k < 1) return 0;
+    return forward_ws_layout(L, T, k, resolve_path(ffn_flags, T)).total;
+}
+
+moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
+                       uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
+                       float* y_shared, const float* shared_scale, float* out, void* workspace, size_t ws_bytes,
+                       hipStream_t stream) {
+    moe_status st = validate_layer(L, T, k, y_shared);
+    if (st != MOE_OK) return st;
+    if (!logits || !x || !out || !y_pair) return fail(MOE_ERR_INVALID_ARGUMENT, "logits, x, y_pair or out is NULL");
+    if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(out, 4) || !aligned(y_pair, 4) ||
+        (y_shared && !aligned(y_shared, 4)) || (shared_scale && !aligned(shared_scale, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned, the other fp32 arrays 4-byte aligned");
+    if (route_flags & ~(uint32_t)MOE_ROUTE_RENORM)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "route_flags = 0x%x: only MOE_ROUTE_RENORM is defined", route_flags);
+    if (ffn_flags != MOE_FFN_AUTO && ffn_flags != MOE_FFN_DECODE && ffn_flags != MOE_FFN_INT8)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "ffn_flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8",
+                    ffn_flags);
+    if (!r || !r->idx || !r->w || !r->count || !r->offset || !r->pair || !r->active || !r->n_active)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_routing or one of its arrays is NULL");
+    const uint32_t path = resolve_path(ffn_flags, T);
+    const ForwardWorkspace wl = forward_ws_layout(L, T, k, path);
+    if (!workspace || ws_bytes < wl.total)
+        return fail(MOE_ERR_WORKSPACE, "forward workspace: %zu bytes given, %zu needed", ws_bytes, wl.total);
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    char* ws = (char*)workspace;
+    moe::RoutingPtrs rp{r->idx, r->w, r->count, r->offset, r->pair, r->active, r->n_active};
+    const int renorm = (route_flags & MOE_ROUTE_RENORM) ? 1 : 0;
+
+    if (use_fused_decode(L, T, k, x, path)) {
+        moe::DecArgs d{};
+        d.logits = logits;
+        d.x = x;
+        d.gate = to_qmat(L->gate);
+        d.up = to_qmat(L->up);
+        d.down = to_qmat(L->down);
+        d.has_shared = L->has_shared ? 1 : 0;
+        if (d.has_shared) {
+            d.sgate = to_qmat(L->sh_gate);
+            d.sup = to_qmat(L->sh_up);
+            d.sdown = to_qmat(L->sh_down);
+        }
+        d.T = T;
+        d.E = L->n_experts;
+        d.k = k;
+        d.H = L->hidden;
+        d.I = L->inter;
+        d.renorm = renorm;
+        d.r = rp;
+        d.h = (float*)(ws + wl.ffn);
+        d.y_pair = y_pair;
+        d.y_shared = y_shared;
+        d.shared_scale = shared_scale;
+        d.out = out;
+        return from_hip(moe::launch_dec_fused(d, stream), "moe_forward (decode) launch");
+    }
+
+    hipError_t e = moe::launch_route(logits, T, L->n_experts, k, renorm, rp, ws + wl.route, stream);
+    if (e != hipSuccess) return from_hip(e, "moe_forward: routing launch");
+    moe::FfnArgs a{};
+    fill_ffn_args(a, L, T, k);
+    a.count = r->count;
+    a.offset = r->offset;
+    a.pair = r->pair;
+    a.active = r->active;
+    a.n_active = r->n_active;
+    a.x = x;
+    a.xq = (int8_t*)(ws + wl.xq);
+    a.xd = (float*)(ws + wl.xd);
+    const FfnWorkspace fl = ffn_ws_layout(L, T, k, path);
+    a.h = (float*)(ws + wl.ffn + fl.h);
+    a.hq = (int8_t*)(ws + wl.ffn + fl.hq);
+    a.hd = (float*)(ws + wl.ffn + fl.hd);
+    a.y_pair = y_pair;
+    a.y_shared = y_shared;
+    if (path == MOE_FFN_INT8) {
+        e = moe::launch_quantize_act(x, T, L->hidden, (int8_t*)a.xq, (float*)a.xd, stream);
+        if (e != hipSuccess) return from_hip(e, "moe_forward: quantisation launch");
+        e = moe::launch_ffn_int8(a, nullptr, stream);
+    } else {
+        e = moe::launch_ffn_decode(a, stream);
+    }
+    if (e != hipSuccess) return from_hip(e, "moe_forward: expert FFN launch");
+    return from_hip(moe::launch_combine(y_pair, r->w, L->has_shared ? y_shared : nullptr, shared_scale, T, k,
+                                        L->hidden, out, stream),
+                    "moe_forward: combine launch");
 }
 
 moe_status moe_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,

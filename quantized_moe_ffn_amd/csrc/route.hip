@@ -19,75 +19,110 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ bool better(uint32_t ka, int ia, uint32_t kb, int ib) {
-    return ka > kb || (ka == kb && ia < ib);
+// Inverse of order_key.
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// One wave selects the top-k of one token's E logits (E <= 64 * kMaxVpl).
-// Lane l owns experts l, l+64, ...  Returns, in lane j < k, the expert of slot j
-// and its weight; other lanes return -1 / 0.
-constexpr int kMaxVpl = 16;  // E <= 1024
-
-__device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool renorm, int& out_e,
-                          float& out_w) {
+// One wave selects the top-k of one token's E logits (E <= 64 * V) and
+// computes the routing weights.  Lane l owns experts l, l+64, ...  Returns, in
+// lane j < k, the expert of slot j and its weight; other lanes get -1 / 0.
+//
+// k rounds of extraction: a DPP wave maximum of the order-preserving keys of
+// the experts not yet taken, then ballots find the lowest expert index holding
+// that key (ties go to the lower index), and its owner lane drops it (key 0
+// marks taken or absent experts; real keys are >= 1).  Rounds produce the
+// slots directly in descending-logit order.  No LDS traffic.
+template <int V>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, int k, bool renorm, int& out_e,
+                                          float& out_w) {
     const int lane = threadIdx.x & (kWave - 1);
-    uint32_t key[kMaxVpl];
+    uint32_t key[V];
     bool bad = false;
 #pragma unroll
-    for (int v = 0; v < kMaxVpl; ++v) {
+    for (int v = 0; v < V; ++v) {
         const int e = lane + kWave * v;
-        float x = (e < E) ? lg[e] : 0.0f;
-        bad |= (e < E) && !isfinite(x);
-        key[v] = (e < E) ? order_key(x) : 0u;
+        const float x = e < E ? lg[e] : 0.0f;
+        bad |= e < E && !isfinite(x);
+        key[v] = e < E ? max(order_key(x), 1u) : 0u;
     }
     if (__any(bad)) {
         if (lane == 0) raise_error(kErrLogitNonFinite);
     }
-    uint32_t taken = 0;
     int my_e = -1;
+    float my_l = 0.0f, top = 0.0f;
     for (int j = 0; j < k; ++j) {
-        // best of this lane's remaining experts
-        uint32_t bk = 0;
-        int bi = 0x7FFFFFFF;
+        uint32_t b = key[0];
 #pragma unroll
-        for (int v = 0; v < kMaxVpl; ++v) {
-            const int e = lane + kWave * v;
-            if (e < E && !((taken >> v) & 1u) && better(key[v], e, bk, bi)) {
-                bk = key[v];
-                bi = e;
+        for (int v = 1; v < V; ++v) b = max(b, key[v]);
+        const uint32_t M = wave_max_u32(b);
+        int wv = V, wl = 0;
+#pragma unroll
+        for (int v = V - 1; v >= 0; --v) {   // the lowest v with a match wins; then its lowest lane
+            const uint64_t msk = __ballot(key[v] == M);
+            if (msk != 0ull) {
+                wv = v;
+                wl = (int)__builtin_ctzll(msk);
             }
         }
-        // butterfly arg-max over the wave
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const uint32_t ok = __shfl_xor(bk, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
-            if (better(ok, oi, bk, bi)) {
-                bk = ok;
-                bi = oi;
-            }
+        for (int v = 0; v < V; ++v)
+            if (v == wv && lane == wl) key[v] = 0u;
+        const float val = key_value(M);
+        if (j == 0) top = val;
+        if (lane == j) {
+            my_e = wl + kWave * wv;
+            my_l = val;
         }
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-        if (lane == j) my_e = bi;
     }
-    // weights
-    const float my_l = (lane < k) ? lg[my_e] : 0.0f;
-    const float top = __shfl(my_l, 0, kWave);
-    float sum;
     if (renorm) {
         const float ex = (lane < k) ? expf(my_l - top) : 0.0f;
-        sum = wave_sum(ex);
+        const float sum = wave_sum(ex);
         out_w = (lane < k) ? ex / sum : 0.0f;
     } else {
         float part = 0.0f;
-        for (int v = 0; v < kMaxVpl; ++v) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
             const int e = lane + kWave * v;
             if (e < E) part += expf(lg[e] - top);
         }
-        sum = wave_sum(part);
+        const float sum = wave_sum(part);
         out_w = (lane < k) ? expf(my_l - top) / sum : 0.0f;
     }
     out_e = my_e;
+}
+
+// Values per lane for E experts (the kernels are instantiated for 4, 8, 16).
+inline int topk_vpl(int E) { return E <= 256 ? 4 : (E <= 512 ? 8 : 16); }
+
+// Buckets of up to 64 (token, slot) pairs inside one wave: lane p holds the
+// expert e of pair p (p < P).  Computes, with readlane loops (no LDS):
+//   below  = pairs with a smaller expert, same_before = earlier pairs of e,
+//   first  = p is e's first pair, ubelow = distinct experts smaller than e,
+//   n_uniq = distinct experts.
+// Then pair p goes to position below + same_before of the pair list and, if
+// first, e is active entry ubelow with its pairs starting at below.
+__device__ __forceinline__ void wave_buckets(int e, int P, int& below, int& same_before, bool& first, int& ubelow,
+                                             int& n_uniq) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool mine = lane < P;
+    below = 0;
+    same_before = 0;
+    for (int q = 0; q < P; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        below += (eq < e);
+        same_before += (q < lane && eq == e);
+    }
+    first = mine && same_before == 0;
+    const uint64_t fm = __ballot(first);
+    ubelow = 0;
+    for (int q = 0; q < P; ++q) {
+        if ((fm >> q) & 1ull) {
+            const int eq = __builtin_amdgcn_readlane(e, q);
+            ubelow += (eq < e);
+        }
+    }
+    n_uniq = __popcll(fm);
 }
 
 // Block-wide exclusive scan of n <= blockDim.x ints held one per thread.
@@ -125,6 +160,7 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int& total) {
 // ---------------------------------------------------------------------------
 // Small batches (T*k <= kSmallPairs): top-k and bucketing in one workgroup.
 // ---------------------------------------------------------------------------
+template <int V>
 __global__ void __launch_bounds__(1024) route_small_kernel(const float* __restrict__ logits, int T,
                                                            int E, int k, int renorm,
                                                            RoutingPtrs r) {
@@ -140,7 +176,7 @@ __global__ void __launch_bounds__(1024) route_small_kernel(const float* __restri
     for (int t = wave; t < T; t += nwaves) {
         int e;
         float w;
-        wave_topk(logits + (int64_t)t * E, E, k, renorm != 0, e, w);
+        wave_topk<V>(logits + (int64_t)t * E, E, k, renorm != 0, e, w);
         if (lane < k) {
             r.idx[t * k + lane] = e;
             r.w[t * k + lane] = w;
@@ -178,6 +214,7 @@ __global__ void __launch_bounds__(1024) route_small_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 // Large batches: one wave per token, then a tiled stable counting sort.
 // ---------------------------------------------------------------------------
+template <int V>
 __global__ void __launch_bounds__(256) route_tokens_kernel(const float* __restrict__ logits, int T,
                                                            int E, int k, int renorm, int32_t* idx,
                                                            float* w) {
@@ -186,7 +223,7 @@ __global__ void __launch_bounds__(256) route_tokens_kernel(const float* __restri
     if (t >= T) return;
     int e;
     float wt;
-    wave_topk(logits + (int64_t)t * E, E, k, renorm != 0, e, wt);
+    wave_topk<V>(logits + (int64_t)t * E, E, k, renorm != 0, e, wt);
     if (lane < k) {
         idx[(int64_t)t * k + lane] = e;
         w[(int64_t)t * k + lane] = wt;
@@ -257,14 +294,25 @@ __global__ void __launch_bounds__(256) bucket_scatter_kernel(const int32_t* __re
 hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, const RoutingPtrs& r,
                         void* ws, hipStream_t s) {
     const int P = T * k;
+    const int vpl = topk_vpl(E);
     if (P <= kSmallPairs) {
-        route_small_kernel<<<1, 1024, 0, s>>>(logits, T, E, k, renorm, r);
+        if (vpl == 4)
+            route_small_kernel<4><<<1, 1024, 0, s>>>(logits, T, E, k, renorm, r);
+        else if (vpl == 8)
+            route_small_kernel<8><<<1, 1024, 0, s>>>(logits, T, E, k, renorm, r);
+        else
+            route_small_kernel<16><<<1, 1024, 0, s>>>(logits, T, E, k, renorm, r);
         return hipGetLastError();
     }
     const int n_tiles = (P + kTilePairs - 1) / kTilePairs;
     int32_t* tile_hist = (int32_t*)ws;
     int32_t* rank = tile_hist + (size_t)n_tiles * E;
-    route_tokens_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
+    if (vpl == 4)
+        route_tokens_kernel<4><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
+    else if (vpl == 8)
+        route_tokens_kernel<8><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
+    else
+        route_tokens_kernel<16><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
     bucket_tile_kernel<<<n_tiles, kTilePairs, 0, s>>>(r.idx, P, E, tile_hist, rank);
     bucket_scan_kernel<<<1, 1024, 0, s>>>(n_tiles, E, P, tile_hist, r);
     bucket_scatter_kernel<<<(P + 255) / 256, 256, 0, s>>>(r.idx, P, E, tile_hist, rank, r.pair);

@@ -159,10 +159,10 @@ def _layer(name, **over):
     return layers.make_layer(w, seed=0, index=0, device=DEV), w
 
 
-def _run_layer(m, dl, logits, x, k, flags):
+def _run_layer(m, dl, logits, x, k, flags, fused=True):
     lg = torch.from_numpy(np.ascontiguousarray(logits)).to(DEV)
     xt = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
-    bufs = m.forward(dl.layer, lg, xt, k, flags=flags)
+    bufs = m.forward(dl.layer, lg, xt, k, flags=flags, fused=fused)
     m.moe_check_device_errors()
     return bufs
 
@@ -192,41 +192,47 @@ def _check_layer(m, dl, w, logits, x, bufs, mode, tol, token_subset=None):
     assert eo.max() <= tol, eo.max()
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name", ["tiny", "sage_decode", "mtp_window", "flash_next_decode"])
-def test_decode_layer_parity(name):
+def test_decode_layer_parity(name, fused):
     m = qm()
-    _say("decode layer", name)
+    _say("decode layer", name, "fused" if fused else "separate calls")
     dl, w = _layer(name)
     from quantized_moe_ffn_amd import layers
     for replay in range(3):
         logits, x = layers.inputs_np(w, seed=0, index=0, replay=replay)
-        bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE)
+        bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused)
         _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
+        _check_routing(bufs.routing, logits, w.top_k)
 
 
 @pytest.mark.parametrize("over", [dict(hidden=256, inter=768, n_experts=3, top_k=3, tokens=5),
                                   dict(hidden=768, inter=256, n_experts=70, top_k=4, tokens=9, qt_down=oracle.Q8_0),
                                   dict(hidden=512, inter=512, n_experts=16, top_k=2, tokens=1, qt_gate=oracle.Q8_0,
                                        qt_up=oracle.Q8_0)])
-def test_decode_ragged_shapes(over):
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_ragged_shapes(over, fused):
     m = qm()
-    _say("decode ragged", over)
+    _say("decode ragged", over, fused)
     dl, w = _layer("tiny", **over)
     from quantized_moe_ffn_amd import layers
     logits, x = layers.inputs_np(w, seed=1)
-    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused)
     _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
 
 
-def test_int8_path_tiny_full():
+@pytest.mark.parametrize("fused", [True, False])
+def test_int8_path_tiny_full(fused):
     m = qm()
-    _say("int8 tiny T=96")
+    _say("int8 tiny T=96", fused)
     dl, w = _layer("tiny", tokens=96)
     from quantized_moe_ffn_amd import layers
     logits, x = layers.inputs_np(w, seed=2)
-    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8)
-    xq, xd = oracle.quantize_act(x)
-    assert np.array_equal(bufs.xq.cpu().numpy(), xq)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8, fused)
+    if not fused:   # the separate calls leave the int8 activations in the caller's buffers
+        xq, xd = oracle.quantize_act(x)
+        assert np.array_equal(bufs.xq.cpu().numpy(), xq)
+        assert np.array_equal(bufs.xd.cpu().numpy(), xd)
     _check_layer(m, dl, w, logits, x, bufs, 1, TOL_INT8)
 
 
@@ -269,17 +275,65 @@ def test_integer_exact_layer_is_bitwise():
     assert np.array_equal(bufs.y_pair.cpu().numpy()[0], expect)
 
 
-def test_determinism_and_batch_invariance():
+@pytest.mark.parametrize("fused", [True, False])
+def test_determinism_and_batch_invariance(fused):
     m = qm()
     dl, w = _layer("mtp_window")
     from quantized_moe_ffn_amd import layers
     logits, x = layers.inputs_np(w, seed=3)
-    a = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE).out.cpu().numpy()
-    b = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE).out.cpu().numpy()
+    a = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused).out.cpu().numpy()
+    b = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused).out.cpu().numpy()
     assert np.array_equal(a, b)
     for t in range(3):
-        one = _run_layer(m, dl, logits[t:t + 1], x[t:t + 1], w.top_k, m.MOE_FFN_DECODE).out.cpu().numpy()
+        one = _run_layer(m, dl, logits[t:t + 1], x[t:t + 1], w.top_k, m.MOE_FFN_DECODE, fused).out.cpu().numpy()
         assert np.array_equal(one[0], a[t])
+
+
+def test_fused_equals_separate_calls_bitwise_for_routing():
+    """The fused layer call and the three separate calls select the same experts and weights."""
+    m = qm()
+    dl, w = _layer("flash_next_decode")
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=5)
+    a = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, True)
+    b = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, False)
+    for f in ("idx", "count", "offset", "pair", "n_active"):
+        assert torch.equal(getattr(a.routing, f), getattr(b.routing, f)), f
+    assert torch.equal(a.routing.w, b.routing.w)
+
+
+def test_graph_replay_matches_eager():
+    """A captured stack of decode layers replays correctly, with eager work between replays."""
+    m = qm()
+    from quantized_moe_ffn_amd import layers
+    w = synth.WORKLOADS["sage_decode"]
+    stack = [layers.make_layer(w, seed=9, index=l, device=DEV) for l in range(3)]
+    ins = [layers.inputs_np(w, seed=9, index=l) for l in range(3)]
+    lgs = [torch.from_numpy(a).to(DEV) for a, _ in ins]
+    xs = [torch.from_numpy(b).to(DEV) for _, b in ins]
+    bufs = [m.LayerBuffers(dl.layer, 1, w.top_k, m.MOE_FFN_DECODE, device=DEV) for dl in stack]
+    for l in range(3):
+        m.forward(stack[l].layer, lgs[l], xs[l], w.top_k, bufs[l], flags=m.MOE_FFN_DECODE)
+    torch.cuda.synchronize()
+    eager = [b.out.clone() for b in bufs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for l in range(3):
+                m.forward(stack[l].layer, lgs[l], xs[l], w.top_k, bufs[l], flags=m.MOE_FFN_DECODE)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for b in bufs:
+            b.out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=DEV).sum()   # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        float(junk)
+        for l in range(3):
+            assert torch.equal(bufs[l].out, eager[l]), (rep, l)
+    m.moe_check_device_errors()
 
 
 def test_corrupted_routing_sets_error_word():
