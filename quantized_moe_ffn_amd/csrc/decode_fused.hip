@@ -50,7 +50,7 @@ struct Gcd<A, 0> {
 // Expert slots u = 0 .. n_uniq-1 each own the pairs pair[uoff[u] .. uoff[u+1]).
 // For one token the slots are the k selections in slot order (pair u = u); for
 // several tokens they are the distinct experts in ascending order.
-struct DecRoute {
+struct DecRoute {   // also copied verbatim through the workspace from K1 to K2
     int sel[kDecMaxPairs];       // expert of pair p = t*k + j (slot order)
     float w[kDecMaxPairs];
     int pair[kDecMaxPairs];
@@ -58,6 +58,8 @@ struct DecRoute {
     int uoff[kDecMaxPairs + 1];
     int n_uniq;
 };
+
+static_assert(sizeof(DecRoute) <= kDecRouteTabBytes, "routing table size");
 
 // Waves 0..T-1 select the top-k of token t; wave 0 then builds the slots.
 // Ends with __syncthreads().
@@ -208,55 +210,22 @@ __device__ __forceinline__ void unpack_f4(const float4 (&v)[4], float (&o)[16]) 
     }
 }
 
-template <int NB, int PASSES, int TT, int V>
-__global__ void __launch_bounds__((K1Shape<NB, PASSES>::THREADS)) dec_gateup_kernel(DecArgs a) {
+// The streaming body of K1 for one expert slot: rows of gate and up of expert
+// e (bank G/U), applied to the nt tokens s_tok[] (their x already loaded into
+// xl4/xh4), h written to rows s_hrow[].
+template <int NB, int PASSES, int TT>
+__device__ __forceinline__ void dec_gateup_body(const DecArgs& a, const QMat& G, const QMat& U, int e, int nt,
+                                                const int (&s_hrow)[TT], float4 (&xl4)[TT][4], float4 (&xh4)[TT][4],
+                                                float* s_part) {
     using S = K1Shape<NB, PASSES>;
-    static_assert(S::IN_WAVE || S::UNITS == 1, "rows spanning waves need a single unit");
-    __shared__ DecRoute R;
-    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * TT * S::P * S::GROUPS)];
-    __shared__ int s_tok[kDecMaxT], s_hrow[kDecMaxT], s_nt;
-
-    dec_route<V>(a.logits, a.T, a.E, a.k, a.renorm, R);
-    if (blockIdx.x == 0 && blockIdx.y == 0) dec_publish(R, a.T, a.E, a.k, a.r);
-
-    // expert slot of this workgroup
-    const int slot = blockIdx.y;
-    const bool shared = a.has_shared && slot == a.T * a.k;
-    if (!shared && slot >= R.n_uniq) return;
-    const int e = shared ? 0 : R.uniq[slot];
-    const QMat G = shared ? a.sgate : a.gate;
-    const QMat U = shared ? a.sup : a.up;
-    if (threadIdx.x == 0) {
-        int nt = 0;
-        if (shared) {
-            for (int t = 0; t < a.T; ++t) {
-                s_tok[nt] = t;
-                s_hrow[nt] = a.T * a.k + t;
-                ++nt;
-            }
-        } else {
-            for (int q = R.uoff[slot]; q < R.uoff[slot + 1]; ++q) {
-                s_tok[nt] = R.pair[q] / a.k;
-                s_hrow[nt] = R.pair[q];
-                ++nt;
-            }
-        }
-        s_nt = nt;
-    }
-    __syncthreads();
-    const int nt = s_nt;
-
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int unit = wave / S::W;
     const int f = (wave % S::W) * kWave + lane;         // flat lane inside the unit
     const int rr = f / S::SLICES;                        // row inside the pass
     const int sl = f % S::SLICES;
     const int b = sl >> 3, part = sl & 7;
-    const int clo = 256 * b + q4k_slice_col_lo(part);
-    const int chi = 256 * b + q4k_slice_col_hi(part);
     const int row0 = blockIdx.x * S::ROWS;
 
-    // every load of the tile first: weights of all passes, then the activations
     const uint8_t* Gb = G.data + (int64_t)e * G.expert_bytes + (int64_t)b * 144;
     const uint8_t* Ub = U.data + (int64_t)e * U.expert_bytes + (int64_t)b * 144;
     uint4 hg[PASSES], qg[PASSES], hu[PASSES], qu[PASSES];
@@ -271,31 +240,16 @@ __global__ void __launch_bounds__((K1Shape<NB, PASSES>::THREADS)) dec_gateup_ker
         hu[ps] = *reinterpret_cast<const uint4*>(ur);
         qu[ps] = *reinterpret_cast<const uint4*>(ur + 16 + 16 * part);
     }
-    float4 xl4[TT][4], xh4[TT][4];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        if (t < nt) {
-            const float4* pl = reinterpret_cast<const float4*>(a.x + (int64_t)s_tok[t] * a.H + clo);
-            const float4* ph = reinterpret_cast<const float4*>(a.x + (int64_t)s_tok[t] * a.H + chi);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                xl4[t][v] = pl[v];
-                xh4[t][v] = ph[v];
-            }
-        }
-    }
     float xl[TT][16], xh[TT][16], sxl[TT], sxh[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         sxl[t] = sxh[t] = 0.f;
-        if (t < nt) {
-            unpack_f4<TT>(xl4[t], xl[t]);
-            unpack_f4<TT>(xh4[t], xh[t]);
+        unpack_f4<TT>(xl4[t], xl[t]);
+        unpack_f4<TT>(xh4[t], xh[t]);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                sxl[t] += xl[t][j];
-                sxh[t] += xh[t][j];
-            }
+        for (int j = 0; j < 16; ++j) {
+            sxl[t] += xl[t][j];
+            sxh[t] += xh[t][j];
         }
     }
 
@@ -349,6 +303,228 @@ __global__ void __launch_bounds__((K1Shape<NB, PASSES>::THREADS)) dec_gateup_ker
     }
 }
 
+// The lane's 32 activation columns of token 0.
+__device__ __forceinline__ void load_x0_slice(const DecArgs& a, int clo, int chi, float4 (&l4)[4], float4 (&h4)[4]) {
+    const float4* pl = reinterpret_cast<const float4*>(a.x + clo);
+    const float4* ph = reinterpret_cast<const float4*>(a.x + chi);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        l4[v] = pl[v];
+        h4[v] = ph[v];
+    }
+}
+
+// The lane's 32 activation columns of token `tok`.
+template <int TT>
+__device__ __forceinline__ void load_x_slice(const DecArgs& a, int tok, int clo, int chi, float4 (&l4)[4],
+                                             float4 (&h4)[4]) {
+    const float4* pl = reinterpret_cast<const float4*>(a.x + (int64_t)tok * a.H + clo);
+    const float4* ph = reinterpret_cast<const float4*>(a.x + (int64_t)tok * a.H + chi);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        l4[v] = pl[v];
+        h4[v] = ph[v];
+    }
+}
+
+template <int NB, int PASSES, int TT, int V>
+__global__ void __launch_bounds__((K1Shape<NB, PASSES>::THREADS)) dec_gateup_kernel(DecArgs a) {
+    using S = K1Shape<NB, PASSES>;
+    static_assert(S::IN_WAVE || S::UNITS == 1, "rows spanning waves need a single unit");
+    __shared__ DecRoute R;
+    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * TT * S::P * S::GROUPS)];
+    __shared__ int s_tok[kDecMaxT], s_hrow[kDecMaxT], s_nt, s_e;
+
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int f = (wave % S::W) * kWave + lane;
+    const int sl = f % S::SLICES;
+    const int clo = 256 * (sl >> 3) + q4k_slice_col_lo(sl & 7);
+    const int chi = 256 * (sl >> 3) + q4k_slice_col_hi(sl & 7);
+    const int slot = blockIdx.y;
+    const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
+    float4 xl4[TT][4], xh4[TT][4];
+
+    if (TT == 1 && !lead) {
+        // One token: the activations do not depend on the routing, so they are
+        // loaded first; slot s needs only the first s + 1 extraction rounds, and
+        // the shared expert none.
+        load_x_slice<TT>(a, 0, clo, chi, xl4[0], xh4[0]);
+        const bool shared = a.has_shared && slot == a.k;
+        if (!shared && slot >= a.k) return;
+        if (!shared) {
+            if (wave == 0) {
+                const int e = wave_topk_nth<V>(a.logits, a.E, slot);
+                if (lane == 0) s_e = e;
+            }
+            __syncthreads();
+        }
+        const int e = shared ? 0 : s_e;
+        int hrow[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) hrow[t] = shared ? a.k : slot;
+        dec_gateup_body<NB, PASSES, TT>(a, shared ? a.sgate : a.gate, shared ? a.sup : a.up, e, 1, hrow, xl4, xh4,
+                                        s_part);
+        return;
+    }
+
+    dec_route<V>(a.logits, a.T, a.E, a.k, a.renorm, R);
+    if (lead) {
+        dec_publish(R, a.T, a.E, a.k, a.r);
+        // hand the routing table to the down kernel
+        const int* src = reinterpret_cast<const int*>(&R);
+        for (int i = threadIdx.x; i < (int)(sizeof(DecRoute) / 4); i += blockDim.x) a.route_tab[i] = src[i];
+    }
+
+    // expert slot of this workgroup
+    const bool shared = a.has_shared && slot == a.T * a.k;
+    if (!shared && slot >= R.n_uniq) return;
+    const int e = shared ? 0 : R.uniq[slot];
+    if (threadIdx.x == 0) {
+        int nt = 0;
+        if (shared) {
+            for (int t = 0; t < a.T; ++t) {
+                s_tok[nt] = t;
+                s_hrow[nt] = a.T * a.k + t;
+                ++nt;
+            }
+        } else {
+            for (int q = R.uoff[slot]; q < R.uoff[slot + 1]; ++q) {
+                s_tok[nt] = R.pair[q] / a.k;
+                s_hrow[nt] = R.pair[q];
+                ++nt;
+            }
+        }
+        s_nt = nt;
+    }
+    __syncthreads();
+    const int nt = s_nt;
+#pragma unroll
+    for (int t = 0; t < TT; ++t)   // unconditional (clamped) loads: all in flight together
+        load_x_slice<TT>(a, s_tok[t < nt ? t : nt - 1], clo, chi, xl4[t], xh4[t]);
+    int hrows[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) hrows[t] = s_hrow[t < nt ? t : nt - 1];
+    dec_gateup_body<NB, PASSES, TT>(a, shared ? a.sgate : a.gate, shared ? a.sup : a.up, e, nt, hrows, xl4, xh4,
+                                    s_part);
+}
+
+// ---------------------------------------------------------------------------
+// K1 for one token: workgroup (tile, group g) owns a tile of rows of gate and
+// up for the expert slots j = g, g + G, g + 2G, ... (and the shared expert in
+// the last group).  Every wave runs the extraction itself and issues the loads
+// of slot j right after round j, so the weight traffic of the early slots
+// overlaps the remaining rounds; the dot products then consume the slots in
+// issue order while later loads are still in flight.  Group y == G is one
+// extra workgroup that publishes the routing (and the table for K2).
+// ---------------------------------------------------------------------------
+constexpr int kT1SlotsPerGroup = 4;
+
+template <int NB, int V>
+__global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_t1_kernel(DecArgs a, int G) {
+    using S = K1Shape<NB, 1>;
+    constexpr int SM = kT1SlotsPerGroup;
+    const int g = blockIdx.y;
+    if (g == G) {
+        __shared__ DecRoute R;
+        if (blockIdx.x != 0) return;
+        dec_route<V>(a.logits, 1, a.E, a.k, a.renorm, R);
+        dec_publish(R, 1, a.E, a.k, a.r);
+        const int* src = reinterpret_cast<const int*>(&R);
+        for (int i = threadIdx.x; i < (int)(sizeof(DecRoute) / 4); i += blockDim.x) a.route_tab[i] = src[i];
+        return;
+    }
+    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * (SM + 1) * S::P * S::GROUPS)];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int unit = wave / S::W;
+    const int f = (wave % S::W) * kWave + lane;
+    const int rr = f / S::SLICES;
+    const int sl = f % S::SLICES;
+    const int b = sl >> 3, part = sl & 7;
+    const int clo = 256 * b + q4k_slice_col_lo(part);
+    const int chi = 256 * b + q4k_slice_col_hi(part);
+    const int i = blockIdx.x * S::ROWS + unit * S::P + rr;
+    const int ic = i < a.I ? i : a.I - 1;   // rows past I load a valid row and are not stored
+    const bool has_sh = a.has_shared && g == G - 1;
+
+    // activations and logits first (they do not depend on the routing)
+    float4 xl4[1][4], xh4[1][4];
+    load_x0_slice(a, clo, chi, xl4[0], xh4[0]);
+    WaveExtract<V> ex;
+    ex.load(a.logits, a.E);
+    uint4 hg[SM + 1], qg[SM + 1], hu[SM + 1], qu[SM + 1];
+    auto issue = [&](int m, const QMat& Gm, const QMat& Um, int e) {
+        const uint8_t* gr = Gm.data + (int64_t)e * Gm.expert_bytes + (int64_t)ic * Gm.row_bytes + (int64_t)b * 144;
+        const uint8_t* ur = Um.data + (int64_t)e * Um.expert_bytes + (int64_t)ic * Um.row_bytes + (int64_t)b * 144;
+        hg[m] = *reinterpret_cast<const uint4*>(gr);
+        qg[m] = *reinterpret_cast<const uint4*>(gr + 16 + 16 * part);
+        hu[m] = *reinterpret_cast<const uint4*>(ur);
+        qu[m] = *reinterpret_cast<const uint4*>(ur + 16 + 16 * part);
+    };
+    if (has_sh) issue(SM, a.sgate, a.sup, 0);
+    int done = 0, win = 0;
+#pragma unroll
+    for (int m = 0; m < SM; ++m) {
+        const int jt = g + m * G;
+        if (jt < a.k) {
+            while (done <= jt) {
+                win = ex.next();
+                ++done;
+            }
+            issue(m, a.gate, a.up, win);
+        }
+    }
+
+    float xl[1][16], xh[1][16], sxl[1], sxh[1];
+    unpack_f4<1>(xl4[0], xl[0]);
+    unpack_f4<1>(xh4[0], xh[0]);
+    sxl[0] = sxh[0] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        sxl[0] += xl[0][j];
+        sxh[0] += xh[0][j];
+    }
+#pragma unroll
+    for (int m = 0; m <= SM; ++m) {
+        const bool live = (m == SM) ? has_sh : (g + m * G < a.k);
+        if (!live) continue;
+        const int hrow = (m == SM) ? a.k : g + m * G;
+        float pg[1], pu[1];
+        q4k_slice_dot<1>(hg[m], qg[m], part, 1, xl, xh, sxl, sxh, pg);
+        q4k_slice_dot<1>(hu[m], qu[m], part, 1, xl, xh, sxl, sxh, pu);
+        if constexpr (S::IN_WAVE) {
+            pg[0] = segment_sum<S::SLICES>(pg[0]);
+            pu[0] = segment_sum<S::SLICES>(pu[0]);
+            if (sl == S::SLICES - 1 && i < a.I) a.h[(int64_t)hrow * a.I + i] = silu_f32(pg[0]) * pu[0];
+        } else {
+            pg[0] = segment_sum<16>(pg[0]);
+            pu[0] = segment_sum<16>(pu[0]);
+            if ((lane & 15) == 15) {
+                const int grp = sl >> 4;
+                s_part[((2 * m + 0) * S::P + rr) * S::GROUPS + grp] = pg[0];
+                s_part[((2 * m + 1) * S::P + rr) * S::GROUPS + grp] = pu[0];
+            }
+        }
+    }
+    if constexpr (!S::IN_WAVE) {
+        __syncthreads();
+        // one thread per (slot, row): the row's 16-lane group sums in order
+        for (int job = threadIdx.x; job < (SM + 1) * S::P; job += blockDim.x) {
+            const int m = job / S::P, r2 = job % S::P;
+            const bool live = (m == SM) ? has_sh : (g + m * G < a.k);
+            const int i2 = blockIdx.x * S::ROWS + r2;
+            if (!live || i2 >= a.I) continue;
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int q = 0; q < S::GROUPS; ++q) {
+                gs += s_part[((2 * m + 0) * S::P + r2) * S::GROUPS + q];
+                us += s_part[((2 * m + 1) * S::P + r2) * S::GROUPS + q];
+            }
+            const int hrow = (m == SM) ? a.k : g + m * G;
+            a.h[(int64_t)hrow * a.I + i2] = silu_f32(gs) * us;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // K2: down + combine.  A "slice" of a down row is 16 quant bytes of a Q4_K
 // super-block (32 weights) or one 34-byte Q8_0 block (32 weights); NS slices
@@ -360,11 +536,12 @@ constexpr int kK2Passes = 2;
 
 template <int TT>
 struct K2Slots {
-    static constexpr int value = TT == 1 ? 2 : 1;   // slots per wave in flight (register budget)
+    static constexpr int value = 1;                      // expert slots per wave in flight
+    static constexpr int max_threads = TT == 1 ? 1024 : 512;   // register budget
 };
 
 template <int QD, int NS, int TT, int V>
-__global__ void __launch_bounds__(512) dec_down_kernel(DecArgs a) {
+__global__ void __launch_bounds__(K2Slots<TT>::max_threads) dec_down_kernel(DecArgs a) {
     constexpr int RP = kWave / NS;              // rows per wave pass
     constexpr int RO = RP * kK2Passes;          // output rows of the workgroup
     constexpr int SM = K2Slots<TT>::value;
@@ -375,7 +552,15 @@ __global__ void __launch_bounds__(512) dec_down_kernel(DecArgs a) {
     const int T = a.T, k = a.k, P = T * k;
     const int o0 = blockIdx.x * RO;
 
-    dec_route<V>(a.logits, T, a.E, k, a.renorm, R);
+    {   // the routing table written by the gate/up kernel's workgroup 0
+        int* dst = reinterpret_cast<int*>(&R);
+        for (int i = threadIdx.x; i < (int)(sizeof(DecRoute) / 4); i += blockDim.x) dst[i] = a.route_tab[i];
+    }
+    __syncthreads();
+    if (R.n_uniq < 0 || R.n_uniq > P) {   // corrupted table: nothing is read through it
+        if (threadIdx.x == 0) raise_error(kErrPairRange);
+        return;
+    }
     const int n_slots = R.n_uniq + (a.has_shared ? 1 : 0);
     const int rr = lane / NS, sl = lane % NS;
     int c_lo, c_hi;
@@ -397,7 +582,17 @@ __global__ void __launch_bounds__(512) dec_down_kernel(DecArgs a) {
             const int u = base + m * nwaves;
             live[m] = u < n_slots;
             shared[m] = live[m] && a.has_shared && u == R.n_uniq;
-            const int e = (!live[m] || shared[m]) ? 0 : R.uniq[u];
+            int e = (!live[m] || shared[m]) ? 0 : R.uniq[u];
+            if (live[m] && !shared[m]) {
+                const int q0 = R.uoff[u], q1 = R.uoff[u + 1];
+                bool ok = e >= 0 && e < a.E && q0 >= 0 && q1 >= q0 && q1 <= P && q1 - q0 <= TT;
+                for (int q = q0; ok && q < q1; ++q) ok = R.pair[q] >= 0 && R.pair[q] < P;
+                if (!ok) {
+                    if (lane == 0) raise_error(kErrExpertRange);
+                    live[m] = false;
+                    e = 0;
+                }
+            }
             const QMat D = shared[m] ? a.sdown : a.down;
             Db[m] = D.data + (int64_t)e * D.expert_bytes;
             rowb[m] = D.row_bytes;
@@ -413,11 +608,8 @@ __global__ void __launch_bounds__(512) dec_down_kernel(DecArgs a) {
 #pragma unroll
         for (int m = 0; m < SM; ++m) {
 #pragma unroll
-            for (int ps = 0; ps < kK2Passes; ++ps) {
-                w0[m][ps] = make_uint4(0, 0, 0, 0);
-                w1[m][ps] = make_uint4(0, 0, 0, 0);
+            for (int ps = 0; ps < kK2Passes; ++ps) {   // dead slots load expert 0's rows, never used
                 w2[m][ps] = 0;
-                if (!live[m]) continue;
                 const int o = o0 + ps * RP + rr;
                 const int oc = o < a.H ? o : a.H - 1;
                 const uint8_t* row = Db[m] + (int64_t)oc * rowb[m];
@@ -439,15 +631,13 @@ __global__ void __launch_bounds__(512) dec_down_kernel(DecArgs a) {
 #pragma unroll
         for (int m = 0; m < SM; ++m) {
 #pragma unroll
-            for (int t = 0; t < TT; ++t) {
-                if (t < np[m]) {
-                    const float4* pl = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m][t] * a.I + c_lo);
-                    const float4* ph = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m][t] * a.I + c_hi);
+            for (int t = 0; t < TT; ++t) {   // unconditional loads; rows past np read row 0, unused
+                const float4* pl = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m][t] * a.I + c_lo);
+                const float4* ph = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m][t] * a.I + c_hi);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        hl4[m][t][v] = pl[v];
-                        hh4[m][t][v] = ph[v];
-                    }
+                for (int v = 0; v < 4; ++v) {
+                    hl4[m][t][v] = pl[v];
+                    hh4[m][t][v] = ph[v];
                 }
             }
         }
@@ -553,9 +743,23 @@ hipError_t launch_k1v(const DecArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int NB, int V>
+hipError_t launch_k1_t1(const DecArgs& a, hipStream_t s) {
+    using S = K1Shape<NB, 1>;
+    const int G = (a.k + kT1SlotsPerGroup - 1) / kT1SlotsPerGroup;   // groups of at most 4 routed slots
+    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, G + 1);
+    dec_gateup_t1_kernel<NB, V><<<grid, S::THREADS, 0, s>>>(a, G);
+    return hipGetLastError();
+}
+
 template <int NB, int PASSES>
 hipError_t launch_k1(const DecArgs& a, hipStream_t s) {
     const int vpl = topk_vpl(a.E);
+    if (a.T == 1) {
+        if (vpl == 4) return launch_k1_t1<NB, 4>(a, s);
+        if (vpl == 8) return launch_k1_t1<NB, 8>(a, s);
+        return launch_k1_t1<NB, 16>(a, s);
+    }
     if (vpl == 4) return launch_k1v<NB, PASSES, 4>(a, s);
     if (vpl == 8) return launch_k1v<NB, PASSES, 8>(a, s);
     return launch_k1v<NB, PASSES, 16>(a, s);
@@ -566,8 +770,9 @@ hipError_t launch_k2v(const DecArgs& a, hipStream_t s) {
     constexpr int RO = (kWave / NS) * kK2Passes;
     const int slots = a.T * a.k + (a.has_shared ? 1 : 0);
     const int sm = a.T == 1 ? K2Slots<1>::value : K2Slots<kDecMaxT>::value;
+    const int max_waves = (a.T == 1 ? K2Slots<1>::max_threads : K2Slots<kDecMaxT>::max_threads) / kWave;
     int waves = (slots + sm - 1) / sm;
-    waves = waves < 4 ? 4 : (waves > 8 ? 8 : waves);   // at least one wave per token, at most 512 threads
+    waves = waves < 4 ? 4 : (waves > max_waves ? max_waves : waves);
     if (a.T == 1)
         dec_down_kernel<QD, NS, 1, V><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
     else

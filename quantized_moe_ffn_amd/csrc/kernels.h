@@ -62,7 +62,10 @@ struct DecArgs {
     float* y_shared;      // [T][H] or null
     const float* shared_scale;
     float* out;           // [T][H]
+    int* route_tab;       // workspace: the routing table K1 hands to K2 (kDecRouteTabBytes)
 };
+
+constexpr int kDecRouteTabBytes = 4096;
 
 bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd);
 hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s);

@@ -93,7 +93,7 @@ FfnWorkspace ffn_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
 }
 
 struct ForwardWorkspace {
-    size_t route, ffn, xq, xd, total;
+    size_t route, ffn, xq, xd, tab, total;
 };
 
 ForwardWorkspace forward_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
@@ -107,6 +107,8 @@ ForwardWorkspace forward_ws_layout(const moe_layer* L, int T, int k, uint32_t pa
     off += align_up((size_t)T * L->hidden, 256);
     w.xd = off;
     off += align_up((size_t)T * (L->hidden / 256) * sizeof(float), 256);
+    w.tab = off;
+    off += moe::kDecRouteTabBytes;
     w.total = off;
     return w;
 }
@@ -326,6 +328,7 @@ moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, 
         d.y_shared = y_shared;
         d.shared_scale = shared_scale;
         d.out = out;
+        d.route_tab = (int*)(ws + wl.tab);
         return from_hip(moe::launch_dec_fused(d, stream), "moe_forward (decode) launch");
     }
 

@@ -38,13 +38,18 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, i
                                           float& out_w) {
     const int lane = threadIdx.x & (kWave - 1);
     uint32_t key[V];
+    float xv[V];
     bool bad = false;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {   // unconditional loads (clamped index): all in flight at once
+        const int e = lane + kWave * v;
+        xv[v] = lg[e < E ? e : E - 1];
+    }
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int e = lane + kWave * v;
-        const float x = e < E ? lg[e] : 0.0f;
-        bad |= e < E && !isfinite(x);
-        key[v] = e < E ? max(order_key(x), 1u) : 0u;
+        bad |= e < E && !isfinite(xv[v]);
+        key[v] = e < E ? max(order_key(xv[v]), 1u) : 0u;
     }
     if (__any(bad)) {
         if (lane == 0) raise_error(kErrLogitNonFinite);
@@ -57,12 +62,23 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, i
         for (int v = 1; v < V; ++v) b = max(b, key[v]);
         const uint32_t M = wave_max_u32(b);
         int wv = V, wl = 0;
+        const uint64_t lanes = __ballot(b == M);
+        if (__popcll(lanes) == 1) {
+            // one lane holds the maximum: its lowest v holding it is the lowest index
+            wl = (int)__builtin_ctzll(lanes);
+            int vl = V;
 #pragma unroll
-        for (int v = V - 1; v >= 0; --v) {   // the lowest v with a match wins; then its lowest lane
-            const uint64_t msk = __ballot(key[v] == M);
-            if (msk != 0ull) {
-                wv = v;
-                wl = (int)__builtin_ctzll(msk);
+            for (int v = V - 1; v >= 0; --v)
+                if (key[v] == M) vl = v;
+            wv = __builtin_amdgcn_readlane(vl, wl);
+        } else {
+#pragma unroll
+            for (int v = V - 1; v >= 0; --v) {   // the lowest v with a match wins; then its lowest lane
+                const uint64_t msk = __ballot(key[v] == M);
+                if (msk != 0ull) {
+                    wv = v;
+                    wl = (int)__builtin_ctzll(msk);
+                }
             }
         }
 #pragma unroll
@@ -84,12 +100,113 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, i
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int e = lane + kWave * v;
-            if (e < E) part += expf(lg[e] - top);
+            if (e < E) part += expf(xv[v] - top);
         }
         const float sum = wave_sum(part);
         out_w = (lane < k) ? expf(my_l - top) / sum : 0.0f;
     }
     out_e = my_e;
+}
+
+// Incremental form of the extraction for callers that act between rounds:
+// load the keys once, then each next() returns the next slot's expert.
+template <int V>
+struct WaveExtract {
+    uint32_t key[V];
+    __device__ __forceinline__ void load(const float* __restrict__ lg, int E) {
+        const int lane = threadIdx.x & (kWave - 1);
+        float xv[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int e = lane + kWave * v;
+            xv[v] = lg[e < E ? e : E - 1];
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int e = lane + kWave * v;
+            key[v] = e < E ? max(order_key(xv[v]), 1u) : 0u;
+        }
+    }
+    __device__ __forceinline__ int next() {
+        const int lane = threadIdx.x & (kWave - 1);
+        uint32_t b = key[0];
+#pragma unroll
+        for (int v = 1; v < V; ++v) b = max(b, key[v]);
+        const uint32_t M = wave_max_u32(b);
+        int wv = V, wl = 0;
+        const uint64_t lanes = __ballot(b == M);
+        if (__popcll(lanes) == 1) {
+            wl = (int)__builtin_ctzll(lanes);
+            int vl = V;
+#pragma unroll
+            for (int v = V - 1; v >= 0; --v)
+                if (key[v] == M) vl = v;
+            wv = __builtin_amdgcn_readlane(vl, wl);
+        } else {
+#pragma unroll
+            for (int v = V - 1; v >= 0; --v) {
+                const uint64_t msk = __ballot(key[v] == M);
+                if (msk != 0ull) {
+                    wv = v;
+                    wl = (int)__builtin_ctzll(msk);
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (v == wv && lane == wl) key[v] = 0u;
+        return wl + kWave * wv;
+    }
+};
+
+// The expert of slot n (0-based) of one token: n + 1 rounds of the extraction
+// above, without the weights.  Uniform result.
+template <int V>
+__device__ __forceinline__ int wave_topk_nth(const float* __restrict__ lg, int E, int n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t key[V];
+    float xv[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int e = lane + kWave * v;
+        xv[v] = lg[e < E ? e : E - 1];
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int e = lane + kWave * v;
+        key[v] = e < E ? max(order_key(xv[v]), 1u) : 0u;
+    }
+    int win = 0;
+    for (int j = 0; j <= n; ++j) {
+        uint32_t b = key[0];
+#pragma unroll
+        for (int v = 1; v < V; ++v) b = max(b, key[v]);
+        const uint32_t M = wave_max_u32(b);
+        int wv = V, wl = 0;
+        const uint64_t lanes = __ballot(b == M);
+        if (__popcll(lanes) == 1) {
+            wl = (int)__builtin_ctzll(lanes);
+            int vl = V;
+#pragma unroll
+            for (int v = V - 1; v >= 0; --v)
+                if (key[v] == M) vl = v;
+            wv = __builtin_amdgcn_readlane(vl, wl);
+        } else {
+#pragma unroll
+            for (int v = V - 1; v >= 0; --v) {
+                const uint64_t msk = __ballot(key[v] == M);
+                if (msk != 0ull) {
+                    wv = v;
+                    wl = (int)__builtin_ctzll(msk);
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (v == wv && lane == wl) key[v] = 0u;
+        win = wl + kWave * wv;
+    }
+    return win;
 }
 
 // Values per lane for E experts (the kernels are instantiated for 4, 8, 16).
