@@ -14,7 +14,6 @@ oracle timed on a bounded sample of the same workload.  Progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -34,16 +33,6 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    d = os.path.join(ROOT, "quantized_moe_ffn_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profiles(config: str):
     """HBM bytes per launch of the dominant call from committed rocprofv3 counter runs, or None
     when they were taken on other kernel sources."""
@@ -54,6 +43,7 @@ def traffic_from_profiles(config: str):
         rec = json.load(open(p)).get(config)
     except (ValueError, OSError):
         return None
+    from quantized_moe_ffn_amd.profiling import kernel_source_hash
     if not rec or rec.get("kernel_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
