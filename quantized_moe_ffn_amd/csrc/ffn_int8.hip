@@ -7,26 +7,55 @@
 // re-quantized per (pair, 256-wide block of I) with the same rule before the
 // down projection.
 //
-// This version evaluates both projections with the decode path's in-register
+// Q4_K gate/up/down run as grouped int8 MFMA GEMMs (ffn_mfma.hip).  Other
+// format mixes evaluate both projections with the decode path's in-register
 // dequantization on x = xd*xq and h = hd*hq.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-hipError_t launch_ffn_int8(const FfnArgs& a, void* ws_extra, hipStream_t s) {
-    (void)ws_extra;
+hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s) {
+    if (a.tiles && mfma_path_supported(a.H, a.I, a.gate.qtype, a.up.qtype, a.down.qtype) &&
+        (!a.has_shared || (a.sgate.qtype == kQ4_K && a.sup.qtype == kQ4_K && a.sdown.qtype == kQ4_K))) {
+        MfmaArgs m{};
+        m.gate = a.gate;
+        m.up = a.up;
+        m.down = a.down;
+        m.sgate = a.sgate;
+        m.sup = a.sup;
+        m.sdown = a.sdown;
+        m.has_shared = a.has_shared;
+        m.H = a.H;
+        m.I = a.I;
+        m.T = a.T;
+        m.k = a.k;
+        m.E = a.E;
+        m.count = a.count;
+        m.offset = a.offset;
+        m.pair = a.pair;
+        m.xq = a.xq;
+        m.xd = a.xd;
+        m.xs = a.xs;
+        m.hq = a.hq;
+        m.hd = a.hd;
+        m.hs = a.hs;
+        m.y_pair = a.y_pair;
+        m.y_shared = a.y_shared;
+        const int mt = mfma_tile_rows(a.H, a.I);
+        const size_t half = (mfma_tiles_bytes(a.T, a.k, a.E, a.has_shared, a.H, a.I) - 256) / 2;
+        m.tile_e = a.tiles;
+        m.tile_m0 = a.tiles + half / sizeof(int32_t);
+        m.n_tiles = a.tiles + 2 * (half / sizeof(int32_t));
+        (void)mt;
+        return launch_ffn_mfma(m, s);
+    }
     hipError_t e = launch_gateup(a, 1, s);
     if (e != hipSuccess) return e;
     const int rows = a.T * a.k + (a.has_shared ? a.T : 0);
     e = launch_quantize_act(a.h, rows, a.I, a.hq, a.hd, s);
     if (e != hipSuccess) return e;
     return launch_down(a, 1, s);
-}
-
-size_t ffn_int8_extra_bytes(int T, int k, int E, int H, int I) {
-    (void)T; (void)k; (void)E; (void)H; (void)I;
-    return 0;
 }
 
 }  // namespace moe

@@ -47,7 +47,37 @@ struct FfnArgs {
     float* y_pair;                 // [T*k][H]
     float* y_shared;               // [T][H]
     int n_slots;                   // min(E, T*k) routed expert slots
+    int16_t* xs;                   // workspace [T][H/32]: per-32 sums of xq (int8 MFMA path)
+    int16_t* hs;                   // workspace [T*k + T][I/32]: per-32 sums of hq (int8 MFMA path)
+    int32_t* tiles;                // workspace: MFMA tile list (mfma_tiles_bytes)
 };
+
+// The grouped int8 MFMA GEMMs of the int8 path (Q4_K gate/up/down).
+constexpr int kMfmaMaxDim = 3584;
+
+struct MfmaArgs {
+    QMat gate, up, down, sgate, sup, sdown;
+    int has_shared, H, I, T, k, E;
+    const int32_t* count;
+    const int32_t* offset;
+    const int32_t* pair;
+    const int8_t* xq;              // [T][H]
+    const float* xd;               // [T][H/256]
+    int16_t* xs;                   // [T][H/32]   per-32 sums of xq
+    int8_t* hq;                    // [T*k + T][I]
+    float* hd;                     // [T*k + T][I/256]
+    int16_t* hs;                   // [T*k + T][I/32] per-32 sums of hq
+    float* y_pair;                 // [T*k][H]
+    float* y_shared;               // [T][H]
+    int32_t* tile_e;
+    int32_t* tile_m0;
+    int32_t* n_tiles;
+};
+
+bool mfma_path_supported(int H, int I, int qg, int qu, int qd);
+int mfma_tile_rows(int H, int I);
+size_t mfma_tiles_bytes(int T, int k, int E, int has_shared, int H, int I);
+hipError_t launch_ffn_mfma(const MfmaArgs& a, hipStream_t s);
 
 // The two-kernel decode layer (route + gate/up + SiLU; down + combine).
 struct DecArgs {
@@ -77,8 +107,7 @@ size_t route_workspace_bytes(int T, int E, int k);
 hipError_t launch_gateup(const FfnArgs& a, int xmode, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, int hmode, hipStream_t s);
 hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s);
-hipError_t launch_ffn_int8(const FfnArgs& a, void* ws_extra, hipStream_t s);
-size_t ffn_int8_extra_bytes(int T, int k, int E, int H, int I);
+hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s);
 
 hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s);
 hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared,

@@ -3,6 +3,7 @@
 #include "ffn_decode.hip"
 #include "route.hip"
 #include "quant.hip"
+#include "ffn_mfma.hip"
 #include "ffn_int8.hip"
 #include "decode_fused.hip"
 #include "moe_api.hip"

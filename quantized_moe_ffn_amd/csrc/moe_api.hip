@@ -73,23 +73,51 @@ moe::QMat to_qmat(const moe_qmatrix& m) {
 }
 
 struct FfnWorkspace {
-    size_t h, hq, hd, total;
+    size_t h, hq, hd, xs, hs, tiles, total;
+    bool mfma;
 };
+
+// The int8 path runs as grouped int8 MFMA GEMMs when every expert matrix is Q4_K.
+bool int8_uses_mfma(const moe_layer* L) {
+    const bool sh_ok = !L->has_shared || (L->sh_gate.qtype == MOE_Q4_K && L->sh_up.qtype == MOE_Q4_K &&
+                                          L->sh_down.qtype == MOE_Q4_K);
+    return sh_ok && moe::mfma_path_supported(L->hidden, L->inter, L->gate.qtype, L->up.qtype, L->down.qtype);
+}
 
 FfnWorkspace ffn_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
     const size_t rows = (size_t)T * k + (L->has_shared ? T : 0);
     FfnWorkspace w{};
+    w.mfma = path == MOE_FFN_INT8 && int8_uses_mfma(L);
+    size_t off = 0;
     w.h = 0;
-    size_t off = align_up(rows * L->inter * sizeof(float), 256);
+    if (!w.mfma) off += align_up(rows * L->inter * sizeof(float), 256);
     w.hq = off;
     w.hd = off;
     if (path == MOE_FFN_INT8) {
+        w.hq = off;
         off += align_up(rows * L->inter, 256);
         w.hd = off;
         off += align_up(rows * (L->inter / 256) * sizeof(float), 256);
+        if (w.mfma) {
+            w.xs = off;
+            off += align_up((size_t)T * (L->hidden / 32) * 2, 256);
+            w.hs = off;
+            off += align_up(rows * (L->inter / 32) * 2, 256);
+            w.tiles = off;
+            off += align_up(moe::mfma_tiles_bytes(T, k, L->n_experts, L->has_shared, L->hidden, L->inter), 256);
+        }
     }
     w.total = off;
     return w;
+}
+
+void set_ffn_ws(moe::FfnArgs& a, char* base, const FfnWorkspace& w) {
+    a.h = (float*)(base + w.h);
+    a.hq = (int8_t*)(base + w.hq);
+    a.hd = (float*)(base + w.hd);
+    a.xs = w.mfma ? (int16_t*)(base + w.xs) : nullptr;
+    a.hs = w.mfma ? (int16_t*)(base + w.hs) : nullptr;
+    a.tiles = w.mfma ? (int32_t*)(base + w.tiles) : nullptr;
 }
 
 struct ForwardWorkspace {
@@ -245,6 +273,8 @@ moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T,
     if (path == MOE_FFN_DECODE && !x) return fail(MOE_ERR_INVALID_ARGUMENT, "decode path needs x (fp32 [T][H])");
     if (path == MOE_FFN_INT8 && (!xq || !xd))
         return fail(MOE_ERR_INVALID_ARGUMENT, "int8 path needs xq and xd from moe_quantize_act");
+    if (path == MOE_FFN_INT8 && !aligned(xq, 16))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "xq must be 16-byte aligned");
     if ((x && !aligned(x, 4)) || (xd && !aligned(xd, 4)) || !aligned(y_pair, 4) || (y_shared && !aligned(y_shared, 4)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "fp32 arrays must be 4-byte aligned");
     const FfnWorkspace wl = ffn_ws_layout(L, T, k, path);
@@ -262,14 +292,11 @@ moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T,
     a.x = x;
     a.xq = xq;
     a.xd = xd;
-    char* ws = (char*)workspace;
-    a.h = (float*)(ws + wl.h);
-    a.hq = (int8_t*)(ws + wl.hq);
-    a.hd = (float*)(ws + wl.hd);
+    set_ffn_ws(a, (char*)workspace, wl);
     a.y_pair = y_pair;
     a.y_shared = y_shared;
     if (path == MOE_FFN_DECODE) return from_hip(moe::launch_ffn_decode(a, stream), "moe_expert_ffn_q (decode) launch");
-    return from_hip(moe::launch_ffn_int8(a, nullptr, stream), "moe_expert_ffn_q (int8) launch");
+    return from_hip(moe::launch_ffn_int8(a, stream), "moe_expert_ffn_q (int8) launch");
 }
 
 size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t ffn_flags) {
@@ -344,16 +371,13 @@ moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, 
     a.x = x;
     a.xq = (int8_t*)(ws + wl.xq);
     a.xd = (float*)(ws + wl.xd);
-    const FfnWorkspace fl = ffn_ws_layout(L, T, k, path);
-    a.h = (float*)(ws + wl.ffn + fl.h);
-    a.hq = (int8_t*)(ws + wl.ffn + fl.hq);
-    a.hd = (float*)(ws + wl.ffn + fl.hd);
+    set_ffn_ws(a, ws + wl.ffn, ffn_ws_layout(L, T, k, path));
     a.y_pair = y_pair;
     a.y_shared = y_shared;
     if (path == MOE_FFN_INT8) {
         e = moe::launch_quantize_act(x, T, L->hidden, (int8_t*)a.xq, (float*)a.xd, stream);
         if (e != hipSuccess) return from_hip(e, "moe_forward: quantisation launch");
-        e = moe::launch_ffn_int8(a, nullptr, stream);
+        e = moe::launch_ffn_int8(a, stream);
     } else {
         e = moe::launch_ffn_decode(a, stream);
     }

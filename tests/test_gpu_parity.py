@@ -248,6 +248,40 @@ def test_int8_prefill_chunk_sampled():
     _check_layer(m, dl, w, logits, x, bufs, 1, TOL_INT8, token_subset=toks)
 
 
+@pytest.mark.parametrize("over", [
+    dict(hidden=256, inter=768, n_experts=3, top_k=3, tokens=70),                  # odd block count along I
+    dict(hidden=768, inter=512, n_experts=40, top_k=4, tokens=130, shared=True),   # shared expert, 3 blocks along H
+    dict(hidden=2560, inter=512, n_experts=16, top_k=2, tokens=40),                # 32-token tiles (hidden > 2048)
+    dict(hidden=512, inter=256, n_experts=8, top_k=2, tokens=20, qt_down=oracle.Q8_0),  # Q8_0 down: in-register path
+])
+@pytest.mark.parametrize("fused", [True, False])
+def test_int8_ragged_shapes(over, fused):
+    m = qm()
+    _say("int8 ragged", over, fused)
+    dl, w = _layer("tiny", **over)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=6)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8, fused)
+    _check_layer(m, dl, w, logits, x, bufs, 1, TOL_INT8)
+
+
+def test_int8_determinism_and_batch_invariance():
+    """The int8 path gives the same bits run to run, and a token's output does not depend on
+    which other tokens share its experts' tiles."""
+    m = qm()
+    dl, w = _layer("tiny", tokens=150, n_experts=4)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=7)
+    a = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8).y_pair.cpu().numpy()
+    b = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8).y_pair.cpu().numpy()
+    assert np.array_equal(a, b)
+    sub = np.array([3, 77, 149])
+    c = _run_layer(m, dl, logits[sub], x[sub], w.top_k, m.MOE_FFN_INT8).y_pair.cpu().numpy()
+    k = w.top_k
+    rows = (sub[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    assert np.array_equal(c, a[rows])
+
+
 def test_integer_exact_layer_is_bitwise():
     """Gate weights all 1/8, up row i all (i mod 4), down row o all (o mod 3), x = 1 (H = I = 256):
     g = 32 (so silu(g) = g in fp32), h_i = 8192 (i mod 4), y_o = (o mod 3) * 8192 * 384.  Every
