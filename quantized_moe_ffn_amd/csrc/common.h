@@ -124,6 +124,9 @@ __device__ __forceinline__ float ubyte_f32(uint32_t v) {
     return (float)((v >> (8 * N)) & 0xFFu);
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware reciprocal (about 1 ulp).  For
+// g >= 17, 1 + e^-g rounds to 1 and the result is g exactly; for very negative
+// g the reciprocal of +inf is 0 and the result is -0.
+__device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 }  // namespace moe

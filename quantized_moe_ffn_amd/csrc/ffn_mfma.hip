@@ -11,24 +11,26 @@
 // K loop.  It is split into two 3-bit limbs, sc = 8*sh + sl, and the weights
 // enter the int8 MFMA as the bytes q*sl and q*sh (both <= 105): two MFMAs per
 // 32-deep K chunk, accumulated exactly in int32 over a 256-wide block, then
-// acc_l + 8*acc_h is scaled once per block by d*xd in fp32.  The min term is a
-// K = H/32 contraction: an fp16 MFMA of the per-32 activation sums X_j*xd
-// (precomputed per token, fp16) with -dmin*m_j (fp16), added to the same fp32
-// accumulators.
+// acc_l + 8*acc_h is scaled once per block by d*xd in fp32.  The block's min
+// term is one K = 16 bf16 MFMA pair: the lane halves carry the same eight
+// sub-blocks, as the hi and lo bf16 parts of X_j*xd (precomputed per token
+// and kept beside the tile), against the hi and lo parts of -dmin*m_j; the
+// four cross products keep the term to about 2^-16 relative.
 //
-// MFMA layouts (v_mfma_i32_32x32x32_i8 and v_mfma_f32_32x32x16_f16): lane l
+// MFMA layouts (v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_bf16): lane l
 // supplies row l%32 of A (tokens) and column l%32 of B (weight rows); both use
 // the same K positions for the same lane half and register byte; the result
 // C[m][n] sits in lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
 //
-// Work.  A tile is (expert, 32*MTILES tokens of its bucket); each tile is cut
-// into 256-row blocks of the output.  Workgroups of 8 waves take one (tile,
-// block); each wave owns 32 output rows (gate/up: the same 32 rows of both
-// matrices, so SiLU(gate)*up is formed in registers).  The tile's activations
-// sit in LDS for the whole K loop; weights stream from global memory straight
-// into registers.  Work items are laid out (expert, token tile, block) and
-// dealt to the 8 XCDs in contiguous ranges, so workgroups that share an
-// expert's weights share an L2.
+// Work.  A tile is (expert, 32*MTILES tokens of its bucket).  Gate/up:
+// workgroups of 8 waves take (tile, 256 rows of I); each wave owns 32 rows and
+// runs them through gate, then up (so SiLU(gate)*up and the requantisation of
+// h happen in registers).  Down: workgroups take (tile, up to 1024 rows of H),
+// each wave 32 rows per round.  The tile's int8 activations, their per-256
+// scales and per-32 sums sit in LDS for the whole K loop; weights stream from
+// global memory into registers one 256-block ahead of use.  Work items are
+// laid out (expert, token tile, row block) and dealt to the 8 XCDs in
+// contiguous ranges, so workgroups that share an expert's weights share an L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,6 +43,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kMWaves = 8;
 constexpr int kMThreads = kMWaves * kWave;
@@ -87,217 +90,180 @@ __device__ __forceinline__ bool work_item(const int32_t* n_tiles, int nblocks, i
 // register v in this lane half).
 __device__ __forceinline__ int c_row(int mt, int v, int h) { return mt * 32 + 8 * (v >> 2) + 4 * h + (v & 3); }
 
-// Smallest power of two >= x (x finite, > 0); 1 otherwise.
-__device__ __forceinline__ float pow2_ceil(float x) {
-    if (!(x > 0.0f) || !(x < INFINITY)) return 1.0f;
-    const uint32_t b = __float_as_uint(x);
-    if ((b & 0x7FFFFFu) == 0 && (b >> 23) != 0) return x;
-    const uint32_t e = (b >> 23) + 1;  // subnormal x: e = 1, i.e. 2^-126
-    return e >= 255 ? 1.0f : __uint_as_float(e << 23);
+// The A side of a tile in LDS.
+struct TileLds {
+    const int8_t* a;     // [MT][lda] int8 codes
+    const float* xd;     // [nsb][MT] per-256 scales
+    const uint16_t* xs;  // [MT][xs_ld] bf16: hi parts of the K/32 scaled sums, then the lo parts
+    int lda, xs_ld, k32;
+};
+
+// Byte j (0..3) of v in both 16-bit halves: (v_j) | (v_j << 16).
+__device__ __forceinline__ uint32_t byte_pair(uint32_t v, int j) {
+    return __builtin_amdgcn_perm(0u, v, (0x0Cu << 24) | ((uint32_t)j << 16) | (0x0Cu << 8) | (uint32_t)j);
 }
 
-// Q4_K x int8 grouped GEMM core.  For each of NT weight rows per lane
-// (rowp[nt], a row of nsb Q4_K blocks) and the A tile in LDS (32*MTILES rows of
-// int8, stride lda; per-256 scales xd_s[b*MT + m]; per-row power-of-two scales
-// s_sc[m] and their inverses s_inv[m]; per-32 code sums in global memory, row
-// pointer sums[mt] or null), sets
-//   out[nt][mt][v] = sum_k w[n][k] * a[m][k]     (C layout).
-template <int NT, int MTILES>
-__device__ __forceinline__ void q4k_i8_core(const uint8_t* const* rowp, int nsb, const int8_t* lds_a, int lda,
-                                            const float* xd_s, const float* s_sc, const float* s_inv,
-                                            const int16_t* const* sums, v16f (&out)[NT][MTILES]) {
+// One 256-block of a weight row, as a lane needs it: the 16-byte header and
+// its four 16-byte quant slices (lane half h: bytes 32c + 16h .. + 15).
+struct BlockRegs {
+    uint4 hdr;
+    uint4 q[4];
+};
+
+__device__ __forceinline__ void load_block(const uint8_t* blk, int h, BlockRegs& r) {
+    r.hdr = *reinterpret_cast<const uint4*>(blk);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint4*>(blk + 16 + 32 * c + 16 * h);
+}
+
+// out[mt] += (this 256-block's contribution) for the lane's weight row and the
+// tile's 32*MTILES rows, block index b of the row.
+template <int MTILES>
+__device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const TileLds& T, v16f (&out)[MTILES]) {
     constexpr int MT = 32 * MTILES;
     const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 31, h = lane >> 5;
-    const int8_t* a_lane = lds_a + n * lda + 16 * h;
+    const Q4KHead hd{br.hdr.x, br.hdr.y, br.hdr.z, br.hdr.w};
+    const int8_t* a_lane = T.a + n * T.lda + 256 * b + 16 * h;
 
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MTILES; ++mt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) out[nt][mt][v] = 0.0f;
+    // the eight 6-bit scales and mins of the block, packed one per byte
+    const uint32_t sc_lo = hd.h1 & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (hd.h3 & 0x0F0F0F0Fu) | ((hd.h1 >> 2) & 0x30303030u);
+    const uint32_t mn_lo = hd.h2 & 0x3F3F3F3Fu;
+    const uint32_t mn_hi = ((hd.h3 >> 4) & 0x0F0F0F0Fu) | ((hd.h2 >> 2) & 0x30303030u);
+    const uint32_t sl4[2] = {sc_lo & 0x07070707u, sc_hi & 0x07070707u};
+    const uint32_t sh4[2] = {(sc_lo >> 3) & 0x07070707u, (sc_hi >> 3) & 0x07070707u};
 
-    // min term, two 256-blocks per MFMA (lane half h takes block 2*s2 + h):
-    //   out = sum_{b,j} (-dmin_b m_bj / t) * (X_bj xd_b / s),  then out *= s * t,
-    // with s a power of two per token row (>= its largest xd) and t one per
-    // weight row (>= 63 * its largest dmin), so both operands stay within fp16
-    // range.  Each operand is carried as an fp16 pair hi + lo (hi*hi + hi*lo +
-    // lo*hi), which keeps the term to about 2^-22 relative.
-    float t_sc[NT], t_inv[NT];
+    v16i accl[MTILES], acch[MTILES];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        float mx = 0.0f;
-        for (int b = 0; b < nsb; ++b)
-            mx = fmaxf(mx, f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(rowp[nt] + (int64_t)b * 144 + 2)));
-        t_sc[nt] = pow2_ceil(63.0f * mx);
-        t_inv[nt] = 1.0f / t_sc[nt];
-    }
-    for (int s2 = 0; s2 < (nsb + 1) / 2; ++s2) {
-        const int b = 2 * s2 + h;
-        const bool ok = b < nsb;
-        v8h Ah[MTILES], Al[MTILES];
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t w4[4] = {br.q[c].x, br.q[c].y, br.q[c].z, br.q[c].w};
 #pragma unroll
-        for (int mt = 0; mt < MTILES; ++mt) {
-            v8h z = {};
-            Ah[mt] = z;
-            Al[mt] = z;
-            const int m = mt * 32 + n;
-            if (ok && sums[mt]) {
-                const uint4 raw = *reinterpret_cast<const uint4*>(sums[mt] + 8 * b);
-                const float f = xd_s[b * MT + m] * s_inv[m];
-                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int hi = 0; hi < 2; ++hi) {
+            const int j = 2 * c + hi;
+            const uint32_t sl = byte_pair(sl4[j >> 2], j & 3), sh = byte_pair(sh4[j >> 2], j & 3);
+            v4i Bl, Bh;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int16_t xs = (int16_t)((w4[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-                    const float av = (float)xs * f;
-                    const _Float16 ah = (_Float16)av;
-                    Ah[mt][i] = ah;
-                    Al[mt][i] = (_Float16)(av - (float)ah);
-                }
-            }
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            v8h Bh = {}, Bl = {};
-            if (ok) {
-                const uint4 v = *reinterpret_cast<const uint4*>(rowp[nt] + (int64_t)b * 144);
-                const Q4KHead hh{v.x, v.y, v.z, v.w};
-                const float dmin = q4k_dmin(hh);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    int sc, mn;
-                    q4k_scale_min(hh, j, sc, mn);
-                    const float bv = -(dmin * (float)mn) * t_inv[nt];
-                    const _Float16 bh = (_Float16)bv;
-                    Bh[j] = bh;
-                    Bl[j] = (_Float16)(bv - (float)bh);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t q = (hi ? (w4[i] >> 4) : w4[i]) & 0x0F0F0F0Fu;
+                Bl[i] = (int)pk_mul_u16(q, sl);
+                Bh[i] = (int)pk_mul_u16(q, sh);
             }
 #pragma unroll
             for (int mt = 0; mt < MTILES; ++mt) {
-                out[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[mt], Bh, out[nt][mt], 0, 0, 0);
-                out[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[mt], Bl, out[nt][mt], 0, 0, 0);
-                out[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al[mt], Bh, out[nt][mt], 0, 0, 0);
+                const v4i A = *reinterpret_cast<const v4i*>(a_lane + mt * 32 * T.lda + 32 * j);
+                if (j == 0) {
+                    const v16i z = {};
+                    accl[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bl, z, 0, 0, 0);
+                    acch[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bh, z, 0, 0, 0);
+                } else {
+                    accl[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bl, accl[mt], 0, 0, 0);
+                    acch[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bh, acch[mt], 0, 0, 0);
+                }
             }
         }
     }
+
+    // min term: out += sum_j (-dmin m_j) (X_j xd), hi/lo bf16 pairs; lane half
+    // 0 carries the hi parts of X_j xd, half 1 the lo parts
+    {
+        const float dmin = q4k_dmin(hd);
+        v8bf Bmh, Bml;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t mb = j < 4 ? mn_lo : mn_hi;
+            const float bv = -(dmin * (float)((mb >> (8 * (j & 3))) & 0xFFu));  // exact: 11 x 6 bits
+            const __bf16 bh = (__bf16)bv;
+            Bmh[j] = bh;
+            Bml[j] = (__bf16)(bv - (float)bh);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MTILES; ++mt) {
+            const v8bf Am =
+                *reinterpret_cast<const v8bf*>(T.xs + (mt * 32 + n) * T.xs_ld + h * T.k32 + 8 * b);
+            out[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Am, Bmh, out[mt], 0, 0, 0);
+            out[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Am, Bml, out[mt], 0, 0, 0);
+        }
+    }
+
+    // main term: out += (acc_l + 8 acc_h) * d * xd
+    const float d = q4k_d(hd);
 #pragma unroll
     for (int mt = 0; mt < MTILES; ++mt) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const float4 s4 = *reinterpret_cast<const float4*>(s_sc + mt * 32 + 8 * g + 4 * h);
-            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+            const float4 x4 = *reinterpret_cast<const float4*>(T.xd + b * MT + mt * 32 + 8 * g + 4 * h);
+            const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) out[nt][mt][4 * g + r] *= sv[r] * t_sc[nt];
-        }
-    }
-
-    for (int b = 0; b < nsb; ++b) {
-        Q4KHead hd[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const uint4 v = *reinterpret_cast<const uint4*>(rowp[nt] + (int64_t)b * 144);
-            hd[nt] = Q4KHead{v.x, v.y, v.z, v.w};
-        }
-        v16i accl[NT][MTILES], acch[NT][MTILES];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < MTILES; ++mt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) accl[nt][mt][v] = acch[nt][mt][v] = 0;
-
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            uint4 raw[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                raw[nt] = *reinterpret_cast<const uint4*>(rowp[nt] + (int64_t)b * 144 + 16 + 32 * c + 16 * h);
-#pragma unroll
-            for (int hi = 0; hi < 2; ++hi) {
-                const int j = 2 * c + hi;
-                v4i A[MTILES];
-#pragma unroll
-                for (int mt = 0; mt < MTILES; ++mt)
-                    A[mt] = *reinterpret_cast<const v4i*>(a_lane + mt * 32 * lda + 256 * b + 32 * j);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    int sc, mn;
-                    q4k_scale_min(hd[nt], j, sc, mn);
-                    const uint32_t sl = (uint32_t)(sc & 7) * 0x10001u, sh = (uint32_t)(sc >> 3) * 0x10001u;
-                    const uint32_t w4[4] = {raw[nt].x, raw[nt].y, raw[nt].z, raw[nt].w};
-                    v4i Bl, Bh;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t q = (hi ? (w4[i] >> 4) : w4[i]) & 0x0F0F0F0Fu;
-                        Bl[i] = (int)pk_mul_u16(q, sl);
-                        Bh[i] = (int)pk_mul_u16(q, sh);
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < MTILES; ++mt) {
-                        accl[nt][mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt], Bl, accl[nt][mt], 0, 0, 0);
-                        acch[nt][mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt], Bh, acch[nt][mt], 0, 0, 0);
-                    }
-                }
-            }
-        }
-        // scale the block: out += (acc_l + 8 acc_h) * d * xd
-#pragma unroll
-        for (int mt = 0; mt < MTILES; ++mt) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 x4 = *reinterpret_cast<const float4*>(xd_s + b * MT + mt * 32 + 8 * g + 4 * h);
-                const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const float d = q4k_d(hd[nt]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int v = 4 * g + r;
-                        const int sm = accl[nt][mt][v] + (acch[nt][mt][v] << 3);
-                        out[nt][mt][v] = fmaf((float)sm, d * xv[r], out[nt][mt][v]);
-                    }
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int v = 4 * g + r;
+                const int sm = accl[mt][v] + (acch[mt][v] << 3);
+                out[mt][v] = fmaf((float)sm, d * xv[r], out[mt][v]);
             }
         }
     }
 }
 
-// Per-row scales of the min-term operand (threads < MT).
-template <int MT>
-__device__ __forceinline__ void row_scales(const float* xd_s, int nsb, float* s_sc, float* s_inv) {
-    const int m = threadIdx.x;
-    if (m >= MT) return;
-    float mx = 0.0f;
-    for (int b = 0; b < nsb; ++b) mx = fmaxf(mx, xd_s[b * MT + m]);
-    const float sc = pow2_ceil(mx);
-    s_sc[m] = sc;
-    s_inv[m] = 1.0f / sc;
-}
-
-// Loads the A tile: rows src_row[m] (or zeros when < 0) of an int8 matrix with
-// K columns, and their per-256 scales, into LDS.
+// Loads the A side of tile: rows src_row[m] (zeros when < 0) of an int8 matrix
+// with K columns, their per-256 scales, and their per-32 code sums.
 template <int MTILES>
-__device__ __forceinline__ void load_a_tile(const int8_t* __restrict__ q, const float* __restrict__ qd, int K,
-                                            const int* s_src, int8_t* lds_a, int lda, float* xd_s) {
+__device__ __forceinline__ void load_tile(const int8_t* __restrict__ q, const float* __restrict__ qd,
+                                          const uint16_t* __restrict__ qs, int K, const int* s_src, int8_t* lds_a,
+                                          int lda, float* xd_s, uint16_t* xs_s, int xs_ld) {
     constexpr int MT = 32 * MTILES;
-    const int per_row = K / 16;
-    for (int idx = threadIdx.x; idx < MT * per_row; idx += blockDim.x) {
-        const int m = idx / per_row, c = idx - m * per_row;
-        const int src = s_src[m];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (src >= 0) v = *reinterpret_cast<const uint4*>(q + (int64_t)src * K + 16 * c);
-        *reinterpret_cast<uint4*>(lds_a + m * lda + 16 * c) = v;
+    constexpr int kBatch = 8;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    // codes: thread -> (row m0 + j*rows_per_pass, 16-byte column c); K/16 <= 224 < nthr
+    {
+        const int per_row = K / 16;
+        const int rows_per_pass = nthr / per_row;
+        const int c = tid % per_row, m0 = tid / per_row;
+        if (m0 < rows_per_pass) {
+            for (int mb = m0; mb < MT; mb += kBatch * rows_per_pass) {
+                uint4 v[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int m = min(mb + i * rows_per_pass, MT - 1);
+                    const int src = s_src[m];
+                    v[i] = *reinterpret_cast<const uint4*>(q + (int64_t)max(src, 0) * K + 16 * c);
+                    if (src < 0) v[i] = make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int m = mb + i * rows_per_pass;
+                    if (m < MT) *reinterpret_cast<uint4*>(lds_a + m * lda + 16 * c) = v[i];
+                }
+            }
+        }
     }
+    // per-256 scales: [b][m]
     const int nsb = K / 256;
-    for (int idx = threadIdx.x; idx < MT * nsb; idx += blockDim.x) {
-        const int b = idx / MT, m = idx - b * MT;
+    for (int idx = tid; idx < MT * nsb; idx += nthr) {
+        const int b = idx / MT, m = idx % MT;
         const int src = s_src[m];
         xd_s[b * MT + m] = src >= 0 ? qd[(int64_t)src * nsb + b] : 0.0f;
     }
+    // per-32 sums, bf16 hi then lo: 2*K/32 values per row, 8 per uint4
+    {
+        const int per_row = (2 * (K / 32)) / 8;
+        const int rows_per_pass = nthr / per_row;
+        const int c = tid % per_row, m0 = tid / per_row;
+        if (m0 < rows_per_pass) {
+            for (int m = m0; m < MT; m += rows_per_pass) {
+                const int src = s_src[m];
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (src >= 0) v = *reinterpret_cast<const uint4*>(qs + (int64_t)src * (2 * (K / 32)) + 8 * c);
+                *reinterpret_cast<uint4*>(xs_s + m * xs_ld + 8 * c) = v;
+            }
+        }
+    }
+}
+
+// LDS bytes of a tile's A side (dynamic part) for K columns.
+template <int MTILES>
+constexpr size_t tile_lds_bytes(int K) {
+    return (size_t)(32 * MTILES) * (K + kLdsPad) + (size_t)(K / 256) * 32 * MTILES * sizeof(float) +
+           (size_t)(32 * MTILES) * (2 * (K / 32) + 8) * sizeof(uint16_t);
 }
 
 // Rows of tile u: A-source row (token for gate/up, h row for down) and output
@@ -332,6 +298,17 @@ __device__ __forceinline__ void tile_rows(const MfmaArgs& a, int e, int m0, bool
     s_out[tid] = orow;
 }
 
+// Carves the dynamic LDS into the tile's A side.
+template <int MTILES>
+__device__ __forceinline__ TileLds carve(unsigned char* lds, int K, int8_t*& a, float*& xd, uint16_t*& xs) {
+    constexpr int MT = 32 * MTILES;
+    const int lda = K + kLdsPad, xs_ld = 2 * (K / 32) + 8;
+    a = reinterpret_cast<int8_t*>(lds);
+    xd = reinterpret_cast<float*>(lds + (size_t)MT * lda);
+    xs = reinterpret_cast<uint16_t*>(lds + (size_t)MT * lda + (size_t)(K / 256) * MT * sizeof(float));
+    return TileLds{a, xd, xs, lda, xs_ld, K / 32};
+}
+
 template <int MTILES>
 __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
@@ -340,10 +317,8 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     __shared__ float s_red[kMWaves * MT];
     __shared__ __attribute__((aligned(16))) float s_id[MT];
     __shared__ float s_d[MT];
-    __shared__ __attribute__((aligned(16))) float s_sc[MT];
-    __shared__ float s_inv[MT];
 
-    const int H = a.H, I = a.I, NB = I / 256;
+    const int H = a.H, I = a.I, NB = I / 256, nsb = H / 256;
     int u, nb;
     if (!work_item(a.n_tiles, NB, u, nb)) return;
     const int e = a.tile_e[u], m0 = a.tile_m0[u];
@@ -351,12 +326,11 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     tile_rows<MT>(a, e, m0, false, s_src, s_out);
     __syncthreads();
 
-    const int lda = H + kLdsPad;
-    int8_t* lds_a = reinterpret_cast<int8_t*>(lds);
-    float* xd_s = reinterpret_cast<float*>(lds + MT * lda);
-    load_a_tile<MTILES>(a.xq, a.xd, H, s_src, lds_a, lda, xd_s);
-    __syncthreads();
-    row_scales<MT>(xd_s, H / 256, s_sc, s_inv);
+    int8_t* lds_a;
+    float* xd_s;
+    uint16_t* xs_s;
+    const TileLds T = carve<MTILES>(lds, H, lds_a, xd_s, xs_s);
+    load_tile<MTILES>(a.xq, a.xd, a.xs, H, s_src, lds_a, T.lda, xd_s, xs_s, T.xs_ld);
     __syncthreads();
 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -364,16 +338,52 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     const int i = nb * 256 + wave * 32 + n;  // row of gate and up (column of h)
     const QMat G = shared ? a.sgate : a.gate, U = shared ? a.sup : a.up;
     const int64_t eo = shared ? 0 : (int64_t)e;
-    const uint8_t* rowp[2] = {G.data + eo * G.expert_bytes + (int64_t)i * G.row_bytes,
+    const uint8_t* rows[2] = {G.data + eo * G.expert_bytes + (int64_t)i * G.row_bytes,
                               U.data + eo * U.expert_bytes + (int64_t)i * U.row_bytes};
-    const int16_t* sums[MTILES];
+
+    // gate row, then up row: 2*nsb blocks, one block of prefetch
+    v16f acc[MTILES], g_out[MTILES];
 #pragma unroll
-    for (int mt = 0; mt < MTILES; ++mt) {
-        const int src = s_src[mt * 32 + n];
-        sums[mt] = src >= 0 ? a.xs + (int64_t)src * (H / 32) : nullptr;
+    for (int mt = 0; mt < MTILES; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
+    // blocks s = 0 .. 2*nsb-1 (gate row, then up row), loaded two ahead of use
+    auto blk_ptr = [&](int sx) {
+        const int r = sx >= nsb ? 1 : 0;
+        return rows[r] + (int64_t)(sx - r * nsb) * 144;
+    };
+    const int steps = 2 * nsb;
+    auto step = [&](const BlockRegs& br, int sx) {
+        block_mma<MTILES>(br, sx >= nsb ? sx - nsb : sx, T, acc);
+        if (sx == nsb - 1) {
+#pragma unroll
+            for (int mt = 0; mt < MTILES; ++mt) {
+                g_out[mt] = acc[mt];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
+            }
+        }
+    };
+    // three register buffers rotate through a 3x unrolled loop (no copies of
+    // registers that loads in flight still write)
+    BlockRegs b0, b1, b2;
+    load_block(blk_ptr(0), h, b0);
+    load_block(blk_ptr(min(1, steps - 1)), h, b1);
+    for (int s = 0; s < steps; s += 3) {
+        load_block(blk_ptr(min(s + 2, steps - 1)), h, b2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(b0, s);
+        if (s + 1 < steps) {
+            load_block(blk_ptr(min(s + 3, steps - 1)), h, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            step(b1, s + 1);
+        }
+        if (s + 2 < steps) {
+            load_block(blk_ptr(min(s + 4, steps - 1)), h, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            step(b2, s + 2);
+        }
     }
-    v16f acc[2][MTILES];
-    q4k_i8_core<2, MTILES>(rowp, H / 256, lds_a, lda, xd_s, s_sc, s_inv, sums, acc);
 
     // h = silu(g) * u, then per-token amax over the 256 rows of this block
     float hv[MTILES][16];
@@ -381,7 +391,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     for (int mt = 0; mt < MTILES; ++mt) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const float hh = silu_f32(acc[0][mt][v]) * acc[1][mt][v];
+            const float hh = silu_f32(g_out[mt][v]) * acc[mt][v];
             hv[mt][v] = hh;
             float am = isfinite(hh) ? fabsf(hh) : INFINITY;
             am = half32_max(am);
@@ -402,7 +412,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
         }
         s_id[m] = id;
         s_d[m] = d;
-        if (s_out[m] >= 0) a.hd[(int64_t)s_out[m] * NB + nb] = d;
+        if (s_out[m] >= 0) a.hd[(uint32_t)(s_out[m] * NB + nb)] = d;
     }
     __syncthreads();
     const int I32 = I / 32;
@@ -423,23 +433,31 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
                     q = (int)qf;
                 }
                 const int orow = s_out[m];
-                if (orow >= 0) a.hq[(int64_t)orow * I + i] = (int8_t)q;
+                if (orow >= 0) a.hq[(uint32_t)(orow * I + i)] = (int8_t)q;
                 const int qs = half32_sum(q);
-                if (n == 0 && orow >= 0) a.hs[(int64_t)orow * I32 + nb * 8 + wave] = (int16_t)qs;
+                if (n == 0 && orow >= 0) {
+                    const float sv = (float)qs * s_d[m];
+                    const __bf16 sh = (__bf16)sv;
+                    const __bf16 sl = (__bf16)(sv - (float)sh);
+                    const uint32_t o0 = (uint32_t)(orow * (2 * I32) + nb * 8 + wave);
+                    a.hs[o0] = __builtin_bit_cast(uint16_t, sh);
+                    a.hs[o0 + I32] = __builtin_bit_cast(uint16_t, sl);
+                }
             }
         }
     }
 }
+
+constexpr int kDownRounds = 4;  // 256-row rounds per down workgroup
 
 template <int MTILES>
 __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int s_src[MT], s_out[MT];
-    __shared__ __attribute__((aligned(16))) float s_sc[MT];
-    __shared__ float s_inv[MT];
 
-    const int H = a.H, I = a.I, NB = H / 256;
+    const int H = a.H, I = a.I, nsb = I / 256;
+    const int NB = (H / 256 + kDownRounds - 1) / kDownRounds;
     int u, ob;
     if (!work_item(a.n_tiles, NB, u, ob)) return;
     const int e = a.tile_e[u], m0 = a.tile_m0[u];
@@ -447,47 +465,78 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     tile_rows<MT>(a, e, m0, true, s_src, s_out);
     __syncthreads();
 
-    const int lda = I + kLdsPad;
-    int8_t* lds_a = reinterpret_cast<int8_t*>(lds);
-    float* hd_s = reinterpret_cast<float*>(lds + MT * lda);
-    load_a_tile<MTILES>(a.hq, a.hd, I, s_src, lds_a, lda, hd_s);
-    __syncthreads();
-    row_scales<MT>(hd_s, I / 256, s_sc, s_inv);
+    int8_t* lds_a;
+    float* hd_s;
+    uint16_t* hs_s;
+    const TileLds T = carve<MTILES>(lds, I, lds_a, hd_s, hs_s);
+    load_tile<MTILES>(a.hq, a.hd, a.hs, I, s_src, lds_a, T.lda, hd_s, hs_s, T.xs_ld);
     __syncthreads();
 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int n = lane & 31, h = lane >> 5;
-    const int o = ob * 256 + wave * 32 + n;
     const QMat D = shared ? a.sdown : a.down;
     const int64_t eo = shared ? 0 : (int64_t)e;
-    const uint8_t* rowp[1] = {D.data + eo * D.expert_bytes + (int64_t)o * D.row_bytes};
-    const int16_t* sums[MTILES];
-#pragma unroll
-    for (int mt = 0; mt < MTILES; ++mt) {
-        const int src = s_src[mt * 32 + n];
-        sums[mt] = src >= 0 ? a.hs + (int64_t)src * (I / 32) : nullptr;
-    }
-    v16f acc[1][MTILES];
-    q4k_i8_core<1, MTILES>(rowp, I / 256, lds_a, lda, hd_s, s_sc, s_inv, sums, acc);
-
+    const int r0 = ob * kDownRounds;
+    const int nr = min(kDownRounds, H / 256 - r0);
+    const uint8_t* base = D.data + eo * D.expert_bytes + (int64_t)(r0 * 256 + wave * 32 + n) * D.row_bytes;
+    const int64_t round_stride = 256 * D.row_bytes;
     const int npairs = a.T * a.k;
+
+    v16f acc[MTILES];
 #pragma unroll
-    for (int mt = 0; mt < MTILES; ++mt) {
+    for (int mt = 0; mt < MTILES; ++mt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int orow = s_out[c_row(mt, v, h)];
-            if (orow < 0) continue;
-            if (orow < npairs)
-                a.y_pair[(int64_t)orow * H + o] = acc[0][mt][v];
-            else
-                a.y_shared[(int64_t)(orow - npairs) * H + o] = acc[0][mt][v];
+        for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
+    auto blk_ptr = [&](int sx) {
+        const int r = sx / nsb;
+        return base + r * round_stride + (int64_t)(sx - r * nsb) * 144;
+    };
+    const int steps = nr * nsb;
+    auto step = [&](const BlockRegs& br, int sx) {
+        const int r = sx / nsb, b = sx - r * nsb;
+        block_mma<MTILES>(br, b, T, acc);
+        if (b == nsb - 1) {
+            const int o = (r0 + r) * 256 + wave * 32 + n;
+#pragma unroll
+            for (int mt = 0; mt < MTILES; ++mt) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int orow = s_out[c_row(mt, v, h)];
+                    if (orow >= 0) {
+                        if (orow < npairs)
+                            a.y_pair[(uint32_t)(orow * H + o)] = acc[mt][v];
+                        else
+                            a.y_shared[(uint32_t)((orow - npairs) * H + o)] = acc[mt][v];
+                    }
+                    acc[mt][v] = 0.0f;
+                }
+            }
+        }
+    };
+    BlockRegs b0, b1, b2;
+    load_block(blk_ptr(0), h, b0);
+    load_block(blk_ptr(min(1, steps - 1)), h, b1);
+    for (int s = 0; s < steps; s += 3) {
+        load_block(blk_ptr(min(s + 2, steps - 1)), h, b2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(b0, s);
+        if (s + 1 < steps) {
+            load_block(blk_ptr(min(s + 3, steps - 1)), h, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            step(b1, s + 1);
+        }
+        if (s + 2 < steps) {
+            load_block(blk_ptr(min(s + 4, steps - 1)), h, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            step(b2, s + 2);
         }
     }
 }
 
-// xs[t][c] = sum_{l<32} xq[t][32c + l] (exact, |xs| <= 4064), one thread per (t, c).
-__global__ void __launch_bounds__(256) act_sums_kernel(const int8_t* __restrict__ xq, int64_t n, int K,
-                                                       int16_t* __restrict__ xs) {
+// xs[t] = the bf16 hi parts of v_c = (sum_{l<32} xq[t][32c + l]) * xd[t][c/8]
+// for c < K/32, then their lo parts bf16(v_c - hi_c); one thread per (t, c).
+__global__ void __launch_bounds__(256) act_sums_kernel(const int8_t* __restrict__ xq, const float* __restrict__ xd,
+                                                       int64_t n, int K, uint16_t* __restrict__ xs) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= n) return;
     const int k32 = K / 32;
@@ -501,7 +550,11 @@ __global__ void __launch_bounds__(256) act_sums_kernel(const int8_t* __restrict_
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int bsh = 0; bsh < 32; bsh += 8) s += (int)(int8_t)(w[i] >> bsh);
-    xs[idx] = (int16_t)s;
+    const float v = (float)s * xd[t * (K / 256) + c / 8];
+    const __bf16 hi = (__bf16)v;
+    const __bf16 lo = (__bf16)(v - (float)hi);
+    xs[t * 2 * k32 + c] = __builtin_bit_cast(uint16_t, hi);
+    xs[t * 2 * k32 + k32 + c] = __builtin_bit_cast(uint16_t, lo);
 }
 
 // Tile list: tiles of 'mt' bucket entries per expert with count > 0, in
@@ -537,10 +590,6 @@ __global__ void __launch_bounds__(1024) mfma_tiles_kernel(const int32_t* __restr
     }
 }
 
-template <int MTILES>
-size_t gateup_lds(int H) {
-    return (size_t)(32 * MTILES) * (H + kLdsPad) + (size_t)(H / 256) * 32 * MTILES * sizeof(float);
-}
 
 int max_tiles(int T, int k, int E, int has_shared, int mt) {
     const int npairs = T * k;
@@ -558,11 +607,12 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n_sums = (int64_t)a.T * (a.H / 32);
-    act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, n_sums, a.H, a.xs);
+    act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, a.xd, n_sums, a.H, a.xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    gateup_mfma_kernel<MTILES><<<grid_for(maxt * (a.I / 256)), kMThreads, gateup_lds<MTILES>(a.H), s>>>(a);
+    gateup_mfma_kernel<MTILES><<<grid_for(maxt * (a.I / 256)), kMThreads, tile_lds_bytes<MTILES>(a.H), s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    down_mfma_kernel<MTILES><<<grid_for(maxt * (a.H / 256)), kMThreads, gateup_lds<MTILES>(a.I), s>>>(a);
+    const int nb_down = (a.H / 256 + kDownRounds - 1) / kDownRounds;
+    down_mfma_kernel<MTILES><<<grid_for(maxt * nb_down), kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(a);
     return hipGetLastError();
 }
 
@@ -570,6 +620,12 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
 
 bool mfma_path_supported(int H, int I, int qg, int qu, int qd) {
     return qg == kQ4_K && qu == kQ4_K && qd == kQ4_K && H <= kMfmaMaxDim && I <= kMfmaMaxDim;
+}
+
+// The kernels index h and y rows with 32-bit element offsets.
+bool mfma_rows_fit(int T, int k, int H, int I) {
+    const int64_t rows = (int64_t)T * k + T;
+    return rows * (H > I ? H : I) < ((int64_t)1 << 31);
 }
 
 int mfma_tile_rows(int H, int I) { return (H <= 2048 && I <= 2048) ? 64 : 32; }

@@ -47,8 +47,8 @@ struct FfnArgs {
     float* y_pair;                 // [T*k][H]
     float* y_shared;               // [T][H]
     int n_slots;                   // min(E, T*k) routed expert slots
-    int16_t* xs;                   // workspace [T][H/32]: per-32 sums of xq (int8 MFMA path)
-    int16_t* hs;                   // workspace [T*k + T][I/32]: per-32 sums of hq (int8 MFMA path)
+    uint16_t* xs;                  // workspace [T][2][H/32] bf16 (int8 MFMA path)
+    uint16_t* hs;                  // workspace [T*k + T][2][I/32] bf16 (int8 MFMA path)
     int32_t* tiles;                // workspace: MFMA tile list (mfma_tiles_bytes)
 };
 
@@ -63,10 +63,10 @@ struct MfmaArgs {
     const int32_t* pair;
     const int8_t* xq;              // [T][H]
     const float* xd;               // [T][H/256]
-    int16_t* xs;                   // [T][H/32]   per-32 sums of xq
+    uint16_t* xs;                  // [T][2][H/32] bf16 hi, lo parts of the per-32 sums of xq times xd
     int8_t* hq;                    // [T*k + T][I]
     float* hd;                     // [T*k + T][I/256]
-    int16_t* hs;                   // [T*k + T][I/32] per-32 sums of hq
+    uint16_t* hs;                  // [T*k + T][2][I/32] the same for hq times hd
     float* y_pair;                 // [T*k][H]
     float* y_shared;               // [T][H]
     int32_t* tile_e;
@@ -75,6 +75,7 @@ struct MfmaArgs {
 };
 
 bool mfma_path_supported(int H, int I, int qg, int qu, int qd);
+bool mfma_rows_fit(int T, int k, int H, int I);
 int mfma_tile_rows(int H, int I);
 size_t mfma_tiles_bytes(int T, int k, int E, int has_shared, int H, int I);
 hipError_t launch_ffn_mfma(const MfmaArgs& a, hipStream_t s);

@@ -375,10 +375,19 @@ __global__ void __launch_bounds__(1024) bucket_scan_kernel(int n_tiles, int E, i
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int t = 0; t < n_tiles; ++t) {
-            const int h = tile_hist[(int64_t)t * E + e];
-            tile_hist[(int64_t)t * E + e] = run;
-            run += h;
+        // per-expert exclusive prefix over tiles, 16 loads in flight at a time
+        constexpr int kB = 16;
+        for (int t0 = 0; t0 < n_tiles; t0 += kB) {
+            int hv[kB];
+#pragma unroll
+            for (int i = 0; i < kB; ++i) hv[i] = tile_hist[(int64_t)min(t0 + i, n_tiles - 1) * E + e];
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                if (t0 + i < n_tiles) {
+                    tile_hist[(int64_t)(t0 + i) * E + e] = run;
+                    run += hv[i];
+                }
+            }
         }
     }
     int total, n_act;
@@ -388,7 +397,6 @@ __global__ void __launch_bounds__(1024) bucket_scan_kernel(int n_tiles, int E, i
         r.count[e] = run;
         r.offset[e] = off;
         if (run > 0) r.active[apos] = e;
-        for (int t = 0; t < n_tiles; ++t) tile_hist[(int64_t)t * E + e] += off;
     }
     if (e == 0) {
         r.offset[E] = total;
@@ -397,15 +405,17 @@ __global__ void __launch_bounds__(1024) bucket_scan_kernel(int n_tiles, int E, i
     (void)P;
 }
 
+// pair[offset[e] + (pairs of e in earlier tiles) + rank of p in its tile] = p
 __global__ void __launch_bounds__(256) bucket_scatter_kernel(const int32_t* __restrict__ idx, int P,
                                                              int E, const int32_t* __restrict__ tile_base,
+                                                             const int32_t* __restrict__ offset,
                                                              const int32_t* __restrict__ rank,
                                                              int32_t* pair) {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= P) return;
     const int tile = p / kTilePairs;
     const int e = idx[p];
-    pair[tile_base[(int64_t)tile * E + e] + rank[p]] = p;
+    pair[offset[e] + tile_base[(int64_t)tile * E + e] + rank[p]] = p;
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, const RoutingPtrs& r,
@@ -432,7 +442,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, co
         route_tokens_kernel<16><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
     bucket_tile_kernel<<<n_tiles, kTilePairs, 0, s>>>(r.idx, P, E, tile_hist, rank);
     bucket_scan_kernel<<<1, 1024, 0, s>>>(n_tiles, E, P, tile_hist, r);
-    bucket_scatter_kernel<<<(P + 255) / 256, 256, 0, s>>>(r.idx, P, E, tile_hist, rank, r.pair);
+    bucket_scatter_kernel<<<(P + 255) / 256, 256, 0, s>>>(r.idx, P, E, tile_hist, r.offset, rank, r.pair);
     return hipGetLastError();
 }
 

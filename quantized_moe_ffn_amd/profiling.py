@@ -54,7 +54,7 @@ def _rows(path: str):
 
 def short_name(name: str) -> str:
     """Kernel name without the argument list and namespace."""
-    base = name.split("(")[0].replace("void ", "").strip()
+    base = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
     return base.replace("moe::", "")
 
 
