@@ -327,113 +327,39 @@ __device__ __forceinline__ void load_x_slice(const DecArgs& a, int tok, int clo,
     }
 }
 
-template <int NB, int PASSES, int TT, int V>
-__global__ void __launch_bounds__((K1Shape<NB, PASSES>::THREADS)) dec_gateup_kernel(DecArgs a) {
-    using S = K1Shape<NB, PASSES>;
-    static_assert(S::IN_WAVE || S::UNITS == 1, "rows spanning waves need a single unit");
-    __shared__ DecRoute R;
-    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * TT * S::P * S::GROUPS)];
-    __shared__ int s_tok[kDecMaxT], s_hrow[kDecMaxT], s_nt, s_e;
-
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int f = (wave % S::W) * kWave + lane;
-    const int sl = f % S::SLICES;
-    const int clo = 256 * (sl >> 3) + q4k_slice_col_lo(sl & 7);
-    const int chi = 256 * (sl >> 3) + q4k_slice_col_hi(sl & 7);
-    const int slot = blockIdx.y;
-    const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
-    float4 xl4[TT][4], xh4[TT][4];
-
-    if (TT == 1 && !lead) {
-        // One token: the activations do not depend on the routing, so they are
-        // loaded first; slot s needs only the first s + 1 extraction rounds, and
-        // the shared expert none.
-        load_x_slice<TT>(a, 0, clo, chi, xl4[0], xh4[0]);
-        const bool shared = a.has_shared && slot == a.k;
-        if (!shared && slot >= a.k) return;
-        if (!shared) {
-            if (wave == 0) {
-                const int e = wave_topk_nth<V>(a.logits, a.E, slot);
-                if (lane == 0) s_e = e;
-            }
-            __syncthreads();
-        }
-        const int e = shared ? 0 : s_e;
-        int hrow[TT];
-#pragma unroll
-        for (int t = 0; t < TT; ++t) hrow[t] = shared ? a.k : slot;
-        dec_gateup_body<NB, PASSES, TT>(a, shared ? a.sgate : a.gate, shared ? a.sup : a.up, e, 1, hrow, xl4, xh4,
-                                        s_part);
-        return;
-    }
-
-    dec_route<V>(a.logits, a.T, a.E, a.k, a.renorm, R);
-    if (lead) {
-        dec_publish(R, a.T, a.E, a.k, a.r);
-        // hand the routing table to the down kernel
-        const int* src = reinterpret_cast<const int*>(&R);
-        for (int i = threadIdx.x; i < (int)(sizeof(DecRoute) / 4); i += blockDim.x) a.route_tab[i] = src[i];
-    }
-
-    // expert slot of this workgroup
-    const bool shared = a.has_shared && slot == a.T * a.k;
-    if (!shared && slot >= R.n_uniq) return;
-    const int e = shared ? 0 : R.uniq[slot];
-    if (threadIdx.x == 0) {
-        int nt = 0;
-        if (shared) {
-            for (int t = 0; t < a.T; ++t) {
-                s_tok[nt] = t;
-                s_hrow[nt] = a.T * a.k + t;
-                ++nt;
-            }
-        } else {
-            for (int q = R.uoff[slot]; q < R.uoff[slot + 1]; ++q) {
-                s_tok[nt] = R.pair[q] / a.k;
-                s_hrow[nt] = R.pair[q];
-                ++nt;
-            }
-        }
-        s_nt = nt;
-    }
-    __syncthreads();
-    const int nt = s_nt;
-#pragma unroll
-    for (int t = 0; t < TT; ++t)   // unconditional (clamped) loads: all in flight together
-        load_x_slice<TT>(a, s_tok[t < nt ? t : nt - 1], clo, chi, xl4[t], xh4[t]);
-    int hrows[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) hrows[t] = s_hrow[t < nt ? t : nt - 1];
-    dec_gateup_body<NB, PASSES, TT>(a, shared ? a.sgate : a.gate, shared ? a.sup : a.up, e, nt, hrows, xl4, xh4,
-                                    s_part);
-}
-
 // ---------------------------------------------------------------------------
-// K1 for one token: workgroup (tile, group g) owns a tile of rows of gate and
-// up for the expert slots j = g, g + G, g + 2G, ... (and the shared expert in
-// the last group).  Every wave runs the extraction itself and issues the loads
-// of slot j right after round j, so the weight traffic of the early slots
-// overlaps the remaining rounds; the dot products then consume the slots in
-// issue order while later loads are still in flight.  Group y == G is one
-// extra workgroup that publishes the routing (and the table for K2).
+// K1: workgroup (tile of rows, group y).  Group y = t*Gk + q (y < T*Gk) owns
+// the slots of token t with ranks q, q + Gk, q + 2Gk, ... (at most four): every
+// wave runs the token's top-k extraction itself and issues the loads of a slot
+// right after the round that names its expert, so the weight traffic of the
+// early slots overlaps the remaining rounds; the dot products then consume the
+// slots in issue order.  Each (token, slot) pair streams its own expert rows:
+// in a 3-token window nearly all 24 experts are distinct, so sharing loads
+// between tokens would save little.  Group T*Gk (when the layer has one) runs
+// the shared expert for all T tokens against one load of its rows; the last
+// group is one workgroup that publishes the routing (and the table for K2).
 // ---------------------------------------------------------------------------
 constexpr int kT1SlotsPerGroup = 4;
 
-template <int NB, int V>
-__global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_t1_kernel(DecArgs a, int G) {
+template <int NB, int V, int TT>
+__global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_kernel(DecArgs a, int Gk) {
     using S = K1Shape<NB, 1>;
     constexpr int SM = kT1SlotsPerGroup;
-    const int g = blockIdx.y;
-    if (g == G) {
+    static_assert(SM >= TT, "s_part holds SM slots");
+    const int y = blockIdx.y;
+    const int Gr = a.T * Gk;
+    const int y_sh = a.has_shared ? Gr : -1;
+    const int y_pub = Gr + (a.has_shared ? 1 : 0);
+    if (y == y_pub) {
         __shared__ DecRoute R;
         if (blockIdx.x != 0) return;
-        dec_route<V>(a.logits, 1, a.E, a.k, a.renorm, R);
-        dec_publish(R, 1, a.E, a.k, a.r);
+        dec_route<V>(a.logits, a.T, a.E, a.k, a.renorm, R);
+        dec_publish(R, a.T, a.E, a.k, a.r);
         const int* src = reinterpret_cast<const int*>(&R);
         for (int i = threadIdx.x; i < (int)(sizeof(DecRoute) / 4); i += blockDim.x) a.route_tab[i] = src[i];
         return;
     }
-    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * (SM + 1) * S::P * S::GROUPS)];
+    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * SM * S::P * S::GROUPS)];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int unit = wave / S::W;
     const int f = (wave % S::W) * kWave + lane;
@@ -444,33 +370,48 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_t1_kerne
     const int chi = 256 * b + q4k_slice_col_hi(part);
     const int i = blockIdx.x * S::ROWS + unit * S::P + rr;
     const int ic = i < a.I ? i : a.I - 1;   // rows past I load a valid row and are not stored
-    const bool has_sh = a.has_shared && g == G - 1;
 
+    if (y == y_sh) {
+        // the shared expert: one load of its rows for all T tokens
+        float4 xl4[TT][4], xh4[TT][4];
+        int hrows[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const int tc = t < a.T ? t : a.T - 1;
+            load_x_slice<TT>(a, tc, clo, chi, xl4[t], xh4[t]);
+            hrows[t] = a.T * a.k + tc;
+        }
+        dec_gateup_body<NB, 1, TT>(a, a.sgate, a.sup, 0, a.T, hrows, xl4, xh4, s_part);
+        return;
+    }
+
+    const int tok = y / Gk, q = y - tok * Gk;
     // activations and logits first (they do not depend on the routing)
     float4 xl4[1][4], xh4[1][4];
-    load_x0_slice(a, clo, chi, xl4[0], xh4[0]);
+    load_x_slice<1>(a, tok, clo, chi, xl4[0], xh4[0]);
     WaveExtract<V> ex;
-    ex.load(a.logits, a.E);
-    uint4 hg[SM + 1], qg[SM + 1], hu[SM + 1], qu[SM + 1];
-    auto issue = [&](int m, const QMat& Gm, const QMat& Um, int e) {
-        const uint8_t* gr = Gm.data + (int64_t)e * Gm.expert_bytes + (int64_t)ic * Gm.row_bytes + (int64_t)b * 144;
-        const uint8_t* ur = Um.data + (int64_t)e * Um.expert_bytes + (int64_t)ic * Um.row_bytes + (int64_t)b * 144;
+    ex.load(a.logits + (int64_t)tok * a.E, a.E);
+    uint4 hg[SM], qg[SM], hu[SM], qu[SM];
+    auto issue = [&](int m, int e) {
+        const uint8_t* gr = a.gate.data + (int64_t)e * a.gate.expert_bytes + (int64_t)ic * a.gate.row_bytes +
+                            (int64_t)b * 144;
+        const uint8_t* ur =
+            a.up.data + (int64_t)e * a.up.expert_bytes + (int64_t)ic * a.up.row_bytes + (int64_t)b * 144;
         hg[m] = *reinterpret_cast<const uint4*>(gr);
         qg[m] = *reinterpret_cast<const uint4*>(gr + 16 + 16 * part);
         hu[m] = *reinterpret_cast<const uint4*>(ur);
         qu[m] = *reinterpret_cast<const uint4*>(ur + 16 + 16 * part);
     };
-    if (has_sh) issue(SM, a.sgate, a.sup, 0);
     int done = 0, win = 0;
 #pragma unroll
     for (int m = 0; m < SM; ++m) {
-        const int jt = g + m * G;
+        const int jt = q + m * Gk;
         if (jt < a.k) {
             while (done <= jt) {
                 win = ex.next();
                 ++done;
             }
-            issue(m, a.gate, a.up, win);
+            issue(m, win);
         }
     }
 
@@ -484,10 +425,10 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_t1_kerne
         sxh[0] += xh[0][j];
     }
 #pragma unroll
-    for (int m = 0; m <= SM; ++m) {
-        const bool live = (m == SM) ? has_sh : (g + m * G < a.k);
-        if (!live) continue;
-        const int hrow = (m == SM) ? a.k : g + m * G;
+    for (int m = 0; m < SM; ++m) {
+        const int jt = q + m * Gk;
+        if (jt >= a.k) continue;
+        const int hrow = tok * a.k + jt;
         float pg[1], pu[1];
         q4k_slice_dot<1>(hg[m], qg[m], part, 1, xl, xh, sxl, sxh, pg);
         q4k_slice_dot<1>(hu[m], qu[m], part, 1, xl, xh, sxl, sxh, pu);
@@ -508,19 +449,18 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_t1_kerne
     if constexpr (!S::IN_WAVE) {
         __syncthreads();
         // one thread per (slot, row): the row's 16-lane group sums in order
-        for (int job = threadIdx.x; job < (SM + 1) * S::P; job += blockDim.x) {
+        for (int job = threadIdx.x; job < SM * S::P; job += blockDim.x) {
             const int m = job / S::P, r2 = job % S::P;
-            const bool live = (m == SM) ? has_sh : (g + m * G < a.k);
+            const int jt = q + m * Gk;
             const int i2 = blockIdx.x * S::ROWS + r2;
-            if (!live || i2 >= a.I) continue;
+            if (jt >= a.k || i2 >= a.I) continue;
             float gs = 0.f, us = 0.f;
 #pragma unroll
-            for (int q = 0; q < S::GROUPS; ++q) {
-                gs += s_part[((2 * m + 0) * S::P + r2) * S::GROUPS + q];
-                us += s_part[((2 * m + 1) * S::P + r2) * S::GROUPS + q];
+            for (int g2 = 0; g2 < S::GROUPS; ++g2) {
+                gs += s_part[((2 * m + 0) * S::P + r2) * S::GROUPS + g2];
+                us += s_part[((2 * m + 1) * S::P + r2) * S::GROUPS + g2];
             }
-            const int hrow = (m == SM) ? a.k : g + m * G;
-            a.h[(int64_t)hrow * a.I + i2] = silu_f32(gs) * us;
+            a.h[(int64_t)(tok * a.k + jt) * a.I + i2] = silu_f32(gs) * us;
         }
     }
 }
@@ -528,23 +468,20 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_t1_kerne
 // ---------------------------------------------------------------------------
 // K2: down + combine.  A "slice" of a down row is 16 quant bytes of a Q4_K
 // super-block (32 weights) or one 34-byte Q8_0 block (32 weights); NS slices
-// per row, 64/NS rows per wave pass, PASSES passes per workgroup.  Every wave
-// covers all the workgroup's rows for up to SMAX expert slots at a time, with
-// every weight and activation load of those slots in flight together.
+// per row, 64/NS rows per wave pass, kK2Passes passes per workgroup.  Slots
+// are the (token, rank) pairs p = t*k + j (expert sel[p], h row p) and, with a
+// shared expert, one slot per token t (h row T*k + t).  Each wave takes SM
+// slots at a time with all their weight and activation loads in flight
+// together (the launcher uses SM = 1); results go to LDS and the combine is
+// formed in slot order.
 // ---------------------------------------------------------------------------
 constexpr int kK2Passes = 2;
+constexpr int kK2MaxThreads = 1024;
 
-template <int TT>
-struct K2Slots {
-    static constexpr int value = 1;                      // expert slots per wave in flight
-    static constexpr int max_threads = TT == 1 ? 1024 : 512;   // register budget
-};
-
-template <int QD, int NS, int TT, int V>
-__global__ void __launch_bounds__(K2Slots<TT>::max_threads) dec_down_kernel(DecArgs a) {
+template <int QD, int NS, int SM, int V>
+__global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
     constexpr int RP = kWave / NS;              // rows per wave pass
     constexpr int RO = RP * kK2Passes;          // output rows of the workgroup
-    constexpr int SM = K2Slots<TT>::value;
     __shared__ DecRoute R;
     __shared__ float s_y[(kDecMaxPairs + kDecMaxT) * RO];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -552,16 +489,12 @@ __global__ void __launch_bounds__(K2Slots<TT>::max_threads) dec_down_kernel(DecA
     const int T = a.T, k = a.k, P = T * k;
     const int o0 = blockIdx.x * RO;
 
-    {   // the routing table written by the gate/up kernel's workgroup 0
+    {   // the routing table written by the gate/up kernel's last workgroup
         int* dst = reinterpret_cast<int*>(&R);
         for (int i = threadIdx.x; i < (int)(sizeof(DecRoute) / 4); i += blockDim.x) dst[i] = a.route_tab[i];
     }
     __syncthreads();
-    if (R.n_uniq < 0 || R.n_uniq > P) {   // corrupted table: nothing is read through it
-        if (threadIdx.x == 0) raise_error(kErrPairRange);
-        return;
-    }
-    const int n_slots = R.n_uniq + (a.has_shared ? 1 : 0);
+    const int n_slots = P + (a.has_shared ? T : 0);
     const int rr = lane / NS, sl = lane % NS;
     int c_lo, c_hi;
     if constexpr (QD == kQ4_K) {
@@ -573,34 +506,28 @@ __global__ void __launch_bounds__(K2Slots<TT>::max_threads) dec_down_kernel(DecA
     }
 
     for (int base = wave; base < n_slots; base += nwaves * SM) {
-        int np[SM], hrow[SM][TT];
-        bool shared[SM], live[SM];
+        int hrow[SM];
+        bool live[SM];
         const uint8_t* Db[SM];
         int64_t rowb[SM];
 #pragma unroll
         for (int m = 0; m < SM; ++m) {
             const int u = base + m * nwaves;
             live[m] = u < n_slots;
-            shared[m] = live[m] && a.has_shared && u == R.n_uniq;
-            int e = (!live[m] || shared[m]) ? 0 : R.uniq[u];
-            if (live[m] && !shared[m]) {
-                const int q0 = R.uoff[u], q1 = R.uoff[u + 1];
-                bool ok = e >= 0 && e < a.E && q0 >= 0 && q1 >= q0 && q1 <= P && q1 - q0 <= TT;
-                for (int q = q0; ok && q < q1; ++q) ok = R.pair[q] >= 0 && R.pair[q] < P;
-                if (!ok) {
+            const bool shared = live[m] && u >= P;
+            int e = 0;
+            if (live[m] && !shared) {
+                e = R.sel[u];
+                if (e < 0 || e >= a.E) {   // corrupted table: nothing is read through it
                     if (lane == 0) raise_error(kErrExpertRange);
                     live[m] = false;
                     e = 0;
                 }
             }
-            const QMat D = shared[m] ? a.sdown : a.down;
+            const QMat D = shared ? a.sdown : a.down;
             Db[m] = D.data + (int64_t)e * D.expert_bytes;
             rowb[m] = D.row_bytes;
-            const int q0 = shared[m] ? 0 : (live[m] ? R.uoff[u] : 0);
-            np[m] = !live[m] ? 0 : (shared[m] ? T : R.uoff[u + 1] - q0);
-#pragma unroll
-            for (int t = 0; t < TT; ++t)
-                hrow[m][t] = t < np[m] ? (shared[m] ? P + t : R.pair[q0 + t]) : 0;
+            hrow[m] = live[m] ? u : 0;   // the h row of slot u is u
         }
         // all weight loads, then the h loads
         uint4 w0[SM][kK2Passes], w1[SM][kK2Passes];
@@ -627,83 +554,55 @@ __global__ void __launch_bounds__(K2Slots<TT>::max_threads) dec_down_kernel(DecA
                 }
             }
         }
-        float4 hl4[SM][TT][4], hh4[SM][TT][4];
+        float4 hl4[SM][4], hh4[SM][4];
 #pragma unroll
         for (int m = 0; m < SM; ++m) {
+            const float4* pl = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m] * a.I + c_lo);
+            const float4* ph = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m] * a.I + c_hi);
 #pragma unroll
-            for (int t = 0; t < TT; ++t) {   // unconditional loads; rows past np read row 0, unused
-                const float4* pl = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m][t] * a.I + c_lo);
-                const float4* ph = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m][t] * a.I + c_hi);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    hl4[m][t][v] = pl[v];
-                    hh4[m][t][v] = ph[v];
-                }
+            for (int v = 0; v < 4; ++v) {
+                hl4[m][v] = pl[v];
+                hh4[m][v] = ph[v];
             }
         }
 #pragma unroll
         for (int m = 0; m < SM; ++m) {
             if (!live[m]) continue;
-            float hl[TT][16], hh[TT][16], shl[TT], shh[TT];
+            float hl[1][16], hh[1][16], shl[1], shh[1];
+            unpack_f4<1>(hl4[m], hl[0]);
+            unpack_f4<1>(hh4[m], hh[0]);
+            shl[0] = shh[0] = 0.f;
 #pragma unroll
-            for (int t = 0; t < TT; ++t) {
-                shl[t] = shh[t] = 0.f;
-                if (t < np[m]) {
-                    unpack_f4<TT>(hl4[m][t], hl[t]);
-                    unpack_f4<TT>(hh4[m][t], hh[t]);
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        shl[t] += hl[t][j];
-                        shh[t] += hh[t][j];
-                    }
-                }
+            for (int j = 0; j < 16; ++j) {
+                shl[0] += hl[0][j];
+                shh[0] += hh[0][j];
             }
 #pragma unroll
             for (int ps = 0; ps < kK2Passes; ++ps) {
-                float acc[TT];
+                float acc[1];
                 if constexpr (QD == kQ4_K) {
-                    q4k_slice_dot<TT>(w0[m][ps], w1[m][ps], sl & 7, np[m], hl, hh, shl, shh, acc);
+                    q4k_slice_dot<1>(w0[m][ps], w1[m][ps], sl & 7, 1, hl, hh, shl, shh, acc);
                 } else {
                     const uint32_t dw[9] = {w0[m][ps].x, w0[m][ps].y, w0[m][ps].z, w0[m][ps].w,
                                             w1[m][ps].x, w1[m][ps].y, w1[m][ps].z, w1[m][ps].w, w2[m][ps]};
                     const bool odd = (sl & 1) != 0;   // 34*sl is 2 mod 4 exactly for odd sl (rows 4-byte aligned)
                     const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
                     const float d = f16_bits_to_f32(odd ? (dw[0] >> 16) : (dw[0] & 0xFFFFu));
-                    float qf[32];
+                    float s0 = 0.f;
 #pragma unroll
                     for (int i4 = 0; i4 < 8; ++i4) {
                         const uint32_t q4 = __builtin_amdgcn_perm(dw[i4 + 1], dw[i4], sel) ^ 0x80808080u;  // q + 128
-                        qf[4 * i4 + 0] = ubyte_f32<0>(q4);
-                        qf[4 * i4 + 1] = ubyte_f32<1>(q4);
-                        qf[4 * i4 + 2] = ubyte_f32<2>(q4);
-                        qf[4 * i4 + 3] = ubyte_f32<3>(q4);
+                        const float* hv = i4 < 4 ? hl[0] : hh[0];
+                        const int j0 = 4 * (i4 & 3);
+                        s0 = fmaf(ubyte_f32<0>(q4), hv[j0 + 0], s0);
+                        s0 = fmaf(ubyte_f32<1>(q4), hv[j0 + 1], s0);
+                        s0 = fmaf(ubyte_f32<2>(q4), hv[j0 + 2], s0);
+                        s0 = fmaf(ubyte_f32<3>(q4), hv[j0 + 3], s0);
                     }
-#pragma unroll
-                    for (int t = 0; t < TT; ++t) {
-                        acc[t] = 0.f;
-                        if (t < np[m]) {
-                            float s0 = 0.f;
-#pragma unroll
-                            for (int j = 0; j < 16; ++j) {
-                                s0 = fmaf(qf[j], hl[t][j], s0);
-                                s0 = fmaf(qf[16 + j], hh[t][j], s0);
-                            }
-                            acc[t] = d * (s0 - 128.0f * (shl[t] + shh[t]));
-                        }
-                    }
+                    acc[0] = d * (s0 - 128.0f * (shl[0] + shh[0]));
                 }
-#pragma unroll
-                for (int t = 0; t < TT; ++t) acc[t] = segment_sum<NS>(acc[t]);
-                if (sl == NS - 1) {
-                    const int r = ps * RP + rr;
-#pragma unroll
-                    for (int t = 0; t < TT; ++t) {
-                        if (t < np[m]) {
-                            const int yrow = shared[m] ? (kDecMaxPairs + t) : hrow[m][t];
-                            s_y[yrow * RO + r] = acc[t];
-                        }
-                    }
-                }
+                acc[0] = segment_sum<NS>(acc[0]);
+                if (sl == NS - 1) s_y[hrow[m] * RO + ps * RP + rr] = acc[0];
             }
         }
     }
@@ -719,7 +618,7 @@ __global__ void __launch_bounds__(K2Slots<TT>::max_threads) dec_down_kernel(DecA
             if (a.y_pair) a.y_pair[(int64_t)(t * k + j) * a.H + o] = y;
         }
         if (a.has_shared) {
-            const float ys = s_y[(kDecMaxPairs + t) * RO + r];
+            const float ys = s_y[(P + t) * RO + r];
             acc = fmaf(a.shared_scale ? a.shared_scale[t] : 1.0f, ys, acc);
             if (a.y_shared) a.y_shared[(int64_t)t * a.H + o] = ys;
         }
@@ -732,51 +631,39 @@ __global__ void __launch_bounds__(K2Slots<TT>::max_threads) dec_down_kernel(DecA
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int NB, int PASSES, int V>
-hipError_t launch_k1v(const DecArgs& a, hipStream_t s) {
-    using S = K1Shape<NB, PASSES>;
-    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, a.T * a.k + (a.has_shared ? 1 : 0));
-    if (a.T == 1)
-        dec_gateup_kernel<NB, PASSES, 1, V><<<grid, S::THREADS, 0, s>>>(a);
-    else
-        dec_gateup_kernel<NB, PASSES, kDecMaxT, V><<<grid, S::THREADS, 0, s>>>(a);
+template <int NB, int V, int TT>
+hipError_t launch_k1_pipe(const DecArgs& a, hipStream_t s) {
+    using S = K1Shape<NB, 1>;
+    const int Gk = (a.k + kT1SlotsPerGroup - 1) / kT1SlotsPerGroup;   // groups per token
+    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, a.T * Gk + (a.has_shared ? 1 : 0) + 1);
+    dec_gateup_pipe_kernel<NB, V, TT><<<grid, S::THREADS, 0, s>>>(a, Gk);
     return hipGetLastError();
 }
 
 template <int NB, int V>
-hipError_t launch_k1_t1(const DecArgs& a, hipStream_t s) {
-    using S = K1Shape<NB, 1>;
-    const int G = (a.k + kT1SlotsPerGroup - 1) / kT1SlotsPerGroup;   // groups of at most 4 routed slots
-    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, G + 1);
-    dec_gateup_t1_kernel<NB, V><<<grid, S::THREADS, 0, s>>>(a, G);
-    return hipGetLastError();
+hipError_t launch_k1_v(const DecArgs& a, hipStream_t s) {
+    // the 4-token shared-expert branch costs registers; it runs only when the
+    // layer has a shared expert and more than one token
+    return (a.T == 1 || !a.has_shared) ? launch_k1_pipe<NB, V, 1>(a, s) : launch_k1_pipe<NB, V, kDecMaxT>(a, s);
 }
 
-template <int NB, int PASSES>
+template <int NB>
 hipError_t launch_k1(const DecArgs& a, hipStream_t s) {
     const int vpl = topk_vpl(a.E);
-    if (a.T == 1) {
-        if (vpl == 4) return launch_k1_t1<NB, 4>(a, s);
-        if (vpl == 8) return launch_k1_t1<NB, 8>(a, s);
-        return launch_k1_t1<NB, 16>(a, s);
-    }
-    if (vpl == 4) return launch_k1v<NB, PASSES, 4>(a, s);
-    if (vpl == 8) return launch_k1v<NB, PASSES, 8>(a, s);
-    return launch_k1v<NB, PASSES, 16>(a, s);
+    if (vpl == 4) return launch_k1_v<NB, 4>(a, s);
+    if (vpl == 8) return launch_k1_v<NB, 8>(a, s);
+    return launch_k1_v<NB, 16>(a, s);
 }
 
 template <int QD, int NS, int V>
 hipError_t launch_k2v(const DecArgs& a, hipStream_t s) {
     constexpr int RO = (kWave / NS) * kK2Passes;
-    const int slots = a.T * a.k + (a.has_shared ? 1 : 0);
-    const int sm = a.T == 1 ? K2Slots<1>::value : K2Slots<kDecMaxT>::value;
-    const int max_waves = (a.T == 1 ? K2Slots<1>::max_threads : K2Slots<kDecMaxT>::max_threads) / kWave;
-    int waves = (slots + sm - 1) / sm;
-    waves = waves < 4 ? 4 : (waves > max_waves ? max_waves : waves);
-    if (a.T == 1)
-        dec_down_kernel<QD, NS, 1, V><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
-    else
-        dec_down_kernel<QD, NS, kDecMaxT, V><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
+    const int slots = a.T * a.k + (a.has_shared ? a.T : 0);
+    const int max_waves = kK2MaxThreads / kWave;
+    // one slot per wave in flight (more spill at this workgroup size); slots
+    // beyond 16 take a second round on some waves
+    const int waves = slots < 4 ? 4 : (slots > max_waves ? max_waves : slots);
+    dec_down_kernel<QD, NS, 1, V><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -805,11 +692,11 @@ bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd) {
 hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s) {
     hipError_t e;
     switch (a.H / 256) {
-        case 1: e = launch_k1<1, 1>(a, s); break;
-        case 2: e = launch_k1<2, 1>(a, s); break;
-        case 4: e = launch_k1<4, 2>(a, s); break;
-        case 8: e = launch_k1<8, 2>(a, s); break;
-        default: e = launch_k1<10, 2>(a, s); break;
+        case 1: e = launch_k1<1>(a, s); break;
+        case 2: e = launch_k1<2>(a, s); break;
+        case 4: e = launch_k1<4>(a, s); break;
+        case 8: e = launch_k1<8>(a, s); break;
+        default: e = launch_k1<10>(a, s); break;
     }
     if (e != hipSuccess) return e;
     const int ns = (a.down.qtype == kQ4_K) ? 8 * (a.I / 256) : a.I / 32;

@@ -159,56 +159,6 @@ struct WaveExtract {
     }
 };
 
-// The expert of slot n (0-based) of one token: n + 1 rounds of the extraction
-// above, without the weights.  Uniform result.
-template <int V>
-__device__ __forceinline__ int wave_topk_nth(const float* __restrict__ lg, int E, int n) {
-    const int lane = threadIdx.x & (kWave - 1);
-    uint32_t key[V];
-    float xv[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-        const int e = lane + kWave * v;
-        xv[v] = lg[e < E ? e : E - 1];
-    }
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-        const int e = lane + kWave * v;
-        key[v] = e < E ? max(order_key(xv[v]), 1u) : 0u;
-    }
-    int win = 0;
-    for (int j = 0; j <= n; ++j) {
-        uint32_t b = key[0];
-#pragma unroll
-        for (int v = 1; v < V; ++v) b = max(b, key[v]);
-        const uint32_t M = wave_max_u32(b);
-        int wv = V, wl = 0;
-        const uint64_t lanes = __ballot(b == M);
-        if (__popcll(lanes) == 1) {
-            wl = (int)__builtin_ctzll(lanes);
-            int vl = V;
-#pragma unroll
-            for (int v = V - 1; v >= 0; --v)
-                if (key[v] == M) vl = v;
-            wv = __builtin_amdgcn_readlane(vl, wl);
-        } else {
-#pragma unroll
-            for (int v = V - 1; v >= 0; --v) {
-                const uint64_t msk = __ballot(key[v] == M);
-                if (msk != 0ull) {
-                    wv = v;
-                    wl = (int)__builtin_ctzll(msk);
-                }
-            }
-        }
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-            if (v == wv && lane == wl) key[v] = 0u;
-        win = wl + kWave * wv;
-    }
-    return win;
-}
-
 // Values per lane for E experts (the kernels are instantiated for 4, 8, 16).
 inline int topk_vpl(int E) { return E <= 256 ? 4 : (E <= 512 ? 8 : 16); }
 
