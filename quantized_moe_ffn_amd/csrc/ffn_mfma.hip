@@ -364,25 +364,16 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
             }
         }
     };
-    // three register buffers rotate through a 3x unrolled loop (no copies of
-    // registers that loads in flight still write)
-    BlockRegs b0, b1, b2;
+    // two register buffers alternate through a 2x unrolled loop (no copies of
+    // registers that loads in flight still write); steps is even, so the body
+    // has no conditional steps and the compiler can interleave them
+    BlockRegs b0, b1;
     load_block(blk_ptr(0), h, b0);
-    load_block(blk_ptr(min(1, steps - 1)), h, b1);
-    for (int s = 0; s < steps; s += 3) {
-        load_block(blk_ptr(min(s + 2, steps - 1)), h, b2);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < steps; s += 2) {
+        load_block(blk_ptr(s + 1), h, b1);
         step(b0, s);
-        if (s + 1 < steps) {
-            load_block(blk_ptr(min(s + 3, steps - 1)), h, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            step(b1, s + 1);
-        }
-        if (s + 2 < steps) {
-            load_block(blk_ptr(min(s + 4, steps - 1)), h, b1);
-            __builtin_amdgcn_sched_barrier(0);
-            step(b2, s + 2);
-        }
+        load_block(blk_ptr(min(s + 2, steps - 1)), h, b0);
+        step(b1, s + 1);
     }
 
     // h = silu(g) * u, then per-token amax over the 256 rows of this block
@@ -513,24 +504,16 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
             }
         }
     };
-    BlockRegs b0, b1, b2;
+    BlockRegs b0, b1;
     load_block(blk_ptr(0), h, b0);
-    load_block(blk_ptr(min(1, steps - 1)), h, b1);
-    for (int s = 0; s < steps; s += 3) {
-        load_block(blk_ptr(min(s + 2, steps - 1)), h, b2);
-        __builtin_amdgcn_sched_barrier(0);
+    int s = 0;
+    for (; s + 1 < steps; s += 2) {
+        load_block(blk_ptr(s + 1), h, b1);
         step(b0, s);
-        if (s + 1 < steps) {
-            load_block(blk_ptr(min(s + 3, steps - 1)), h, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            step(b1, s + 1);
-        }
-        if (s + 2 < steps) {
-            load_block(blk_ptr(min(s + 4, steps - 1)), h, b1);
-            __builtin_amdgcn_sched_barrier(0);
-            step(b2, s + 2);
-        }
+        load_block(blk_ptr(min(s + 2, steps - 1)), h, b0);
+        step(b1, s + 1);
     }
+    if (s < steps) step(b0, s);
 }
 
 // xs[t] = the bf16 hi parts of v_c = (sum_{l<32} xq[t][32c + l]) * xd[t][c/8]
