@@ -44,7 +44,7 @@ def traffic_from_profiles(config: str):
     except (ValueError, OSError):
         return None
     from quantized_moe_ffn_amd.profiling import kernel_source_hash
-    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_hash") != kernel_source_hash(config):
         return None
     return rec.get("bytes_per_launch")
 
@@ -233,11 +233,30 @@ def cpu_baseline(w, stack, inputs, bufs, flags, k, budget_s):
     tok_sample = np.arange(T) if T <= 64 else np.linspace(0, T - 1, 16).round().astype(np.int64)
     mode = 1 if w.int8_path else 0
     spent, tokens_done, layers_done, errs = 0.0, 0, 0, []
+    qt = (w.qt_gate, w.qt_up, w.qt_down)
+    cache = []          # host copies of the first items, reused once every item has been seen
+    kCache = 32
+
+    def run_oracle(lg, x, hb, remap, shared):
+        idx, wts = oracle.route_topk(lg, k)
+        oracle.bucket(idx, w.n_experts)
+        pe = remap[idx.reshape(-1)]
+        bad = bool(np.any(pe < 0))      # the oracle chose an expert the GPU did not: parity failure
+        pe = np.maximum(pe, 0)
+        pt = np.repeat(np.arange(len(tok_sample)), k)
+        y = oracle.expert_ffn(hb["gate"], hb["up"], hb["down"], qt, w.hidden, w.inter, pe, pt, x, mode)
+        ys = None
+        if shared is not None:
+            ys = oracle.expert_ffn(*shared, qt, w.hidden, w.inter, np.zeros(len(tok_sample), np.int32),
+                                   np.arange(len(tok_sample), dtype=np.int32), x, mode)
+        return oracle.combine(y, wts, ys), bad
+
+    # first pass: every (replay, layer) input once, checked against the GPU output
     items = [(r, l) for r in range(len(inputs)) for l in range(len(stack))]
     for r, l in items:
-        dl = stack[l]
         if spent >= budget_s:
             break
+        dl = stack[l]
         lg_t, x_t = inputs[r][l]
         qm.forward(dl.layer, lg_t, x_t, k, bufs, flags=flags)
         torch.cuda.synchronize()
@@ -251,30 +270,28 @@ def cpu_baseline(w, stack, inputs, bufs, flags, k, budget_s):
         hb = {n: dl.banks[n].index_select(0, sel).cpu().numpy() for n in ("gate", "up", "down")}
         remap = np.full(w.n_experts, -1, np.int64)
         remap[uniq] = np.arange(len(uniq))
-        shared = None
-        if w.shared:
-            shared = tuple(dl.banks[n].cpu().numpy() for n in ("sh_gate", "sh_up", "sh_down"))
-        qt = (w.qt_gate, w.qt_up, w.qt_down)
+        shared = tuple(dl.banks[n].cpu().numpy() for n in ("sh_gate", "sh_up", "sh_down")) if w.shared else None
         t0 = time.perf_counter()
-        idx, wts = oracle.route_topk(lg, k)
-        oracle.bucket(idx, w.n_experts)
-        pe = remap[idx.reshape(-1)]
-        if np.any(pe < 0):      # the oracle chose an expert the GPU did not: parity failure
-            pe = np.maximum(pe, 0)
-            errs.append(float("inf"))
-        pt = np.repeat(np.arange(len(tok_sample)), k)
-        y = oracle.expert_ffn(hb["gate"], hb["up"], hb["down"], qt, w.hidden, w.inter, pe, pt, x, mode)
-        ys = None
-        if shared is not None:
-            ys = oracle.expert_ffn(*shared, qt, w.hidden, w.inter, np.zeros(len(tok_sample), np.int32),
-                                   np.arange(len(tok_sample), dtype=np.int32), x, mode)
-        out = oracle.combine(y, wts, ys)
+        out, bad = run_oracle(lg, x, hb, remap, shared)
         spent += time.perf_counter() - t0
         tokens_done += len(tok_sample)
         layers_done += 1
         den = np.abs(out).max(axis=1)
-        errs.append(float((np.abs(gpu_out - out).max(axis=1) / den).max()))
+        errs.append(float("inf") if bad else float((np.abs(gpu_out - out).max(axis=1) / den).max()))
+        if len(cache) < kCache:
+            cache.append((lg, x, hb, remap, shared))
         if layers_done % 20 == 0:
+            log("[bench] cpu oracle: %d layer calls done, %.1f s spent" % (layers_done, spent))
+    # then the cached items again until the budget is spent (no GPU work, no copies)
+    i = 0
+    while spent < budget_s and cache:
+        t0 = time.perf_counter()
+        run_oracle(*cache[i % len(cache)])
+        spent += time.perf_counter() - t0
+        tokens_done += len(tok_sample)
+        layers_done += 1
+        i += 1
+        if layers_done % 500 == 0:
             log("[bench] cpu oracle: %d layer calls done, %.1f s spent" % (layers_done, spent))
     cpu = {"value": round(tokens_done / spent, 3), "unit": "layer-tokens/s", "cores": oracle.threads(),
            "kind": "oracle",

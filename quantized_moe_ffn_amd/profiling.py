@@ -8,8 +8,8 @@ Two uses:
     then WRITE_SIZE, KiB per dispatch) over the library's kernels, each scaled
     by what the same counter reads for a device-to-device copy of known size.
     The record goes into ``profiles/traffic.json`` keyed by the workload name and
-    tagged with a hash of the kernel sources, so a reader can tell when the
-    kernels have changed since the counters were taken.
+    tagged with a hash of the sources of that workload's kernels, so a reader
+    can tell when they have changed since the counters were taken.
 
 Only reads CSV files; runs nothing on the GPU.
 """
@@ -29,14 +29,27 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 
-def kernel_source_hash() -> str:
-    """Hash of every .hip/.h file of the library (names and bytes)."""
+# Sources of each path's kernels (plus the API layer that launches them).
+_COMMON = ("common.h", "kernels.h", "libmoe.hip", "moe_api.hip", "route.hip")
+_DECODE = _COMMON + ("qblock.h", "decode_fused.hip")
+_INT8 = _COMMON + ("quant.hip", "ffn_mfma.hip", "ffn_int8.hip", "ffn_decode.hip")
+
+
+def kernel_files(workload: str | None = None):
+    """The library sources a workload's kernels are built from (all sources when None)."""
+    if workload is None:
+        return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    from quantized_moe_ffn_amd import synth
+    return sorted(_INT8 if synth.WORKLOADS[workload].int8_path else _DECODE)
+
+
+def kernel_source_hash(workload: str | None = None) -> str:
+    """Hash of the named sources (names and bytes) of a workload's kernel path."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    for f in kernel_files(workload):
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -129,7 +142,8 @@ def cmd_traffic(a) -> int:
         kernels[name] = {"fetch_bytes": round(f), "write_bytes": round(w),
                          "dispatches": max(fetch.get(name, (0, 0))[1], write.get(name, (0, 0))[1])}
         total += f + w
-    rec = {"kernel_hash": kernel_source_hash(), "bytes_per_launch": round(total),
+    rec = {"kernel_hash": kernel_source_hash(a.workload), "kernel_files": kernel_files(a.workload),
+           "bytes_per_launch": round(total),
            "fetch_scale_bytes_per_unit": round(fs, 3), "write_scale_bytes_per_unit": round(ws, 3),
            "copy_bytes": a.copy_bytes, "kernels": kernels}
     data = {}
