@@ -31,6 +31,8 @@
 // global memory into registers one 256-block ahead of use.  Work items are
 // laid out (expert, token tile, row block) and dealt to the 8 XCDs in
 // contiguous ranges, so workgroups that share an expert's weights share an L2.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -49,6 +51,7 @@ constexpr int kMWaves = 8;
 constexpr int kMThreads = kMWaves * kWave;
 constexpr int kLdsPad = 16;  // bytes after each LDS row: consecutive rows start 4 banks apart
 constexpr int kXcds = 8;
+constexpr int kHStride = 256 + 4;  // LDS row stride (floats) of the gate/up epilogue's h tile
 
 __device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b) {
     const v2u16 x = __builtin_bit_cast(v2u16, a), y = __builtin_bit_cast(v2u16, b);
@@ -314,9 +317,6 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int s_src[MT], s_out[MT];
-    __shared__ float s_red[kMWaves * MT];
-    __shared__ __attribute__((aligned(16))) float s_id[MT];
-    __shared__ float s_d[MT];
 
     const int H = a.H, I = a.I, NB = I / 256, nsb = H / 256;
     int u, nb;
@@ -376,65 +376,75 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
         step(b1, s + 1);
     }
 
-    // h = silu(g) * u, then per-token amax over the 256 rows of this block
-    float hv[MTILES][16];
-#pragma unroll
-    for (int mt = 0; mt < MTILES; ++mt) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float hh = silu_f32(g_out[mt][v]) * acc[mt][v];
-            hv[mt][v] = hh;
-            float am = isfinite(hh) ? fabsf(hh) : INFINITY;
-            am = half32_max(am);
-            if (n == 0) s_red[wave * MT + c_row(mt, v, h)] = am;
-        }
-    }
+    // h = silu(g) * u goes through LDS (the tile is no longer needed), so that
+    // each thread then owns one (token, 32-row block): the token's amax over
+    // the 256 rows is a reduction over 8 neighbouring lanes, and the codes of
+    // a block and their sum stay in one thread
     __syncthreads();
-    if (threadIdx.x < MT) {
-        const int m = threadIdx.x;
+    float* s_h = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int mt = 0; mt < MTILES; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            s_h[c_row(mt, v, h) * kHStride + wave * 32 + n] = silu_f32(g_out[mt][v]) * acc[mt][v];
+    __syncthreads();
+    const int m = threadIdx.x >> 3, c32 = threadIdx.x & 7;
+    if (m < MT) {   // whole waves past the tile's rows stay idle
+        float hv[32];
+        const float4* src = reinterpret_cast<const float4*>(s_h + m * kHStride + c32 * 32);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float4 f4 = src[j];
+            hv[4 * j] = f4.x;
+            hv[4 * j + 1] = f4.y;
+            hv[4 * j + 2] = f4.z;
+            hv[4 * j + 3] = f4.w;
+        }
+        bool fin = true;
         float am = 0.0f;
-        for (int w = 0; w < kMWaves; ++w) am = fmaxf(am, s_red[w * MT + m]);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            fin = fin && isfinite(hv[j]);
+            am = fmaxf(am, fabsf(hv[j]));
+        }
+        am = fin ? am : INFINITY;
+        am = fmaxf(am, dpp_f<0xB1>(am));    // the token's 8 threads: quad swaps,
+        am = fmaxf(am, dpp_f<0x4E>(am));
+        am = fmaxf(am, dpp_f<0x141>(am));   // then the half-row mirror
+        const int orow = s_out[m];
         float id = 0.0f, d = 0.0f;
         if (!(am < INFINITY)) {
-            if (s_out[m] >= 0) raise_error(kErrActNonFinite);
+            if (orow >= 0 && c32 == 0) raise_error(kErrActNonFinite);
         } else if (am > 0.0f) {
             id = __fdiv_rn(127.0f, am);
             d = __fdiv_rn(am, 127.0f);
         }
-        s_id[m] = id;
-        s_d[m] = d;
-        if (s_out[m] >= 0) a.hd[(uint32_t)(s_out[m] * NB + nb)] = d;
-    }
-    __syncthreads();
-    const int I32 = I / 32;
+        uint32_t packed[8];
+        int qsum = 0;
 #pragma unroll
-    for (int mt = 0; mt < MTILES; ++mt) {
+        for (int j = 0; j < 8; ++j) {
+            uint32_t w = 0;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 i4 = *reinterpret_cast<const float4*>(s_id + mt * 32 + 8 * g + 4 * h);
-            const float iv[4] = {i4.x, i4.y, i4.z, i4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int v = 4 * g + r;
-                const int m = c_row(mt, v, h);
+            for (int bb = 0; bb < 4; ++bb) {
                 int q = 0;
-                if (iv[r] != 0.0f) {
-                    float qf = rintf(__fmul_rn(hv[mt][v], iv[r]));
-                    qf = fminf(fmaxf(qf, -127.0f), 127.0f);
-                    q = (int)qf;
-                }
-                const int orow = s_out[m];
-                if (orow >= 0) a.hq[(uint32_t)(orow * I + i)] = (int8_t)q;
-                const int qs = half32_sum(q);
-                if (n == 0 && orow >= 0) {
-                    const float sv = (float)qs * s_d[m];
-                    const __bf16 sh = (__bf16)sv;
-                    const __bf16 sl = (__bf16)(sv - (float)sh);
-                    const uint32_t o0 = (uint32_t)(orow * (2 * I32) + nb * 8 + wave);
-                    a.hs[o0] = __builtin_bit_cast(uint16_t, sh);
-                    a.hs[o0 + I32] = __builtin_bit_cast(uint16_t, sl);
-                }
+                if (id != 0.0f) q = (int)fminf(fmaxf(rintf(__fmul_rn(hv[4 * j + bb], id)), -127.0f), 127.0f);
+                qsum += q;
+                w |= ((uint32_t)q & 0xFFu) << (8 * bb);
             }
+            packed[j] = w;
+        }
+        if (orow >= 0) {
+            uint4* dst = reinterpret_cast<uint4*>(a.hq + (uint32_t)(orow * I + nb * 256 + c32 * 32));
+            dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+            dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+            const int I32 = I / 32;
+            const float sv = (float)qsum * d;
+            const __bf16 sh = (__bf16)sv;
+            const __bf16 sl = (__bf16)(sv - (float)sh);
+            const uint32_t o0 = (uint32_t)(orow * (2 * I32) + nb * 8 + c32);
+            a.hs[o0] = __builtin_bit_cast(uint16_t, sh);
+            a.hs[o0 + I32] = __builtin_bit_cast(uint16_t, sl);
+            if (c32 == 0) a.hd[(uint32_t)(orow * NB + nb)] = d;
         }
     }
 }
@@ -592,7 +602,8 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     const int64_t n_sums = (int64_t)a.T * (a.H / 32);
     act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, a.xd, n_sums, a.H, a.xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    gateup_mfma_kernel<MTILES><<<grid_for(maxt * (a.I / 256)), kMThreads, tile_lds_bytes<MTILES>(a.H), s>>>(a);
+    const size_t lds_gu = std::max(tile_lds_bytes<MTILES>(a.H), (size_t)MT * kHStride * sizeof(float));
+    gateup_mfma_kernel<MTILES><<<grid_for(maxt * (a.I / 256)), kMThreads, lds_gu, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int nb_down = (a.H / 256 + kDownRounds - 1) / kDownRounds;
     down_mfma_kernel<MTILES><<<grid_for(maxt * nb_down), kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(a);
