@@ -12,12 +12,14 @@
 // enter the int8 MFMA as the bytes q*sl and q*sh (both <= 105): two MFMAs per
 // 32-deep K chunk, accumulated exactly in int32 over a 256-wide block, then
 // acc_l + 8*acc_h is scaled once per block by d*xd in fp32.  The block's min
-// term is one K = 16 bf16 MFMA pair: the lane halves carry the same eight
-// sub-blocks, as the hi and lo bf16 parts of X_j*xd (precomputed per token
-// and kept beside the tile), against the hi and lo parts of -dmin*m_j; the
-// four cross products keep the term to about 2^-16 relative.
+// term is one K = 16 fp16 MFMA pair: the lane halves carry the same eight
+// sub-blocks, as the hi and lo fp16 parts of X_j*xd/s (X_j the exact per-32
+// code sums; s a power of two >= the row's largest xd, so the operand stays
+// below 4064), against the hi and lo parts of -dmin*m_j (exact); the four
+// cross products keep the term to about 2^-22 relative.  1/s is folded into
+// the row's block scales, and each finished row is multiplied by s.
 //
-// MFMA layouts (v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_bf16): lane l
+// MFMA layouts (v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_f16): lane l
 // supplies row l%32 of A (tokens) and column l%32 of B (weight rows); both use
 // the same K positions for the same lane half and register byte; the result
 // C[m][n] sits in lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
@@ -45,7 +47,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kMWaves = 8;
 constexpr int kMThreads = kMWaves * kWave;
@@ -96,8 +98,9 @@ __device__ __forceinline__ int c_row(int mt, int v, int h) { return mt * 32 + 8 
 // The A side of a tile in LDS.
 struct TileLds {
     const int8_t* a;     // [MT][lda] int8 codes
-    const float* xd;     // [nsb][MT] per-256 scales
-    const uint16_t* xs;  // [MT][xs_ld] bf16: hi parts of the K/32 scaled sums, then the lo parts
+    const float* xd;     // [nsb][MT] per-256 scales divided by the row's s
+    const uint16_t* xs;  // [MT][xs_ld] fp16: hi parts of the K/32 values X*xd/s, then the lo parts
+    const float* s;      // [MT] the rows' power-of-two s
     int lda, xs_ld, k32;
 };
 
@@ -167,25 +170,25 @@ __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const Tile
         }
     }
 
-    // min term: out += sum_j (-dmin m_j) (X_j xd), hi/lo bf16 pairs; lane half
-    // 0 carries the hi parts of X_j xd, half 1 the lo parts
+    // min term: out += sum_j (-dmin m_j) (X_j xd / s), hi/lo fp16 pairs; lane
+    // half 0 carries the hi parts of X_j xd / s, half 1 the lo parts
     {
         const float dmin = q4k_dmin(hd);
-        v8bf Bmh, Bml;
+        v8h Bmh, Bml;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t mb = j < 4 ? mn_lo : mn_hi;
             const float bv = -(dmin * (float)((mb >> (8 * (j & 3))) & 0xFFu));  // exact: 11 x 6 bits
-            const __bf16 bh = (__bf16)bv;
+            const _Float16 bh = (_Float16)bv;
             Bmh[j] = bh;
-            Bml[j] = (__bf16)(bv - (float)bh);
+            Bml[j] = (_Float16)(bv - (float)bh);
         }
 #pragma unroll
         for (int mt = 0; mt < MTILES; ++mt) {
-            const v8bf Am =
-                *reinterpret_cast<const v8bf*>(T.xs + (mt * 32 + n) * T.xs_ld + h * T.k32 + 8 * b);
-            out[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Am, Bmh, out[mt], 0, 0, 0);
-            out[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Am, Bml, out[mt], 0, 0, 0);
+            const v8h Am =
+                *reinterpret_cast<const v8h*>(T.xs + (mt * 32 + n) * T.xs_ld + h * T.k32 + 8 * b);
+            out[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Am, Bmh, out[mt], 0, 0, 0);
+            out[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Am, Bml, out[mt], 0, 0, 0);
         }
     }
 
@@ -207,12 +210,38 @@ __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const Tile
     }
 }
 
+// out[mt][v] *= s of its row (C layout), turning the K loop's rows back to scale.
+template <int MTILES>
+__device__ __forceinline__ void apply_row_scale(const TileLds& T, v16f (&out)[MTILES]) {
+    const int h = (threadIdx.x & (kWave - 1)) >> 5;
+#pragma unroll
+    for (int mt = 0; mt < MTILES; ++mt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 s4 = *reinterpret_cast<const float4*>(T.s + mt * 32 + 8 * g + 4 * h);
+            out[mt][4 * g + 0] *= s4.x;
+            out[mt][4 * g + 1] *= s4.y;
+            out[mt][4 * g + 2] *= s4.z;
+            out[mt][4 * g + 3] *= s4.w;
+        }
+    }
+}
+
+// Smallest power of two >= x (x finite, > 0); 1 otherwise.
+__device__ __forceinline__ float pow2_ceil(float x) {
+    if (!(x > 0.0f) || !(x < INFINITY)) return 1.0f;
+    const uint32_t b = __float_as_uint(x);
+    if ((b & 0x7FFFFFu) == 0 && (b >> 23) != 0) return x;
+    const uint32_t e = (b >> 23) + 1;  // subnormal x: e = 1, i.e. 2^-126
+    return e >= 255 ? 1.0f : __uint_as_float(e << 23);
+}
+
 // Loads the A side of tile: rows src_row[m] (zeros when < 0) of an int8 matrix
 // with K columns, their per-256 scales, and their per-32 code sums.
 template <int MTILES>
 __device__ __forceinline__ void load_tile(const int8_t* __restrict__ q, const float* __restrict__ qd,
-                                          const uint16_t* __restrict__ qs, int K, const int* s_src, int8_t* lds_a,
-                                          int lda, float* xd_s, uint16_t* xs_s, int xs_ld) {
+                                          const int16_t* __restrict__ qs, int K, const int* s_src, int8_t* lds_a,
+                                          int lda, float* xd_s, uint16_t* xs_s, int xs_ld, float* s_sc) {
     constexpr int MT = 32 * MTILES;
     constexpr int kBatch = 8;
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -239,26 +268,32 @@ __device__ __forceinline__ void load_tile(const int8_t* __restrict__ q, const fl
             }
         }
     }
-    // per-256 scales: [b][m]
+    // per-256 scales [b][m], then each row's s and the scales divided by it
     const int nsb = K / 256;
     for (int idx = tid; idx < MT * nsb; idx += nthr) {
         const int b = idx / MT, m = idx % MT;
         const int src = s_src[m];
         xd_s[b * MT + m] = src >= 0 ? qd[(int64_t)src * nsb + b] : 0.0f;
     }
-    // per-32 sums, bf16 hi then lo: 2*K/32 values per row, 8 per uint4
-    {
-        const int per_row = (2 * (K / 32)) / 8;
-        const int rows_per_pass = nthr / per_row;
-        const int c = tid % per_row, m0 = tid / per_row;
-        if (m0 < rows_per_pass) {
-            for (int m = m0; m < MT; m += rows_per_pass) {
-                const int src = s_src[m];
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (src >= 0) v = *reinterpret_cast<const uint4*>(qs + (int64_t)src * (2 * (K / 32)) + 8 * c);
-                *reinterpret_cast<uint4*>(xs_s + m * xs_ld + 8 * c) = v;
-            }
-        }
+    __syncthreads();
+    if (tid < MT) {
+        float mx = 0.0f;
+        for (int b = 0; b < nsb; ++b) mx = fmaxf(mx, xd_s[b * MT + tid]);
+        const float sv = pow2_ceil(mx), inv = 1.0f / sv;  // powers of two: exact
+        s_sc[tid] = sv;
+        for (int b = 0; b < nsb; ++b) xd_s[b * MT + tid] *= inv;
+    }
+    __syncthreads();
+    // per-32 values X*xd/s as fp16 hi/lo pairs: [m][0 .. K/32) hi, [m][K/32 .. 2K/32) lo
+    const int k32 = K / 32;
+    for (int idx = tid; idx < MT * k32; idx += nthr) {
+        const int m = idx / k32, c = idx - m * k32;
+        const int src = s_src[m];
+        const float xv = src >= 0 ? (float)qs[(int64_t)src * k32 + c] : 0.0f;
+        const float v = xv * xd_s[(c >> 3) * MT + m];
+        const _Float16 vh = (_Float16)v;
+        xs_s[m * xs_ld + c] = __builtin_bit_cast(uint16_t, vh);
+        xs_s[m * xs_ld + k32 + c] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)vh));
     }
 }
 
@@ -303,13 +338,14 @@ __device__ __forceinline__ void tile_rows(const MfmaArgs& a, int e, int m0, bool
 
 // Carves the dynamic LDS into the tile's A side.
 template <int MTILES>
-__device__ __forceinline__ TileLds carve(unsigned char* lds, int K, int8_t*& a, float*& xd, uint16_t*& xs) {
+__device__ __forceinline__ TileLds carve(unsigned char* lds, int K, const float* s_sc, int8_t*& a, float*& xd,
+                                         uint16_t*& xs) {
     constexpr int MT = 32 * MTILES;
     const int lda = K + kLdsPad, xs_ld = 2 * (K / 32) + 8;
     a = reinterpret_cast<int8_t*>(lds);
     xd = reinterpret_cast<float*>(lds + (size_t)MT * lda);
     xs = reinterpret_cast<uint16_t*>(lds + (size_t)MT * lda + (size_t)(K / 256) * MT * sizeof(float));
-    return TileLds{a, xd, xs, lda, xs_ld, K / 32};
+    return TileLds{a, xd, xs, s_sc, lda, xs_ld, K / 32};
 }
 
 template <int MTILES>
@@ -317,6 +353,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int s_src[MT], s_out[MT];
+    __shared__ __attribute__((aligned(16))) float s_sc[MT];
 
     const int H = a.H, I = a.I, NB = I / 256, nsb = H / 256;
     int u, nb;
@@ -329,8 +366,8 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     int8_t* lds_a;
     float* xd_s;
     uint16_t* xs_s;
-    const TileLds T = carve<MTILES>(lds, H, lds_a, xd_s, xs_s);
-    load_tile<MTILES>(a.xq, a.xd, a.xs, H, s_src, lds_a, T.lda, xd_s, xs_s, T.xs_ld);
+    const TileLds T = carve<MTILES>(lds, H, s_sc, lds_a, xd_s, xs_s);
+    load_tile<MTILES>(a.xq, a.xd, a.xs, H, s_src, lds_a, T.lda, xd_s, xs_s, T.xs_ld, s_sc);
     __syncthreads();
 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -356,6 +393,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     auto step = [&](const BlockRegs& br, int sx) {
         block_mma<MTILES>(br, sx >= nsb ? sx - nsb : sx, T, acc);
         if (sx == nsb - 1) {
+            apply_row_scale<MTILES>(T, acc);
 #pragma unroll
             for (int mt = 0; mt < MTILES; ++mt) {
                 g_out[mt] = acc[mt];
@@ -376,6 +414,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
         step(b1, s + 1);
     }
 
+    apply_row_scale<MTILES>(T, acc);
     // h = silu(g) * u goes through LDS (the tile is no longer needed), so that
     // each thread then owns one (token, 32-row block): the token's amax over
     // the 256 rows is a reduction over 8 neighbouring lanes, and the codes of
@@ -437,13 +476,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
             uint4* dst = reinterpret_cast<uint4*>(a.hq + (uint32_t)(orow * I + nb * 256 + c32 * 32));
             dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
             dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-            const int I32 = I / 32;
-            const float sv = (float)qsum * d;
-            const __bf16 sh = (__bf16)sv;
-            const __bf16 sl = (__bf16)(sv - (float)sh);
-            const uint32_t o0 = (uint32_t)(orow * (2 * I32) + nb * 8 + c32);
-            a.hs[o0] = __builtin_bit_cast(uint16_t, sh);
-            a.hs[o0 + I32] = __builtin_bit_cast(uint16_t, sl);
+            a.hs[(uint32_t)(orow * (I / 32) + nb * 8 + c32)] = (int16_t)qsum;
             if (c32 == 0) a.hd[(uint32_t)(orow * NB + nb)] = d;
         }
     }
@@ -456,6 +489,7 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int s_src[MT], s_out[MT];
+    __shared__ __attribute__((aligned(16))) float s_sc[MT];
 
     const int H = a.H, I = a.I, nsb = I / 256;
     const int NB = (H / 256 + kDownRounds - 1) / kDownRounds;
@@ -469,8 +503,8 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     int8_t* lds_a;
     float* hd_s;
     uint16_t* hs_s;
-    const TileLds T = carve<MTILES>(lds, I, lds_a, hd_s, hs_s);
-    load_tile<MTILES>(a.hq, a.hd, a.hs, I, s_src, lds_a, T.lda, hd_s, hs_s, T.xs_ld);
+    const TileLds T = carve<MTILES>(lds, I, s_sc, lds_a, hd_s, hs_s);
+    load_tile<MTILES>(a.hq, a.hd, a.hs, I, s_src, lds_a, T.lda, hd_s, hs_s, T.xs_ld, s_sc);
     __syncthreads();
 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -497,6 +531,7 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
         const int r = sx / nsb, b = sx - r * nsb;
         block_mma<MTILES>(br, b, T, acc);
         if (b == nsb - 1) {
+            apply_row_scale<MTILES>(T, acc);
             const int o = (r0 + r) * 256 + wave * 32 + n;
 #pragma unroll
             for (int mt = 0; mt < MTILES; ++mt) {
@@ -526,10 +561,9 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     if (s < steps) step(b0, s);
 }
 
-// xs[t] = the bf16 hi parts of v_c = (sum_{l<32} xq[t][32c + l]) * xd[t][c/8]
-// for c < K/32, then their lo parts bf16(v_c - hi_c); one thread per (t, c).
-__global__ void __launch_bounds__(256) act_sums_kernel(const int8_t* __restrict__ xq, const float* __restrict__ xd,
-                                                       int64_t n, int K, uint16_t* __restrict__ xs) {
+// xs[t][c] = sum_{l<32} xq[t][32c + l] (exact, |xs| <= 4064), one thread per (t, c).
+__global__ void __launch_bounds__(256) act_sums_kernel(const int8_t* __restrict__ xq, int64_t n, int K,
+                                                       int16_t* __restrict__ xs) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= n) return;
     const int k32 = K / 32;
@@ -543,11 +577,7 @@ __global__ void __launch_bounds__(256) act_sums_kernel(const int8_t* __restrict_
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int bsh = 0; bsh < 32; bsh += 8) s += (int)(int8_t)(w[i] >> bsh);
-    const float v = (float)s * xd[t * (K / 256) + c / 8];
-    const __bf16 hi = (__bf16)v;
-    const __bf16 lo = (__bf16)(v - (float)hi);
-    xs[t * 2 * k32 + c] = __builtin_bit_cast(uint16_t, hi);
-    xs[t * 2 * k32 + k32 + c] = __builtin_bit_cast(uint16_t, lo);
+    xs[idx] = (int16_t)s;
 }
 
 // Tile list: tiles of 'mt' bucket entries per expert with count > 0, in
@@ -600,7 +630,7 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n_sums = (int64_t)a.T * (a.H / 32);
-    act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, a.xd, n_sums, a.H, a.xs);
+    act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, n_sums, a.H, a.xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds_gu = std::max(tile_lds_bytes<MTILES>(a.H), (size_t)MT * kHStride * sizeof(float));
     gateup_mfma_kernel<MTILES><<<grid_for(maxt * (a.I / 256)), kMThreads, lds_gu, s>>>(a);

@@ -47,8 +47,8 @@ struct FfnArgs {
     float* y_pair;                 // [T*k][H]
     float* y_shared;               // [T][H]
     int n_slots;                   // min(E, T*k) routed expert slots
-    uint16_t* xs;                  // workspace [T][2][H/32] bf16 (int8 MFMA path)
-    uint16_t* hs;                  // workspace [T*k + T][2][I/32] bf16 (int8 MFMA path)
+    int16_t* xs;                   // workspace [T][H/32]: per-32 sums of xq (int8 MFMA path)
+    int16_t* hs;                   // workspace [T*k + T][I/32]: per-32 sums of hq (int8 MFMA path)
     int32_t* tiles;                // workspace: MFMA tile list (mfma_tiles_bytes)
 };
 
@@ -63,10 +63,10 @@ struct MfmaArgs {
     const int32_t* pair;
     const int8_t* xq;              // [T][H]
     const float* xd;               // [T][H/256]
-    uint16_t* xs;                  // [T][2][H/32] bf16 hi, lo parts of the per-32 sums of xq times xd
+    int16_t* xs;                   // [T][H/32] per-32 sums of xq
     int8_t* hq;                    // [T*k + T][I]
     float* hd;                     // [T*k + T][I/256]
-    uint16_t* hs;                  // [T*k + T][2][I/32] the same for hq times hd
+    int16_t* hs;                   // [T*k + T][I/32] per-32 sums of hq
     float* y_pair;                 // [T*k][H]
     float* y_shared;               // [T][H]
     int32_t* tile_e;

@@ -100,9 +100,9 @@ FfnWorkspace ffn_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
         off += align_up(rows * (L->inter / 256) * sizeof(float), 256);
         if (w.mfma) {
             w.xs = off;
-            off += align_up((size_t)T * (L->hidden / 32) * 4, 256);
+            off += align_up((size_t)T * (L->hidden / 32) * 2, 256);
             w.hs = off;
-            off += align_up(rows * (L->inter / 32) * 4, 256);
+            off += align_up(rows * (L->inter / 32) * 2, 256);
             w.tiles = off;
             off += align_up(moe::mfma_tiles_bytes(T, k, L->n_experts, L->has_shared, L->hidden, L->inter), 256);
         }
@@ -115,8 +115,8 @@ void set_ffn_ws(moe::FfnArgs& a, char* base, const FfnWorkspace& w) {
     a.h = (float*)(base + w.h);
     a.hq = (int8_t*)(base + w.hq);
     a.hd = (float*)(base + w.hd);
-    a.xs = w.mfma ? (uint16_t*)(base + w.xs) : nullptr;
-    a.hs = w.mfma ? (uint16_t*)(base + w.hs) : nullptr;
+    a.xs = w.mfma ? (int16_t*)(base + w.xs) : nullptr;
+    a.hs = w.mfma ? (int16_t*)(base + w.hs) : nullptr;
     a.tiles = w.mfma ? (int32_t*)(base + w.tiles) : nullptr;
 }
 

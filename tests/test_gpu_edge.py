@@ -1,0 +1,181 @@
+"""GPU parity on the degenerate and boundary cases of the layer, through the C ABI.
+
+Covered here: a single expert (E = 1, k = 1); every expert selected (k = E);
+every token routed to the same experts (one bucket spanning several MFMA
+tiles); all-zero activations (the quantiser's amax = 0 rule, outputs exactly 0);
+the largest hidden and intermediate sizes the library takes (3,584); the
+boundary of the AUTO path choice (T = 64 decode, T = 65 int8); and graph replay
+of the int8 path.  References come from the CPU oracle on the same seeded
+inputs; tolerances as in the other parity tests.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_moe_ffn_amd import synth
+
+from tests.gpu_helpers import TOL_DECODE, TOL_INT8, normwise_err, oracle_pairs, oracle_shared
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def qm():
+    import quantized_moe_ffn_amd as m
+    m.load_library()
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _layer(**over):
+    from quantized_moe_ffn_amd import layers
+    w = synth.Workload(**{**synth.WORKLOADS["tiny"].__dict__, **over})
+    return layers.make_layer(w, seed=11, index=0, device=DEV), w
+
+
+def _forward(m, dl, logits, x, k, flags, fused):
+    lg = torch.from_numpy(np.ascontiguousarray(logits)).to(DEV)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    bufs = m.forward(dl.layer, lg, xt, k, flags=flags, fused=fused)
+    m.moe_check_device_errors()
+    return bufs
+
+
+def _reference(dl, w, logits, x, mode):
+    k = w.top_k
+    T = x.shape[0]
+    idx, wts = oracle.route_topk(logits, k)
+    y, hb = oracle_pairs(dl, idx.reshape(-1), np.repeat(np.arange(T), k), x, mode)
+    ys = oracle_shared(dl, hb, np.arange(T), x, mode) if w.shared else None
+    return y, ys, oracle.combine(y, wts, ys), idx
+
+
+def _check(m, dl, w, logits, x, flags, fused, tol):
+    mode = 1 if flags == m.MOE_FFN_INT8 else 0
+    bufs = _forward(m, dl, logits, x, w.top_k, flags, fused)
+    y, ys, out, idx = _reference(dl, w, logits, x, mode)
+    assert np.array_equal(bufs.routing.idx.cpu().numpy(), idx)
+    ey = normwise_err(bufs.y_pair.cpu().numpy(), y)
+    eo = normwise_err(bufs.out.cpu().numpy(), out)
+    _say("  y_pair err max %.3e  out err max %.3e" % (ey.max(), eo.max()))
+    assert ey.max() <= tol and eo.max() <= tol
+    if ys is not None:
+        assert normwise_err(bufs.y_shared.cpu().numpy(), ys).max() <= tol
+    return bufs
+
+
+PATHS = [("decode", False), ("decode", True), ("int8", False), ("int8", True)]
+
+
+def _flags(m, path):
+    return m.MOE_FFN_INT8 if path == "int8" else m.MOE_FFN_DECODE
+
+
+@pytest.mark.parametrize("path,fused", PATHS)
+@pytest.mark.parametrize("over", [
+    dict(n_experts=1, top_k=1, tokens=5),                     # a single expert
+    dict(n_experts=4, top_k=4, tokens=3, shared=True),        # every expert selected, plus the shared one
+    dict(n_experts=4, top_k=4, tokens=70),                    # k = E with 70 tokens per bucket
+])
+def test_degenerate_expert_counts(over, path, fused):
+    m = qm()
+    _say("edge", over, path, fused)
+    dl, w = _layer(**over)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=12)
+    _check(m, dl, w, logits, x, _flags(m, path), fused, TOL_INT8 if path == "int8" else TOL_DECODE)
+
+
+@pytest.mark.parametrize("path,fused", PATHS)
+def test_every_token_on_the_same_experts(path, fused):
+    """Identical logit rows: all pairs land in k buckets; the int8 path then tiles one
+    expert's bucket of 300 tokens into several 64-token tiles."""
+    m = qm()
+    dl, w = _layer(n_experts=16, top_k=3, tokens=300 if path == "int8" else 4)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=13)
+    logits[:] = logits[0]
+    bufs = _check(m, dl, w, logits, x, _flags(m, path), fused, TOL_INT8 if path == "int8" else TOL_DECODE)
+    counts = bufs.routing.count.cpu().numpy()
+    assert sorted(counts[counts > 0].tolist()) == [x.shape[0]] * 3
+
+
+@pytest.mark.parametrize("path,fused", PATHS)
+def test_zero_activations_give_zero_outputs(path, fused):
+    """x = 0: the int8 quantiser's amax = 0 rule gives d = 0 and q = 0, h = silu(0)*0 = 0,
+    and every output is exactly +-0 on both paths."""
+    m = qm()
+    dl, w = _layer(n_experts=8, top_k=2, tokens=6, shared=True)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=14)
+    x[:] = 0.0
+    bufs = _forward(m, dl, logits, x, w.top_k, _flags(m, path), fused)
+    assert not np.any(bufs.out.cpu().numpy())
+    assert not np.any(bufs.y_pair.cpu().numpy())
+    assert not np.any(bufs.y_shared.cpu().numpy())
+
+
+@pytest.mark.parametrize("path", ["decode", "int8"])
+@pytest.mark.parametrize("over", [
+    dict(hidden=3584, inter=256, n_experts=3, top_k=2, tokens=3),    # largest hidden: 14 blocks per gate row
+    dict(hidden=256, inter=3584, n_experts=3, top_k=2, tokens=3),    # largest inter: 14 blocks per down row
+])
+def test_largest_dimensions(over, path):
+    m = qm()
+    _say("largest dims", over, path)
+    dl, w = _layer(**over)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=15)
+    _check(m, dl, w, logits, x, _flags(m, path), True, TOL_INT8 if path == "int8" else TOL_DECODE)
+
+
+@pytest.mark.parametrize("T,mode", [(64, 0), (65, 1)])
+def test_auto_path_boundary(T, mode):
+    """MOE_FFN_AUTO runs the fp-activation path up to 64 tokens and the int8 path above."""
+    m = qm()
+    dl, w = _layer(n_experts=8, top_k=2, tokens=T)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=16)
+    bufs = _forward(m, dl, logits, x, w.top_k, m.MOE_FFN_AUTO, True)
+    y, ys, out, idx = _reference(dl, w, logits, x, mode)
+    e = normwise_err(bufs.out.cpu().numpy(), out)
+    assert e.max() <= (TOL_INT8 if mode else TOL_DECODE)
+    # the other path's reference is farther away (quantisation-sized) for the int8 case
+    if mode == 1:
+        _, _, out_fp, _ = _reference(dl, w, logits, x, 0)
+        assert normwise_err(bufs.out.cpu().numpy(), out_fp).max() > 10 * e.max()
+
+
+def test_int8_graph_replay_matches_eager():
+    """The int8 path (routing, quantisation, tile list, MFMA GEMMs, combine) captured in a
+    graph replays to the eager bits, with unrelated eager work between replays."""
+    m = qm()
+    dl, w = _layer(n_experts=8, top_k=2, tokens=200)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=17)
+    lg = torch.from_numpy(logits).to(DEV)
+    xt = torch.from_numpy(x).to(DEV)
+    bufs = m.LayerBuffers(dl.layer, x.shape[0], w.top_k, m.MOE_FFN_INT8, device=DEV)
+    m.forward(dl.layer, lg, xt, w.top_k, bufs, flags=m.MOE_FFN_INT8)
+    torch.cuda.synchronize()
+    eager = bufs.out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            m.forward(dl.layer, lg, xt, w.top_k, bufs, flags=m.MOE_FFN_INT8)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        bufs.out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        g.replay()
+        torch.cuda.synchronize()
+        float(junk)
+        assert torch.equal(bufs.out, eager), rep
+    m.moe_check_device_errors()
