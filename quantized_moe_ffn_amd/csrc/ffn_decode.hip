@@ -303,8 +303,46 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     out[idx] = acc;
 }
 
+// Four consecutive outputs per thread with 16-byte loads and stores (the same
+// per-element summation order as combine_kernel, so the same bits).
+__global__ void __launch_bounds__(256) combine4_kernel(const float4* __restrict__ y_pair,
+                                                       const float* __restrict__ w,
+                                                       const float4* __restrict__ y_shared,
+                                                       const float* __restrict__ shared_scale, int T, int k,
+                                                       int H4, float4* __restrict__ out) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)T * H4) return;
+    const int t = (int)(idx / H4), o = (int)(idx - (int64_t)t * H4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const float wj = w[t * k + j];
+        const float4 y = y_pair[((int64_t)t * k + j) * H4 + o];
+        acc.x = fmaf(wj, y.x, acc.x);
+        acc.y = fmaf(wj, y.y, acc.y);
+        acc.z = fmaf(wj, y.z, acc.z);
+        acc.w = fmaf(wj, y.w, acc.w);
+    }
+    if (y_shared) {
+        const float sc = shared_scale ? shared_scale[t] : 1.0f;
+        const float4 ys = y_shared[(int64_t)t * H4 + o];
+        acc.x = fmaf(sc, ys.x, acc.x);
+        acc.y = fmaf(sc, ys.y, acc.y);
+        acc.z = fmaf(sc, ys.z, acc.z);
+        acc.w = fmaf(sc, ys.w, acc.w);
+    }
+    out[idx] = acc;
+}
+
 hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared,
                           const float* shared_scale, int T, int k, int H, float* out, hipStream_t s) {
+    const auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+    if (H % 4 == 0 && a16(y_pair) && a16(out) && (!y_shared || a16(y_shared))) {
+        const int64_t n = (int64_t)T * (H / 4);
+        combine4_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+            reinterpret_cast<const float4*>(y_pair), w, reinterpret_cast<const float4*>(y_shared), shared_scale,
+            T, k, H / 4, reinterpret_cast<float4*>(out));
+        return hipGetLastError();
+    }
     const int64_t n = (int64_t)T * H;
     combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(y_pair, w, y_shared, shared_scale, T, k, H, out);
     return hipGetLastError();

@@ -403,3 +403,30 @@ def test_combine_shared_scale_and_one_hot():
                   torch.from_numpy(sc).to(DEV))
     ref = oracle.combine(y.astype(np.float64), wts.astype(np.float64), ys.astype(np.float64), sc.astype(np.float64))
     assert np.abs(out.cpu().numpy() - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_combine_vector_and_scalar_paths_agree():
+    """16-byte aligned buffers take the 4-wide combine; buffers offset by one float take
+    the scalar one; both sum in slot order, then the shared expert, so the bits agree."""
+    m = qm()
+    g = np.random.default_rng(501)
+    T, k, H = 5, 3, 768
+    y = torch.from_numpy(g.standard_normal((T * k, H)).astype(np.float32)).to(DEV)
+    wts = torch.from_numpy(g.random((T, k)).astype(np.float32)).to(DEV)
+    ys = torch.from_numpy(g.standard_normal((T, H)).astype(np.float32)).to(DEV)
+    out_a = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    m.moe_combine(y, wts, out_a, ys)
+
+    def shifted(t):   # same values, data pointer 4 bytes past a 16-byte boundary
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+    out_b = shifted(torch.zeros((T, H), dtype=torch.float32, device=DEV))
+    m.moe_combine(shifted(y), wts, out_b, shifted(ys))
+    m.moe_check_device_errors()
+    assert out_b.data_ptr() % 16 == 4
+    assert torch.equal(out_a, out_b)
+    ref = oracle.combine(y.cpu().numpy().astype(np.float64), wts.cpu().numpy().astype(np.float64),
+                         ys.cpu().numpy().astype(np.float64))
+    assert np.abs(out_a.cpu().numpy() - ref).max() <= 1e-6 * np.abs(ref).max()
