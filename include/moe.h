@@ -70,7 +70,8 @@ enum { MOE_ROUTE_RENORM = 1u }; /* weights = softmax over the k selected logits 
 enum {
     MOE_FFN_AUTO = 0u,   /* decode path for small batches, int8 path otherwise        */
     MOE_FFN_DECODE = 1u, /* fp32 activations, weights dequantized in registers        */
-    MOE_FFN_INT8 = 2u    /* int8 activations (moe_quantize_act), grouped int8 MFMA GEMM */
+    MOE_FFN_INT8 = 2u    /* int8 activations (moe_quantize_act); grouped int8 MFMA GEMMs
+                            when gate, up and down (and the shared expert) are all Q4_K */
 };
 
 /* One projection of an expert bank: n_experts matrices of rows x cols weights,
@@ -152,10 +153,16 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_
  *   y_pair[p] = W_down[e] * (silu(W_gate[e] x_t) .* (W_up[e] x_t)),  e = idx[p], t = p / k
  *   y_shared[t] = the same with the shared expert's matrices (when has_shared).
  * Weights are dequantized inside the dot products.  Decode path: x fp32 [T][H].
- * Int8 path: xq/xd from moe_quantize_act; h is re-quantized per 256-wide block
- * of I for the int8 down projection.  y_pair fp32 [T*k][H]; y_shared fp32
- * [T][H] (required iff has_shared).  r must hold the result of moe_route_topk
- * for the same T, k and E (read on the device: no host synchronisation).
+ * Int8 path: xq/xd from moe_quantize_act (xq 16-byte aligned); h is
+ * re-quantized per (pair, 256-wide block of I) with moe_quantize_act's rule for
+ * the int8 down projection.  With every matrix Q4_K (and (T*k + T)*max(H, I) <
+ * 2^31) both projections run as grouped int8 MFMA GEMMs over the tokens of each
+ * expert; there the Q4_K min term is carried in fp16, so every block's dmin must
+ * be below 1039 in magnitude (dmin*63 < 65504).  Other format mixes use the
+ * decode path's kernels on the dequantized int8 activations.  y_pair fp32
+ * [T*k][H]; y_shared fp32 [T][H] (required iff has_shared).  r must hold the
+ * result of moe_route_topk for the same T, k and E (read on the device: no host
+ * synchronisation).
  * Checks: shapes consistent with L; H, I multiples of 256; qtypes supported
  * (gate/up/down: Q4_K or Q8_0); alignment; workspace size. */
 moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T, int32_t k,
@@ -181,9 +188,9 @@ size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uin
  * enqueued on one stream.  For decode batches (T <= 4, T*k <= 64, Q4_K
  * gate/up with H/256 in {1,2,4,8,10}, down rows of 8, 16 or 32 32-weight
  * blocks, 16-byte aligned banks) the layer runs as two kernels: routing fused
- * into the gate/up kernel (recomputed per workgroup) and the combine fused
- * into the down kernel (formed in slot order in LDS); other shapes run the
- * separate stages.  Same results contract as the three calls (bitwise
+ * into the gate/up kernel (each workgroup recomputes the top-k of its token)
+ * and the combine fused into the down kernel (formed in slot order in LDS);
+ * other shapes run the separate stages.  Same results contract as the three calls (bitwise
  * deterministic; combine in slot order).  y_pair [T*k][H] is always written;
  * y_shared [T][H] is required iff the layer has a shared expert;
  * shared_scale [T] or NULL.  x must be 16-byte aligned.  Checks: those of

@@ -46,74 +46,34 @@ struct Gcd<A, 0> {
     static constexpr int value = A;
 };
 
-// Routing of up to kDecMaxT tokens, computed redundantly by every workgroup.
-// Expert slots u = 0 .. n_uniq-1 each own the pairs pair[uoff[u] .. uoff[u+1]).
-// For one token the slots are the k selections in slot order (pair u = u); for
-// several tokens they are the distinct experts in ascending order.
-struct DecRoute {   // also copied verbatim through the workspace from K1 to K2
-    int sel[kDecMaxPairs];       // expert of pair p = t*k + j (slot order)
+// Routing of up to kDecMaxT tokens: the expert and weight of every pair
+// p = t*k + j in slot order.  One workgroup of K1 computes it and hands it to
+// K2 through the workspace.
+struct DecRoute {
+    int sel[kDecMaxPairs];
     float w[kDecMaxPairs];
-    int pair[kDecMaxPairs];
-    int uniq[kDecMaxPairs];
-    int uoff[kDecMaxPairs + 1];
-    int n_uniq;
 };
 
 static_assert(sizeof(DecRoute) <= kDecRouteTabBytes, "routing table size");
 
-// Waves 0..T-1 select the top-k of token t; wave 0 then builds the slots.
-// Ends with __syncthreads().
+// Waves 0..T-1 select the top-k of token t.  Ends with __syncthreads().
 template <int V>
 __device__ __forceinline__ void dec_route(const float* __restrict__ logits, int T, int E, int k, int renorm, DecRoute& R) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    int e = -1;
-    float w = 0.f;
     if (wave < T) {
+        int e = -1;
+        float w = 0.f;
         wave_topk<V>(logits + (int64_t)wave * E, E, k, renorm != 0, e, w);
         if (lane < k) {
             R.sel[wave * k + lane] = e;
             R.w[wave * k + lane] = w;
         }
     }
-    if (T == 1) {
-        if (wave == 0) {
-            if (lane < k) {
-                R.uniq[lane] = e;
-                R.uoff[lane] = lane;
-                R.pair[lane] = lane;
-            }
-            if (lane == 0) {
-                R.n_uniq = k;
-                R.uoff[k] = k;
-            }
-        }
-        __syncthreads();
-        return;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const int P = T * k;
-        const int ep = lane < P ? R.sel[lane] : 0x7FFFFFFF;
-        int below, same_before, ubelow, n_uniq;
-        bool first;
-        wave_buckets(ep, P, below, same_before, first, ubelow, n_uniq);
-        if (lane < P) {
-            R.pair[below + same_before] = lane;
-            if (first) {
-                R.uniq[ubelow] = ep;
-                R.uoff[ubelow] = below;
-            }
-        }
-        if (lane == 0) {
-            R.n_uniq = n_uniq;
-            R.uoff[n_uniq] = P;
-        }
-    }
     __syncthreads();
 }
 
-// Workgroup 0 of K1 publishes the routing results in the layout moe_route_topk
-// writes (active experts ascending, pairs grouped by expert).
+// The publishing workgroup of K1 writes the routing results in the layout
+// moe_route_topk writes (active experts ascending, pairs grouped by expert).
 __device__ __forceinline__ void dec_publish(const DecRoute& R, int T, int E, int k, const RoutingPtrs& r) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int P = T * k;
