@@ -68,7 +68,7 @@ enum { MOE_ROUTE_RENORM = 1u }; /* weights = softmax over the k selected logits 
 
 /* moe_expert_ffn_q path selection */
 enum {
-    MOE_FFN_AUTO = 0u,   /* decode path for small batches, int8 path otherwise        */
+    MOE_FFN_AUTO = 0u,   /* decode path up to 8 tokens, int8 path above               */
     MOE_FFN_DECODE = 1u, /* fp32 activations, weights dequantized in registers        */
     MOE_FFN_INT8 = 2u    /* int8 activations (moe_quantize_act); grouped int8 MFMA GEMMs
                             when gate, up and down (and the shared expert) are all Q4_K */
@@ -185,7 +185,7 @@ size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uin
 /* The whole layer: routing (as moe_route_topk, results written to r), expert
  * FFN (as moe_expert_ffn_q, from fp32 x; on the int8 path x is quantized with
  * moe_quantize_act's rule into the workspace) and combine (as moe_combine),
- * enqueued on one stream.  For decode batches (T <= 4, T*k <= 64, Q4_K
+ * enqueued on one stream.  For decode batches (T <= 8, T*k <= 64, Q4_K
  * gate/up with H/256 in {1,2,4,8,10}, down rows of 8, 16 or 32 32-weight
  * blocks, 16-byte aligned banks) the layer runs as two kernels: routing fused
  * into the gate/up kernel (each workgroup recomputes the top-k of its token)

@@ -25,6 +25,7 @@ MOE_Q8_0 = 8
 MOE_Q4_K = 12
 MOE_ROUTE_RENORM = 1
 MOE_FFN_AUTO = 0
+AUTO_DECODE_MAX_T = 8   # MOE_FFN_AUTO takes the fp-activation path up to this many tokens
 MOE_FFN_DECODE = 1
 MOE_FFN_INT8 = 2
 
@@ -284,7 +285,7 @@ def forward(layer: Layer, logits, x, k: int, bufs: LayerBuffers | None = None, f
         moe_forward(layer, logits, x, k, bufs.routing, bufs.y_pair, bufs.out, bufs.y_shared, shared_scale, renorm,
                     flags, bufs.fwd_ws, stream)
         return bufs
-    path = flags if flags != MOE_FFN_AUTO else (MOE_FFN_DECODE if T <= 64 else MOE_FFN_INT8)
+    path = flags if flags != MOE_FFN_AUTO else (MOE_FFN_DECODE if T <= AUTO_DECODE_MAX_T else MOE_FFN_INT8)
     moe_route_topk(logits, k, bufs.routing, renorm, bufs.route_ws, stream)
     if path == MOE_FFN_INT8:
         moe_quantize_act(x, bufs.xq, bufs.xd, stream)

@@ -34,7 +34,8 @@
 
 namespace moe {
 
-constexpr int kDecMaxT = 4;      // tokens handled by the fused decode path
+constexpr int kDecMaxT = 8;      // tokens handled by the fused decode path
+constexpr int kShTok = 4;        // tokens per shared-expert group of the gate/up kernel
 constexpr int kDecMaxPairs = 64; // T*k
 
 template <int A, int B>
@@ -56,17 +57,18 @@ struct DecRoute {
 
 static_assert(sizeof(DecRoute) <= kDecRouteTabBytes, "routing table size");
 
-// Waves 0..T-1 select the top-k of token t.  Ends with __syncthreads().
+// Wave w selects the top-k of tokens w, w + nwaves, ...  Ends with __syncthreads().
 template <int V>
 __device__ __forceinline__ void dec_route(const float* __restrict__ logits, int T, int E, int k, int renorm, DecRoute& R) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    if (wave < T) {
+    const int nwaves = blockDim.x / kWave;
+    for (int t = wave; t < T; t += nwaves) {
         int e = -1;
         float w = 0.f;
-        wave_topk<V>(logits + (int64_t)wave * E, E, k, renorm != 0, e, w);
+        wave_topk<V>(logits + (int64_t)t * E, E, k, renorm != 0, e, w);
         if (lane < k) {
-            R.sel[wave * k + lane] = e;
-            R.w[wave * k + lane] = w;
+            R.sel[t * k + lane] = e;
+            R.w[t * k + lane] = w;
         }
     }
     __syncthreads();
@@ -295,9 +297,10 @@ __device__ __forceinline__ void load_x_slice(const DecArgs& a, int tok, int clo,
 // early slots overlaps the remaining rounds; the dot products then consume the
 // slots in issue order.  Each (token, slot) pair streams its own expert rows:
 // in a 3-token window nearly all 24 experts are distinct, so sharing loads
-// between tokens would save little.  Group T*Gk (when the layer has one) runs
-// the shared expert for all T tokens against one load of its rows; the last
-// group is one workgroup that publishes the routing (and the table for K2).
+// between tokens would save little.  Groups T*Gk .. T*Gk + ceil(T/4) - 1 (when
+// the layer has a shared expert) each run it for 4 tokens against one load of
+// its rows; the last group is one workgroup that publishes the routing (and
+// the table for K2).
 // ---------------------------------------------------------------------------
 constexpr int kT1SlotsPerGroup = 4;
 
@@ -305,11 +308,11 @@ template <int NB, int V, int TT>
 __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_kernel(DecArgs a, int Gk) {
     using S = K1Shape<NB, 1>;
     constexpr int SM = kT1SlotsPerGroup;
-    static_assert(SM >= TT, "s_part holds SM slots");
+    static_assert(SM >= TT && TT <= kShTok, "s_part holds SM slots");
     const int y = blockIdx.y;
     const int Gr = a.T * Gk;
-    const int y_sh = a.has_shared ? Gr : -1;
-    const int y_pub = Gr + (a.has_shared ? 1 : 0);
+    const int n_sh = a.has_shared ? (a.T + kShTok - 1) / kShTok : 0;
+    const int y_pub = Gr + n_sh;
     if (y == y_pub) {
         __shared__ DecRoute R;
         if (blockIdx.x != 0) return;
@@ -331,17 +334,19 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
     const int i = blockIdx.x * S::ROWS + unit * S::P + rr;
     const int ic = i < a.I ? i : a.I - 1;   // rows past I load a valid row and are not stored
 
-    if (y == y_sh) {
-        // the shared expert: one load of its rows for all T tokens
+    if (y >= Gr) {
+        // the shared expert: one load of its rows for tokens t0 .. t0 + TT - 1
+        const int t0 = (y - Gr) * kShTok;
+        const int nt = min(TT, a.T - t0);
         float4 xl4[TT][4], xh4[TT][4];
         int hrows[TT];
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-            const int tc = t < a.T ? t : a.T - 1;
+            const int tc = t0 + (t < nt ? t : nt - 1);
             load_x_slice<TT>(a, tc, clo, chi, xl4[t], xh4[t]);
             hrows[t] = a.T * a.k + tc;
         }
-        dec_gateup_body<NB, 1, TT>(a, a.sgate, a.sup, 0, a.T, hrows, xl4, xh4, s_part);
+        dec_gateup_body<NB, 1, TT>(a, a.sgate, a.sup, 0, nt, hrows, xl4, xh4, s_part);
         return;
     }
 
@@ -595,7 +600,8 @@ template <int NB, int V, int TT>
 hipError_t launch_k1_pipe(const DecArgs& a, hipStream_t s) {
     using S = K1Shape<NB, 1>;
     const int Gk = (a.k + kT1SlotsPerGroup - 1) / kT1SlotsPerGroup;   // groups per token
-    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, a.T * Gk + (a.has_shared ? 1 : 0) + 1);
+    const int n_sh = a.has_shared ? (a.T + kShTok - 1) / kShTok : 0;  // shared-expert groups
+    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, a.T * Gk + n_sh + 1);
     dec_gateup_pipe_kernel<NB, V, TT><<<grid, S::THREADS, 0, s>>>(a, Gk);
     return hipGetLastError();
 }
@@ -604,7 +610,7 @@ template <int NB, int V>
 hipError_t launch_k1_v(const DecArgs& a, hipStream_t s) {
     // the 4-token shared-expert branch costs registers; it runs only when the
     // layer has a shared expert and more than one token
-    return (a.T == 1 || !a.has_shared) ? launch_k1_pipe<NB, V, 1>(a, s) : launch_k1_pipe<NB, V, kDecMaxT>(a, s);
+    return (a.T == 1 || !a.has_shared) ? launch_k1_pipe<NB, V, 1>(a, s) : launch_k1_pipe<NB, V, kShTok>(a, s);
 }
 
 template <int NB>

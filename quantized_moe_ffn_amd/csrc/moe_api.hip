@@ -39,7 +39,7 @@ int blk_bytes(int qt) { return qt == MOE_Q4_K ? 144 : 34; }
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxDim = 3584;   // H and I: LDS staging of kTokChunk rows of fp32 (< 64 KB)
-constexpr int kAutoDecodeMaxT = 64;
+constexpr int kAutoDecodeMaxT = 8;   // AUTO: fp-activation path up to this many tokens
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

@@ -4,7 +4,7 @@ Covered here: a single expert (E = 1, k = 1); every expert selected (k = E);
 every token routed to the same experts (one bucket spanning several MFMA
 tiles); all-zero activations (the quantiser's amax = 0 rule, outputs exactly 0);
 the largest hidden and intermediate sizes the library takes (3,584); the
-boundary of the AUTO path choice (T = 64 decode, T = 65 int8); and graph replay
+boundary of the AUTO path choice (T = 8 decode, T = 9 int8); and graph replay
 of the int8 path.  References come from the CPU oracle on the same seeded
 inputs; tolerances as in the other parity tests.
 """
@@ -134,9 +134,9 @@ def test_largest_dimensions(over, path):
     _check(m, dl, w, logits, x, _flags(m, path), True, TOL_INT8 if path == "int8" else TOL_DECODE)
 
 
-@pytest.mark.parametrize("T,mode", [(64, 0), (65, 1)])
+@pytest.mark.parametrize("T,mode", [(8, 0), (9, 1)])
 def test_auto_path_boundary(T, mode):
-    """MOE_FFN_AUTO runs the fp-activation path up to 64 tokens and the int8 path above."""
+    """MOE_FFN_AUTO runs the fp-activation path up to 8 tokens and the int8 path above."""
     m = qm()
     dl, w = _layer(n_experts=8, top_k=2, tokens=T)
     from quantized_moe_ffn_amd import layers
@@ -179,3 +179,22 @@ def test_int8_graph_replay_matches_eager():
         float(junk)
         assert torch.equal(bufs.out, eager), rep
     m.moe_check_device_errors()
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name,T,over", [
+    ("sage_decode", 5, dict(n_experts=64)),
+    ("sage_decode", 6, dict(n_experts=64)),
+    ("sage_decode", 8, dict(n_experts=64)),                 # T*k = 64, the fused path's maximum
+    ("flash_next_decode", 6, dict(n_experts=64)),           # shared expert in two 4-token groups, Q8_0 down
+])
+def test_decode_batches_up_to_eight_tokens(name, T, over, fused):
+    """Decode batches of 5-8 tokens (verify windows of prompt lookup, parallel slots) on the
+    two-kernel layer (fused) and the separate calls, against the oracle."""
+    m = qm()
+    _say("decode batch", name, T, fused)
+    from quantized_moe_ffn_amd import layers
+    w = synth.Workload(**{**synth.WORKLOADS[name].__dict__, **over, "tokens": T})
+    dl = layers.make_layer(w, seed=18, index=0, device=DEV)
+    logits, x = layers.inputs_np(w, seed=18)
+    _check(m, dl, w, logits, x, m.MOE_FFN_DECODE, fused, TOL_DECODE)
