@@ -108,3 +108,69 @@ def test_dequant_validation():
     assert lib.moe_dequant_q(ctypes.c_void_p(257), 12, 256, ctypes.c_void_p(256), None) == 1
     assert lib.moe_dequant_q(ctypes.c_void_p(256), 2, 256, ctypes.c_void_p(256), None) == 2
     assert lib.moe_dequant_q(ctypes.c_void_p(256), 8, 0, ctypes.c_void_p(256), None) == 0
+
+
+def _forward_args(L, r, T=2, k=2, x=4096, ws=None, ws_bytes=None, route_flags=0, ffn_flags=0, y_shared=None):
+    lib = qm.load_library()
+    if ws_bytes is None:
+        ws_bytes = lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, ffn_flags)
+    return (ctypes.byref(L), ctypes.c_void_p(4096), ctypes.c_void_p(x), T, k, route_flags, ffn_flags,
+            ctypes.byref(r), ctypes.c_void_p(8192), y_shared, None, ctypes.c_void_p(16384),
+            ctypes.c_void_p(4096 if ws is None else ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(T=0), 1, "T = 0"),
+    (dict(k=5), 1, "k = 5"),                          # k > E = 4
+    (dict(x=4100), 1, "16-byte aligned"),              # x 4-byte but not 16-byte aligned
+    (dict(route_flags=4), 1, "route_flags = 0x4"),
+    (dict(ffn_flags=7), 1, "ffn_flags = 0x7"),
+    (dict(ws=4096 + 64), 1, "256-byte aligned"),
+])
+def test_forward_validation_messages(over, status, msg):
+    lib = qm.load_library()
+    r = _routing_null()
+    L = _layer()
+    st = lib.moe_forward(*_forward_args(L, r, ws_bytes=1 << 30, **over))
+    assert st == status, qm.moe_last_error()
+    assert msg in qm.moe_last_error()
+
+
+@pytest.mark.parametrize("T,flags", [(1, 0), (3, 1), (8, 0), (9, 0), (64, 2)])
+def test_forward_rejects_short_workspace(T, flags):
+    lib = qm.load_library()
+    r = _routing_null()
+    L = _layer()
+    need = lib.moe_forward_workspace_bytes(ctypes.byref(L), T, 2, flags)
+    st = lib.moe_forward(*_forward_args(L, r, T=T, ws_bytes=need - 1, ffn_flags=flags))
+    assert st == 3 and "forward workspace" in qm.moe_last_error()
+    st = lib.moe_forward(*_forward_args(L, r, T=T, ws=0, ws_bytes=need, ffn_flags=flags))
+    assert st == 3
+
+
+def test_forward_requires_y_shared_for_a_shared_layer():
+    lib = qm.load_library()
+    r = _routing_null()
+    L = _layer()
+    L.has_shared = 1
+    L.sh_gate, L.sh_up, L.sh_down = _qm(qm.MOE_Q4_K, 256, 512, 1), _qm(qm.MOE_Q4_K, 256, 512, 1), \
+        _qm(qm.MOE_Q4_K, 512, 256, 1)
+    st = lib.moe_forward(*_forward_args(L, r))
+    assert st == 1 and "y_shared is NULL" in qm.moe_last_error()
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 9, 64, 4096])
+@pytest.mark.parametrize("flags", [0, 1, 2])
+@pytest.mark.parametrize("shape", [dict(H=2048, I=512, E=256), dict(H=2560, I=512, E=512, qd=qm.MOE_Q8_0)])
+def test_workspace_sizes_cover_the_stages(T, flags, shape):
+    """moe_forward's workspace holds the routing and FFN workspaces of the same path plus the
+    int8 codes and scales of x, and the FFN workspace of one path grows with T."""
+    lib = qm.load_library()
+    L = _layer(**shape)
+    k = 8
+    fwd = lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, flags)
+    ffn = lib.moe_ffn_workspace_bytes(ctypes.byref(L), T, k, flags)
+    route = lib.moe_route_workspace_bytes(T, L.n_experts, k)
+    assert fwd >= ffn + route + T * L.hidden + T * (L.hidden // 256) * 4
+    if flags != 0:
+        assert lib.moe_ffn_workspace_bytes(ctypes.byref(L), 2 * T, k, flags) >= ffn
