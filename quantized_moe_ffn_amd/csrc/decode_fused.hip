@@ -1,14 +1,17 @@
-// decode_fused.hip — the decode-sized layer (T <= 4 tokens) in two kernels:
+// decode_fused.hip — the decode-sized layer (T <= 8 tokens, T*k <= 64) in two
+// kernels:
 //
-//   K1 route + gate/up + SiLU: every workgroup recomputes the top-k of the (at
-//      most 4) tokens from the router logits (one wave per token), derives the
-//      expert buckets in LDS, then streams its tile of gate and up rows of one
-//      expert and writes h = silu(W_gate x) * (W_up x) for the tokens routed to
-//      it.  Workgroup 0 also writes the routing results (idx, w, count, offset,
-//      pair, active, n_active).
-//   K2 down + combine: a workgroup owns a tile of output rows for EVERY expert
-//      of the layer (waves split the experts), so the routing-weighted sum over
-//      the k slots (plus the shared expert) is formed in LDS in slot order and
+//   K1 route + gate/up + SiLU: every wave recomputes the top-k of its token
+//      from the router logits and issues the weight loads of each slot as soon
+//      as the extraction round that names its expert ends; each workgroup
+//      streams a tile of gate and up rows for up to two slots of one token
+//      (or the shared expert for up to four tokens) and writes
+//      h = silu(W_gate x) * (W_up x).  One extra workgroup writes the routing
+//      results (idx, w, count, offset, pair, active, n_active) and a compact
+//      table of the selected experts and weights for K2.
+//   K2 down + combine: a workgroup owns a tile of output rows for every slot
+//      of the layer (one slot per wave), so the routing-weighted sum over the k
+//      slots (plus the shared expert) is formed in LDS in slot order and
 //      written once: no float atomics, bitwise deterministic.
 //
 // Two launches per layer instead of four: on MI355X a small kernel costs a few
@@ -119,22 +122,42 @@ struct K1Shape {
     static constexpr int GROUPS = IN_WAVE ? 1 : SLICES / 16;  // 16-lane groups per row otherwise
 };
 
+// Per-lane constants of the slice decode.  They are hidden from the compiler
+// (an empty asm that claims to change them) so that it keeps the byte masks as
+// written: a masked word then converts with one v_cvt_f32_ubyteN per weight
+// instead of a bit-field extract plus a conversion.
+//   scale word of the slice's sub-blocks: ((h1 >> sa) & ma) | (h3 & mb),
+//   min word:                             ((h2 >> sa) & ma) | ((h3 >> 4) & mb),
+// each holding the 6-bit values of sub-blocks 0-3 (c < 2) or 4-7 (c >= 2) in
+// its bytes; sub-blocks 2c, 2c+1 are bytes 2(c%2), 2(c%2)+1, brought down by sh.
+struct SliceKit {
+    uint32_t m_lo, m_hi, sa, ma, mb, sh;
+};
+
+__device__ __forceinline__ SliceKit slice_kit(int part) {
+    const bool upper = part >= 4;
+    SliceKit k{0x0F0F0F0Fu, 0xF0F0F0F0u, upper ? 2u : 0u, upper ? 0x30303030u : 0x3F3F3F3Fu,
+               upper ? 0x0F0F0F0Fu : 0u, 8u * (uint32_t)(part & 2)};
+    asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.sa), "+v"(k.ma), "+v"(k.mb), "+v"(k.sh));
+    return k;
+}
+
 // Dot products of one slice (16 quant bytes + its super-block header) with the
 // lane's activations of nt tokens: acc[t] = sum over the slice's 32 weights.
+// High nibbles are converted in place (16*q) and their scale carries the 1/16.
 template <int TT>
-__device__ __forceinline__ void q4k_slice_dot(const uint4 hv, const uint4 qv, int part, int nt,
+__device__ __forceinline__ void q4k_slice_dot(const uint4 hv, const uint4 qv, const SliceKit& kit, int nt,
                                               const float (&xl)[TT][16], const float (&xh)[TT][16],
                                               const float (&sxl)[TT], const float (&sxh)[TT], float (&acc)[TT]) {
-    const Q4KHead hd{hv.x, hv.y, hv.z, hv.w};
-    int sc_lo, m_lo, sc_hi, m_hi;
-    q4k_scale_min(hd, 2 * (part >> 1), sc_lo, m_lo);
-    q4k_scale_min(hd, 2 * (part >> 1) + 1, sc_hi, m_hi);
-    const float d = q4k_d(hd), dmin = q4k_dmin(hd);
+    const uint32_t scw = ((hv.y >> kit.sa) & kit.ma) | (hv.w & kit.mb);
+    const uint32_t mnw = ((hv.z >> kit.sa) & kit.ma) | ((hv.w >> 4) & kit.mb);
+    const uint32_t sc2 = scw >> kit.sh, mn2 = mnw >> kit.sh;
+    const float d = f16_bits_to_f32(hv.x & 0xFFFFu), dmin = f16_bits_to_f32(hv.x >> 16);
     const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
     float ql[16], qh[16];
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-        const uint32_t lo = qw[i4] & 0x0F0F0F0Fu, hi = (qw[i4] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t lo = qw[i4] & kit.m_lo, hi = qw[i4] & kit.m_hi;
         ql[4 * i4 + 0] = ubyte_f32<0>(lo);
         ql[4 * i4 + 1] = ubyte_f32<1>(lo);
         ql[4 * i4 + 2] = ubyte_f32<2>(lo);
@@ -144,19 +167,22 @@ __device__ __forceinline__ void q4k_slice_dot(const uint4 hv, const uint4 qv, in
         qh[4 * i4 + 2] = ubyte_f32<2>(hi);
         qh[4 * i4 + 3] = ubyte_f32<3>(hi);
     }
-    const float dsl = d * (float)sc_lo, dsh = d * (float)sc_hi;
-    const float mml = dmin * (float)m_lo, mmh = dmin * (float)m_hi;
+    const float dsl = d * ubyte_f32<0>(sc2), dsh = (d * 0.0625f) * ubyte_f32<1>(sc2);
+    const float mml = dmin * ubyte_f32<0>(mn2), mmh = dmin * ubyte_f32<1>(mn2);
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         acc[t] = 0.f;
         if (t < nt) {
-            float slo = 0.f, shi = 0.f;
+            // four accumulation chains (even/odd weights of each sub-block)
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                slo = fmaf(ql[j], xl[t][j], slo);
-                shi = fmaf(qh[j], xh[t][j], shi);
+            for (int j = 0; j < 16; j += 2) {
+                s0 = fmaf(ql[j], xl[t][j], s0);
+                s1 = fmaf(ql[j + 1], xl[t][j + 1], s1);
+                s2 = fmaf(qh[j], xh[t][j], s2);
+                s3 = fmaf(qh[j + 1], xh[t][j + 1], s3);
             }
-            acc[t] = dsl * slo + dsh * shi - (mml * sxl[t] + mmh * sxh[t]);
+            acc[t] = dsl * (s0 + s1) + dsh * (s2 + s3) - (mml * sxl[t] + mmh * sxh[t]);
         }
     }
 }
@@ -186,6 +212,7 @@ __device__ __forceinline__ void dec_gateup_body(const DecArgs& a, const QMat& G,
     const int rr = f / S::SLICES;                        // row inside the pass
     const int sl = f % S::SLICES;
     const int b = sl >> 3, part = sl & 7;
+    const SliceKit kit = slice_kit(part);
     const int row0 = blockIdx.x * S::ROWS;
 
     const uint8_t* Gb = G.data + (int64_t)e * G.expert_bytes + (int64_t)b * 144;
@@ -219,8 +246,8 @@ __device__ __forceinline__ void dec_gateup_body(const DecArgs& a, const QMat& G,
     for (int ps = 0; ps < PASSES; ++ps) {
         const int i = row0 + (ps * S::UNITS + unit) * S::P + rr;
         float pg[TT], pu[TT];
-        q4k_slice_dot<TT>(hg[ps], qg[ps], part, nt, xl, xh, sxl, sxh, pg);
-        q4k_slice_dot<TT>(hu[ps], qu[ps], part, nt, xl, xh, sxl, sxh, pu);
+        q4k_slice_dot<TT>(hg[ps], qg[ps], kit, nt, xl, xh, sxl, sxh, pg);
+        q4k_slice_dot<TT>(hu[ps], qu[ps], kit, nt, xl, xh, sxl, sxh, pu);
         if constexpr (S::IN_WAVE) {
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
@@ -291,29 +318,33 @@ __device__ __forceinline__ void load_x_slice(const DecArgs& a, int tok, int clo,
 
 // ---------------------------------------------------------------------------
 // K1: workgroup (tile of rows, group y).  Group y = t*Gk + q (y < T*Gk) owns
-// the slots of token t with ranks q, q + Gk, q + 2Gk, ... (at most four): every
-// wave runs the token's top-k extraction itself and issues the loads of a slot
+// the slots of token t with ranks q, q + Gk, ... (at most kT1SlotsPerGroup):
+// every wave runs the token's top-k extraction itself and issues the loads of a slot
 // right after the round that names its expert, so the weight traffic of the
 // early slots overlaps the remaining rounds; the dot products then consume the
 // slots in issue order.  Each (token, slot) pair streams its own expert rows:
 // in a 3-token window nearly all 24 experts are distinct, so sharing loads
-// between tokens would save little.  Groups T*Gk .. T*Gk + ceil(T/4) - 1 (when
+// between tokens would save little.  Two slots per group give about two waves
+// per SIMD at one token (640 workgroups of 4 waves for top-8), so the dot
+// products of one wave overlap the extraction rounds of another; the
+// extraction itself is repeated by every wave.  Groups T*Gk .. T*Gk + ceil(T/4) - 1 (when
 // the layer has a shared expert) each run it for 4 tokens against one load of
-// its rows; the last group is one workgroup that publishes the routing (and
-// the table for K2).
+// its rows.  Grid row 0 holds one more workgroup that publishes the routing
+// (and the table for K2); the groups take rows 1 and up.
 // ---------------------------------------------------------------------------
-constexpr int kT1SlotsPerGroup = 4;
+constexpr int kT1SlotsPerGroup = 2;
 
 template <int NB, int V, int TT>
 __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_kernel(DecArgs a, int Gk) {
     using S = K1Shape<NB, 1>;
     constexpr int SM = kT1SlotsPerGroup;
-    static_assert(SM >= TT && TT <= kShTok, "s_part holds SM slots");
-    const int y = blockIdx.y;
+    static_assert(TT <= kShTok, "shared-expert groups of at most kShTok tokens");
+    constexpr int SP = SM > TT ? SM : TT;   // slots or tokens whose partial sums s_part holds
+    // row 0 of the grid publishes (dispatched first, so it never waits for a
+    // free slot behind the streaming workgroups); rows 1.. stream
+    const int y = (int)blockIdx.y - 1;
     const int Gr = a.T * Gk;
-    const int n_sh = a.has_shared ? (a.T + kShTok - 1) / kShTok : 0;
-    const int y_pub = Gr + n_sh;
-    if (y == y_pub) {
+    if (y < 0) {
         __shared__ DecRoute R;
         if (blockIdx.x != 0) return;
         dec_route<V>(a.logits, a.T, a.E, a.k, a.renorm, R);
@@ -322,13 +353,14 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
         for (int i = threadIdx.x; i < (int)(sizeof(DecRoute) / 4); i += blockDim.x) a.route_tab[i] = src[i];
         return;
     }
-    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * SM * S::P * S::GROUPS)];
+    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * SP * S::P * S::GROUPS)];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int unit = wave / S::W;
     const int f = (wave % S::W) * kWave + lane;
     const int rr = f / S::SLICES;
     const int sl = f % S::SLICES;
     const int b = sl >> 3, part = sl & 7;
+    const SliceKit kit = slice_kit(part);
     const int clo = 256 * b + q4k_slice_col_lo(part);
     const int chi = 256 * b + q4k_slice_col_hi(part);
     const int i = blockIdx.x * S::ROWS + unit * S::P + rr;
@@ -389,18 +421,21 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
         sxl[0] += xl[0][j];
         sxh[0] += xh[0][j];
     }
+    // h values of the slots, stored after the last slot: a store between the
+    // slots would make the later loads wait for its completion
+    float hv[SM];
 #pragma unroll
     for (int m = 0; m < SM; ++m) {
+        hv[m] = 0.f;
         const int jt = q + m * Gk;
         if (jt >= a.k) continue;
-        const int hrow = tok * a.k + jt;
         float pg[1], pu[1];
-        q4k_slice_dot<1>(hg[m], qg[m], part, 1, xl, xh, sxl, sxh, pg);
-        q4k_slice_dot<1>(hu[m], qu[m], part, 1, xl, xh, sxl, sxh, pu);
+        q4k_slice_dot<1>(hg[m], qg[m], kit, 1, xl, xh, sxl, sxh, pg);
+        q4k_slice_dot<1>(hu[m], qu[m], kit, 1, xl, xh, sxl, sxh, pu);
         if constexpr (S::IN_WAVE) {
             pg[0] = segment_sum<S::SLICES>(pg[0]);
             pu[0] = segment_sum<S::SLICES>(pu[0]);
-            if (sl == S::SLICES - 1 && i < a.I) a.h[(int64_t)hrow * a.I + i] = silu_f32(pg[0]) * pu[0];
+            hv[m] = silu_f32(pg[0]) * pu[0];
         } else {
             pg[0] = segment_sum<16>(pg[0]);
             pu[0] = segment_sum<16>(pu[0]);
@@ -411,7 +446,15 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
             }
         }
     }
-    if constexpr (!S::IN_WAVE) {
+    if constexpr (S::IN_WAVE) {
+        if (sl == S::SLICES - 1 && i < a.I) {
+#pragma unroll
+            for (int m = 0; m < SM; ++m) {
+                const int jt = q + m * Gk;
+                if (jt < a.k) a.h[(int64_t)(tok * a.k + jt) * a.I + i] = hv[m];
+            }
+        }
+    } else {
         __syncthreads();
         // one thread per (slot, row): the row's 16-lane group sums in order
         for (int job = threadIdx.x; job < SM * S::P; job += blockDim.x) {
@@ -461,6 +504,7 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
     __syncthreads();
     const int n_slots = P + (a.has_shared ? T : 0);
     const int rr = lane / NS, sl = lane % NS;
+    const SliceKit kit = slice_kit(sl & 7);   // used by the Q4_K rows
     int c_lo, c_hi;
     if constexpr (QD == kQ4_K) {
         c_lo = 256 * (sl >> 3) + q4k_slice_col_lo(sl & 7);
@@ -546,7 +590,7 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
             for (int ps = 0; ps < kK2Passes; ++ps) {
                 float acc[1];
                 if constexpr (QD == kQ4_K) {
-                    q4k_slice_dot<1>(w0[m][ps], w1[m][ps], sl & 7, 1, hl, hh, shl, shh, acc);
+                    q4k_slice_dot<1>(w0[m][ps], w1[m][ps], kit, 1, hl, hh, shl, shh, acc);
                 } else {
                     const uint32_t dw[9] = {w0[m][ps].x, w0[m][ps].y, w0[m][ps].z, w0[m][ps].w,
                                             w1[m][ps].x, w1[m][ps].y, w1[m][ps].z, w1[m][ps].w, w2[m][ps]};

@@ -24,77 +24,115 @@ __device__ __forceinline__ float key_value(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// One wave selects the top-k of one token's E logits (E <= 64 * V) and
-// computes the routing weights.  Lane l owns experts l, l+64, ...  Returns, in
-// lane j < k, the expert of slot j and its weight; other lanes get -1 / 0.
-//
-// k rounds of extraction: a DPP wave maximum of the order-preserving keys of
-// the experts not yet taken, then ballots find the lowest expert index holding
-// that key (ties go to the lower index), and its owner lane drops it (key 0
-// marks taken or absent experts; real keys are >= 1).  Rounds produce the
-// slots directly in descending-logit order.  No LDS traffic.
+// Extraction engine: one wave, the E (<= 64*V) logits of one token, lane l
+// owning experts l, l+64, ...  Each lane caches the largest key it still holds
+// (best) and the lowest v holding it (bv), so a round is one DPP wave maximum
+// of best, a ballot, and a readlane of the winner's bv; only the winning lane
+// then rescans its V keys.  Ties: equal keys resolve to the lower expert index
+// (lower v first, since e = lane + 64*v, then the lower lane).  Key 0 marks
+// taken or absent experts; real keys are >= 1.  Rounds return the slots in
+// descending-logit order.  No LDS traffic.
 template <int V>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, int k, bool renorm, int& out_e,
-                                          float& out_w) {
-    const int lane = threadIdx.x & (kWave - 1);
+struct WaveExtract {
     uint32_t key[V];
-    float xv[V];
-    bool bad = false;
+    uint32_t best;
+    int bv;
+    __device__ __forceinline__ void refresh() {
+        best = key[0];
 #pragma unroll
-    for (int v = 0; v < V; ++v) {   // unconditional loads (clamped index): all in flight at once
-        const int e = lane + kWave * v;
-        xv[v] = lg[e < E ? e : E - 1];
-    }
+        for (int v = 1; v < V; ++v) best = max(best, key[v]);
+        bv = V - 1;
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-        const int e = lane + kWave * v;
-        bad |= e < E && !isfinite(xv[v]);
-        key[v] = e < E ? max(order_key(xv[v]), 1u) : 0u;
+        for (int v = V - 2; v >= 0; --v)
+            if (key[v] == best) bv = v;
     }
-    if (__any(bad)) {
-        if (lane == 0) raise_error(kErrLogitNonFinite);
-    }
-    int my_e = -1;
-    float my_l = 0.0f, top = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        uint32_t b = key[0];
+    // Loads the logits (clamped index, all loads in flight at once) and keys
+    // them.  Returns true in lanes that hold a non-finite logit.
+    __device__ __forceinline__ bool load(const float* __restrict__ lg, int E, float (&xv)[V]) {
+        const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-        for (int v = 1; v < V; ++v) b = max(b, key[v]);
-        const uint32_t M = wave_max_u32(b);
-        int wv = V, wl = 0;
-        const uint64_t lanes = __ballot(b == M);
+        for (int v = 0; v < V; ++v) {
+            const int e = lane + kWave * v;
+            xv[v] = lg[e < E ? e : E - 1];
+        }
+        bool bad = false;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int e = lane + kWave * v;
+            bad |= e < E && !isfinite(xv[v]);
+            key[v] = e < E ? max(order_key(xv[v]), 1u) : 0u;
+        }
+        refresh();
+        return bad;
+    }
+    __device__ __forceinline__ void load(const float* __restrict__ lg, int E) {
+        float xv[V];
+        (void)load(lg, E, xv);
+    }
+    // The expert of the next slot; M receives its key.
+    __device__ __forceinline__ int next(uint32_t& M) {
+        const int lane = threadIdx.x & (kWave - 1);
+        M = wave_max_u32(best);
+        const uint64_t lanes = __ballot(best == M);
+        int wl, wv;
         if (__popcll(lanes) == 1) {
-            // one lane holds the maximum: its lowest v holding it is the lowest index
             wl = (int)__builtin_ctzll(lanes);
-            int vl = V;
-#pragma unroll
-            for (int v = V - 1; v >= 0; --v)
-                if (key[v] == M) vl = v;
-            wv = __builtin_amdgcn_readlane(vl, wl);
+            wv = __builtin_amdgcn_readlane(bv, wl);
         } else {
+            // the key is held by several lanes: the lowest v, then the lowest lane
+            wv = V;
+            wl = 0;
 #pragma unroll
-            for (int v = V - 1; v >= 0; --v) {   // the lowest v with a match wins; then its lowest lane
-                const uint64_t msk = __ballot(key[v] == M);
+            for (int v = V - 1; v >= 0; --v) {
+                const uint64_t msk = __ballot(best == M && bv == v);
                 if (msk != 0ull) {
                     wv = v;
                     wl = (int)__builtin_ctzll(msk);
                 }
             }
         }
+        if (lane == wl) {
 #pragma unroll
-        for (int v = 0; v < V; ++v)
-            if (v == wv && lane == wl) key[v] = 0u;
+            for (int v = 0; v < V; ++v)
+                if (v == wv) key[v] = 0u;
+            refresh();
+        }
+        return wl + kWave * wv;
+    }
+    __device__ __forceinline__ int next() {
+        uint32_t M;
+        return next(M);
+    }
+};
+
+// One wave selects the top-k of one token's E logits and computes the routing
+// weights.  Returns, in lane j < k, the expert of slot j and its weight; other
+// lanes get -1 / 0.  Raises kErrLogitNonFinite for a NaN or infinite logit.
+template <int V>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, int k, bool renorm, int& out_e,
+                                          float& out_w) {
+    const int lane = threadIdx.x & (kWave - 1);
+    WaveExtract<V> ex;
+    float xv[V];
+    if (__any(ex.load(lg, E, xv))) {
+        if (lane == 0) raise_error(kErrLogitNonFinite);
+    }
+    int my_e = -1;
+    float my_l = 0.0f, top = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        uint32_t M;
+        const int e = ex.next(M);
         const float val = key_value(M);
         if (j == 0) top = val;
         if (lane == j) {
-            my_e = wl + kWave * wv;
+            my_e = e;
             my_l = val;
         }
     }
     if (renorm) {
-        const float ex = (lane < k) ? expf(my_l - top) : 0.0f;
-        const float sum = wave_sum(ex);
-        out_w = (lane < k) ? ex / sum : 0.0f;
+        const float ex2 = (lane < k) ? expf(my_l - top) : 0.0f;
+        const float sum = wave_sum(ex2);
+        out_w = (lane < k) ? ex2 / sum : 0.0f;
     } else {
         float part = 0.0f;
 #pragma unroll
@@ -107,57 +145,6 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, i
     }
     out_e = my_e;
 }
-
-// Incremental form of the extraction for callers that act between rounds:
-// load the keys once, then each next() returns the next slot's expert.
-template <int V>
-struct WaveExtract {
-    uint32_t key[V];
-    __device__ __forceinline__ void load(const float* __restrict__ lg, int E) {
-        const int lane = threadIdx.x & (kWave - 1);
-        float xv[V];
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const int e = lane + kWave * v;
-            xv[v] = lg[e < E ? e : E - 1];
-        }
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const int e = lane + kWave * v;
-            key[v] = e < E ? max(order_key(xv[v]), 1u) : 0u;
-        }
-    }
-    __device__ __forceinline__ int next() {
-        const int lane = threadIdx.x & (kWave - 1);
-        uint32_t b = key[0];
-#pragma unroll
-        for (int v = 1; v < V; ++v) b = max(b, key[v]);
-        const uint32_t M = wave_max_u32(b);
-        int wv = V, wl = 0;
-        const uint64_t lanes = __ballot(b == M);
-        if (__popcll(lanes) == 1) {
-            wl = (int)__builtin_ctzll(lanes);
-            int vl = V;
-#pragma unroll
-            for (int v = V - 1; v >= 0; --v)
-                if (key[v] == M) vl = v;
-            wv = __builtin_amdgcn_readlane(vl, wl);
-        } else {
-#pragma unroll
-            for (int v = V - 1; v >= 0; --v) {
-                const uint64_t msk = __ballot(key[v] == M);
-                if (msk != 0ull) {
-                    wv = v;
-                    wl = (int)__builtin_ctzll(msk);
-                }
-            }
-        }
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-            if (v == wv && lane == wl) key[v] = 0u;
-        return wl + kWave * wv;
-    }
-};
 
 // Values per lane for E experts (the kernels are instantiated for 4, 8, 16).
 inline int topk_vpl(int E) { return E <= 256 ? 4 : (E <= 512 ? 8 : 16); }
