@@ -69,34 +69,26 @@ struct WaveExtract {
         float xv[V];
         (void)load(lg, E, xv);
     }
-    // The expert of the next slot; M receives its key.
+    // The expert of the next slot; M receives its key.  Branch-free except for
+    // the rare case of a key held by several lanes.
     __device__ __forceinline__ int next(uint32_t& M) {
         const int lane = threadIdx.x & (kWave - 1);
         M = wave_max_u32(best);
         const uint64_t lanes = __ballot(best == M);
-        int wl, wv;
-        if (__popcll(lanes) == 1) {
-            wl = (int)__builtin_ctzll(lanes);
-            wv = __builtin_amdgcn_readlane(bv, wl);
-        } else {
-            // the key is held by several lanes: the lowest v, then the lowest lane
-            wv = V;
-            wl = 0;
-#pragma unroll
-            for (int v = V - 1; v >= 0; --v) {
-                const uint64_t msk = __ballot(best == M && bv == v);
-                if (msk != 0ull) {
-                    wv = v;
-                    wl = (int)__builtin_ctzll(msk);
-                }
-            }
+        int wl = (int)__builtin_ctzll(lanes);
+        int wv = __builtin_amdgcn_readlane(bv, wl);
+        if (__popcll(lanes) != 1) {
+            // the lowest (v, lane) among the lanes holding M: a wave minimum of
+            // 64*v + lane over those lanes
+            const uint32_t cand = best == M ? (uint32_t)(kWave * bv + lane) : 0xFFFFFFFFu;
+            const uint32_t c = ~wave_max_u32(~cand);
+            wl = (int)(c & (kWave - 1));
+            wv = (int)(c / kWave);
         }
-        if (lane == wl) {
+        const bool mine = lane == wl;
 #pragma unroll
-            for (int v = 0; v < V; ++v)
-                if (v == wv) key[v] = 0u;
-            refresh();
-        }
+        for (int v = 0; v < V; ++v) key[v] = (mine && v == wv) ? 0u : key[v];
+        refresh();
         return wl + kWave * wv;
     }
     __device__ __forceinline__ int next() {
