@@ -383,11 +383,15 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
     }
 
     const int tok = y / Gk, q = y - tok * Gk;
-    // activations and logits first (they do not depend on the routing)
+    // logits, then activations (neither depends on the routing): the logits
+    // gate the extraction rounds, the activations are needed only once the
+    // weights arrive, so they load behind the logits
+    WaveExtract<V> ex;
+    float xv[V];
+    ex.issue(a.logits + (int64_t)tok * a.E, a.E, xv);
     float4 xl4[1][4], xh4[1][4];
     load_x_slice<1>(a, tok, clo, chi, xl4[0], xh4[0]);
-    WaveExtract<V> ex;
-    ex.load(a.logits + (int64_t)tok * a.E, a.E);
+    (void)ex.keys(a.E, xv);
     uint4 hg[SM], qg[SM], hu[SM], qu[SM];
     auto issue = [&](int m, int e) {
         const uint8_t* gr = a.gate.data + (int64_t)e * a.gate.expert_bytes + (int64_t)ic * a.gate.row_bytes +

@@ -46,28 +46,36 @@ struct WaveExtract {
         for (int v = V - 2; v >= 0; --v)
             if (key[v] == best) bv = v;
     }
-    // Loads the logits (clamped index, all loads in flight at once) and keys
-    // them.  Returns true in lanes that hold a non-finite logit.
-    __device__ __forceinline__ bool load(const float* __restrict__ lg, int E, float (&xv)[V]) {
+    // Issues the logit loads (clamped index, all in flight at once).
+    __device__ __forceinline__ void issue(const float* __restrict__ lg, int E, float (&xv)[V]) {
         const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int e = lane + kWave * v;
             xv[v] = lg[e < E ? e : E - 1];
         }
+    }
+    // Loads the logits and keys them.  Returns true in lanes that hold a
+    // non-finite logit.
+    __device__ __forceinline__ bool load(const float* __restrict__ lg, int E, float (&xv)[V]) {
+        issue(lg, E, xv);
+        return keys(E, xv);
+    }
+    // Keys the issued logits (waits for them).
+    __device__ __forceinline__ bool keys(int E, const float (&xv)[V]) {
+        const int lane = threadIdx.x & (kWave - 1);
         bool bad = false;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            const int e = lane + kWave * v;
-            bad |= e < E && !isfinite(xv[v]);
-            key[v] = e < E ? max(order_key(xv[v]), 1u) : 0u;
+            // no short-circuit: a branch here lets the compiler move the
+            // load of v into it, behind later loads
+            const bool in = lane + kWave * v < E;
+            const uint32_t kk = max(order_key(xv[v]), 1u);
+            bad |= in & !isfinite(xv[v]);
+            key[v] = in ? kk : 0u;
         }
         refresh();
         return bad;
-    }
-    __device__ __forceinline__ void load(const float* __restrict__ lg, int E) {
-        float xv[V];
-        (void)load(lg, E, xv);
     }
     // The expert of the next slot; M receives its key.  Branch-free except for
     // the rare case of a key held by several lanes.
