@@ -31,6 +31,8 @@
 // lane issues two 16-byte loads (super-block header + quants), decodes the two
 // 6-bit scale/min pairs it needs and applies them once per 16 weights:
 //   partial = d*(sc_lo*S_lo + sc_hi*S_hi) - dmin*(m_lo*X_lo + m_hi*X_hi).
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "qblock.h"
@@ -318,7 +320,7 @@ __device__ __forceinline__ void load_x_slice(const DecArgs& a, int tok, int clo,
 
 // ---------------------------------------------------------------------------
 // K1: workgroup (tile of rows, group y).  Group y = t*Gk + q (y < T*Gk) owns
-// the slots of token t with ranks q, q + Gk, ... (at most kT1SlotsPerGroup):
+// the slots of token t with ranks q, q + Gk, ... (at most SM):
 // every wave runs the token's top-k extraction itself and issues the loads of a slot
 // right after the round that names its expert, so the weight traffic of the
 // early slots overlaps the remaining rounds; the dot products then consume the
@@ -332,12 +334,9 @@ __device__ __forceinline__ void load_x_slice(const DecArgs& a, int tok, int clo,
 // its rows.  Grid row 0 holds one more workgroup that publishes the routing
 // (and the table for K2); the groups take rows 1 and up.
 // ---------------------------------------------------------------------------
-constexpr int kT1SlotsPerGroup = 2;
-
-template <int NB, int V, int TT>
+template <int NB, int V, int TT, int SM>
 __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_kernel(DecArgs a, int Gk) {
     using S = K1Shape<NB, 1>;
-    constexpr int SM = kT1SlotsPerGroup;
     static_assert(TT <= kShTok, "shared-expert groups of at most kShTok tokens");
     constexpr int SP = SM > TT ? SM : TT;   // slots or tokens whose partial sums s_part holds
     // row 0 of the grid publishes (dispatched first, so it never waits for a
@@ -480,20 +479,22 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
 // ---------------------------------------------------------------------------
 // K2: down + combine.  A "slice" of a down row is 16 quant bytes of a Q4_K
 // super-block (32 weights) or one 34-byte Q8_0 block (32 weights); NS slices
-// per row, 64/NS rows per wave pass, kK2Passes passes per workgroup.  Slots
+// per row, 64/NS rows per wave pass, PS passes per workgroup.  Slots
 // are the (token, rank) pairs p = t*k + j (expert sel[p], h row p) and, with a
 // shared expert, one slot per token t (h row T*k + t).  Each wave takes SM
 // slots at a time with all their weight and activation loads in flight
 // together (the launcher uses SM = 1); results go to LDS and the combine is
 // formed in slot order.
 // ---------------------------------------------------------------------------
-constexpr int kK2Passes = 2;
+constexpr int kK2MinPasses = 2;   // passes per workgroup: enough to cover H with
+constexpr int kK2MaxPasses = 3;   // about one workgroup per CU
+constexpr int kDecCUs = 256;      // compute units of an MI355X
 constexpr int kK2MaxThreads = 1024;
 
-template <int QD, int NS, int SM, int V>
+template <int QD, int NS, int SM, int PS>
 __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
     constexpr int RP = kWave / NS;              // rows per wave pass
-    constexpr int RO = RP * kK2Passes;          // output rows of the workgroup
+    constexpr int RO = RP * PS;                 // output rows of the workgroup
     __shared__ DecRoute R;
     __shared__ float s_y[(kDecMaxPairs + kDecMaxT) * RO];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -543,12 +544,12 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
             hrow[m] = live[m] ? u : 0;   // the h row of slot u is u
         }
         // all weight loads, then the h loads
-        uint4 w0[SM][kK2Passes], w1[SM][kK2Passes];
-        uint32_t w2[SM][kK2Passes];
+        uint4 w0[SM][PS], w1[SM][PS];
+        uint32_t w2[SM][PS];
 #pragma unroll
         for (int m = 0; m < SM; ++m) {
 #pragma unroll
-            for (int ps = 0; ps < kK2Passes; ++ps) {   // dead slots load expert 0's rows, never used
+            for (int ps = 0; ps < PS; ++ps) {   // dead slots load expert 0's rows, never used
                 w2[m][ps] = 0;
                 const int o = o0 + ps * RP + rr;
                 const int oc = o < a.H ? o : a.H - 1;
@@ -591,7 +592,7 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
                 shh[0] += hh[0][j];
             }
 #pragma unroll
-            for (int ps = 0; ps < kK2Passes; ++ps) {
+            for (int ps = 0; ps < PS; ++ps) {
                 float acc[1];
                 if constexpr (QD == kQ4_K) {
                     q4k_slice_dot<1>(w0[m][ps], w1[m][ps], kit, 1, hl, hh, shl, shh, acc);
@@ -644,14 +645,58 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 
+// Workgroups of a K1 instance that the current device holds at once (per-CU
+// occupancy times CUs), looked up once per instance and device; 0 if unknown.
+constexpr int kDecMaxDevices = 64;
+
+template <int NB, int V, int TT, int SM>
+int k1_capacity() {
+    static std::atomic<int> cap[kDecMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDecMaxDevices) return 0;
+    int c = cap[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dec_gateup_pipe_kernel<NB, V, TT, SM>,
+                                                         K1Shape<NB, 1>::THREADS, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        c = per_cu * cus;
+        cap[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+template <int NB, int V, int TT, int SM>
+int k1_grid_rows(const DecArgs& a, int& Gk) {
+    Gk = (a.k + SM - 1) / SM;                                         // groups per token
+    const int n_sh = a.has_shared ? (a.T + kShTok - 1) / kShTok : 0;  // shared-expert groups
+    return a.T * Gk + n_sh + 1;
+}
+
+template <int NB, int V, int TT, int SM>
+hipError_t launch_k1_sm(const DecArgs& a, hipStream_t s) {
+    using S = K1Shape<NB, 1>;
+    int Gk;
+    const int rows = k1_grid_rows<NB, V, TT, SM>(a, Gk);
+    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, rows);
+    dec_gateup_pipe_kernel<NB, V, TT, SM><<<grid, S::THREADS, 0, s>>>(a, Gk);
+    return hipGetLastError();
+}
+
+// Slots per group: the fewest of 2, 3, 4 whose grid the device holds at once.
+// Fewer slots per wave shorten each wave's dot products and let waves of one
+// SIMD overlap, but a grid that needs a second round of workgroups ends a
+// whole workgroup duration later (the 3-token window at two slots: 1,664
+// workgroups for 1,024 places).
 template <int NB, int V, int TT>
 hipError_t launch_k1_pipe(const DecArgs& a, hipStream_t s) {
     using S = K1Shape<NB, 1>;
-    const int Gk = (a.k + kT1SlotsPerGroup - 1) / kT1SlotsPerGroup;   // groups per token
-    const int n_sh = a.has_shared ? (a.T + kShTok - 1) / kShTok : 0;  // shared-expert groups
-    dim3 grid((a.I + S::ROWS - 1) / S::ROWS, a.T * Gk + n_sh + 1);
-    dec_gateup_pipe_kernel<NB, V, TT><<<grid, S::THREADS, 0, s>>>(a, Gk);
-    return hipGetLastError();
+    const int cols = (a.I + S::ROWS - 1) / S::ROWS;
+    int Gk;
+    if (cols * k1_grid_rows<NB, V, TT, 2>(a, Gk) <= k1_capacity<NB, V, TT, 2>()) return launch_k1_sm<NB, V, TT, 2>(a, s);
+    if (cols * k1_grid_rows<NB, V, TT, 3>(a, Gk) <= k1_capacity<NB, V, TT, 3>()) return launch_k1_sm<NB, V, TT, 3>(a, s);
+    return launch_k1_sm<NB, V, TT, 4>(a, s);
 }
 
 template <int NB, int V>
@@ -669,24 +714,28 @@ hipError_t launch_k1(const DecArgs& a, hipStream_t s) {
     return launch_k1_v<NB, 16>(a, s);
 }
 
-template <int QD, int NS, int V>
-hipError_t launch_k2v(const DecArgs& a, hipStream_t s) {
-    constexpr int RO = (kWave / NS) * kK2Passes;
+template <int QD, int NS, int PS>
+hipError_t launch_k2p(const DecArgs& a, hipStream_t s) {
+    constexpr int RO = (kWave / NS) * PS;
     const int slots = a.T * a.k + (a.has_shared ? a.T : 0);
     const int max_waves = kK2MaxThreads / kWave;
     // one slot per wave in flight (more spill at this workgroup size); slots
     // beyond 16 take a second round on some waves
     const int waves = slots < 4 ? 4 : (slots > max_waves ? max_waves : slots);
-    dec_down_kernel<QD, NS, 1, V><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
+    dec_down_kernel<QD, NS, 1, PS><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
     return hipGetLastError();
 }
 
+// Passes per workgroup: the fewest (at least two) that cover H in about one
+// workgroup per CU, so no CU takes a second workgroup while others idle
+// (H = 2,560 with 4-row passes: 214 workgroups of 3 passes, not 320 of 2).
 template <int QD, int NS>
 hipError_t launch_k2(const DecArgs& a, hipStream_t s) {
-    const int vpl = topk_vpl(a.E);
-    if (vpl == 4) return launch_k2v<QD, NS, 4>(a, s);
-    if (vpl == 8) return launch_k2v<QD, NS, 8>(a, s);
-    return launch_k2v<QD, NS, 16>(a, s);
+    constexpr int RP = kWave / NS;
+    const int groups = (a.H + RP - 1) / RP;
+    int ps = (groups + kDecCUs - 1) / kDecCUs;
+    ps = ps < kK2MinPasses ? kK2MinPasses : (ps > kK2MaxPasses ? kK2MaxPasses : ps);
+    return ps == 2 ? launch_k2p<QD, NS, 2>(a, s) : launch_k2p<QD, NS, 3>(a, s);
 }
 
 }  // namespace
