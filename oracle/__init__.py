@@ -60,6 +60,7 @@ def _load():
     lib.orc_q4k_dequant.argtypes = [P, i64, P]
     lib.orc_q80_dequant.argtypes = [P, i64, P]
     lib.orc_route_topk.argtypes = [P, i32, i32, i32, i32, P, P]
+    lib.orc_router_logits.argtypes = [P, i32, i32, P, i32, P]
     lib.orc_bucket.argtypes = [P, i32, i32, i32, P, P, P, P, P]
     lib.orc_quant_act_f32.argtypes = [P, i32, i32, P, P]
     lib.orc_silu.argtypes = [ctypes.c_double]
@@ -137,6 +138,21 @@ def q80_dequant(blocks) -> np.ndarray:
 
 def dequant(blocks, qtype: int) -> np.ndarray:
     return q4k_dequant(blocks) if qtype == Q4_K else q80_dequant(blocks)
+
+
+def router_logits(x, w_router) -> np.ndarray:
+    """Router projection (R-router in moe_oracle.c; "Strata - the details",
+    "How it works": routers are a GPU stage): fp32 x [T][H] and fp32 W [E][H]
+    -> fp64 logits [T][E], each a sequential fp64 sum over h."""
+    lib = _load()
+    xa = np.ascontiguousarray(x, dtype=np.float32)
+    wa = np.ascontiguousarray(w_router, dtype=np.float32)
+    T, H = xa.shape
+    E, H2 = wa.shape
+    assert H == H2
+    out = np.empty((T, E), dtype=np.float64)
+    lib.orc_router_logits(_ptr(xa), T, H, _ptr(wa), E, _ptr(out))
+    return out
 
 
 def route_topk(logits, k: int, renorm: bool = True):

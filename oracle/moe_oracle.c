@@ -40,6 +40,10 @@
  *            silu(g) = g / (1 + exp(-g)).
  *  R-combine out_t = sum_j w_tj * y_tj (slot order) + s_t * y_shared_t; no
  *            residual, norm or bias.
+ *  R-router  router logits are a plain projection of the token's hidden
+ *            state by an fp32 [E][H] router matrix: logit_e = sum_h W[e][h]
+ *            x[h], no bias ("Strata - the details", "How it works": routers
+ *            are a GPU stage; their weights live in VRAM).
  *  R-quant   activations quantized once per token, per 256-wide block:
  *            amax = max|x|; amax == 0 gives d = 0, q = 0; otherwise
  *            id = 127/amax, q = rint(x*id) (ties to even) clamped to +-127,
@@ -185,6 +189,22 @@ static void dequant_row(const uint8_t* row, int qtype, int cols, double* out) {
         orc_q4k_dequant(row, nb, out);
     else
         orc_q80_dequant(row, nb, out);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Router projection (R-router): x fp32 [T][H], W fp32 [E][H] -> fp64 [T][E] */
+/* logits, each a sequential fp64 sum over h.                                */
+/* ------------------------------------------------------------------------- */
+void orc_router_logits(const float* x, int32_t T, int32_t H, const float* W, int32_t E, double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t te = 0; te < (int64_t)T * E; ++te) {
+        const int64_t t = te / E, e = te % E;
+        const float* xr = x + t * H;
+        const float* wr = W + e * H;
+        double acc = 0.0;
+        for (int32_t h = 0; h < H; ++h) acc += (double)wr[h] * (double)xr[h];
+        out[te] = acc;
+    }
 }
 
 /* ------------------------------------------------------------------------- */
