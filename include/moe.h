@@ -135,6 +135,19 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
                           const moe_routing* r, void* workspace, size_t ws_bytes,
                           hipStream_t stream);
 
+/* Router projection, the GPU stage in front of the top-k ("Strata - the
+ * details", "How it works": routers run on the GPU with their weights in
+ * VRAM):  logits[t][e] = sum_h w_router[e][h] * x[t][h], no bias.
+ * x fp32 [T][H], w_router fp32 [E][H] (rows contiguous), logits fp32 [T][E];
+ * all device pointers owned by the caller.  Sums are fp32 in a fixed order:
+ * up to 16 tokens a matrix-vector kernel, above that fp32 MFMA tiles of 32
+ * tokens x 32 experts.  Bitwise deterministic; within each of the two kernels
+ * a token's logits depend on its own row only (the kernel follows from T).
+ * Checks: T >= 1; 1 <= E <= 1024; 8 <= H <= 8192, H % 8 == 0; x and w_router
+ * 16-byte aligned, logits 4-byte aligned. */
+moe_status moe_router_logits(const float* x, int32_t T, int32_t H, const float* w_router, int32_t E,
+                             float* logits, hipStream_t stream);
+
 /* Per-token int8 activation quantisation, once per token and 256-wide block
  * (the "one quantization per token" of the Sage-A1.5 card's round-2 table):
  * amax = max|x|; amax == 0 gives d = 0 and q = 0; otherwise id = 127/amax

@@ -7,7 +7,7 @@ kernels.  There is no CPU fallback: if ``libmoe.so`` is missing or cannot be
 loaded, the first call raises.
 
 Entry points keep the C names: ``moe_route_topk``, ``moe_quantize_act``,
-``moe_expert_ffn_q``, ``moe_combine``, ``moe_forward``, ``moe_dequant_q``,
+``moe_router_logits``, ``moe_expert_ffn_q``, ``moe_combine``, ``moe_forward``, ``moe_dequant_q``,
 ``moe_check_device_errors``, ``moe_last_error``, ``moe_abi_version``,
 ``moe_route_workspace_bytes``, ``moe_ffn_workspace_bytes``,
 ``moe_forward_workspace_bytes``.
@@ -36,6 +36,7 @@ EXPORTS = (
     "moe_abi_version", "moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
     "moe_quantize_act", "moe_ffn_workspace_bytes", "moe_expert_ffn_q", "moe_combine",
     "moe_dequant_q", "moe_check_device_errors", "moe_forward_workspace_bytes", "moe_forward",
+    "moe_router_logits",
 )
 
 
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_route_topk.restype = st
     lib.moe_quantize_act.argtypes = [P, i32, i32, P, P, P]
     lib.moe_quantize_act.restype = st
+    lib.moe_router_logits.argtypes = [P, i32, i32, P, i32, P, P]
+    lib.moe_router_logits.restype = st
     lib.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer), i32, i32, u32]
     lib.moe_ffn_workspace_bytes.restype = sz
     lib.moe_expert_ffn_q.argtypes = [ctypes.POINTER(moe_layer), ctypes.POINTER(moe_routing), i32, i32, P, P, P,
@@ -198,6 +201,15 @@ def moe_route_topk(logits, k: int, routing: Routing, renorm: bool = True, worksp
     st = load_library().moe_route_topk(_ptr(logits), T, E, k, MOE_ROUTE_RENORM if renorm else 0,
                                        ctypes.byref(routing.struct()), _ptr(workspace), nbytes, _stream(stream))
     _check(st, "moe_route_topk")
+
+
+def moe_router_logits(x, w_router, logits, stream=None):
+    """logits[t][e] = sum_h w_router[e][h] * x[t][h] (fp32 device tensors)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    assert w_router.shape[1] == H and tuple(logits.shape) == (T, E)
+    _check(load_library().moe_router_logits(_ptr(x), T, H, _ptr(w_router), E, _ptr(logits), _stream(stream)),
+           "moe_router_logits")
 
 
 def moe_quantize_act(x, xq, xd, stream=None):

@@ -110,6 +110,10 @@ hipError_t launch_down(const FfnArgs& a, int hmode, hipStream_t s);
 hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s);
 
+constexpr int kRouterGemvMaxT = 16;   // router: tokens up to which the matrix-vector kernel runs
+constexpr int kRouterMaxH = 8192;     // router: largest hidden size
+hipError_t launch_router(const float* x, int T, int H, const float* w, int E, float* logits, hipStream_t s);
+
 hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s);
 hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared,
                           const float* shared_scale, int T, int k, int H, float* out, hipStream_t s);

@@ -2,6 +2,7 @@
 // one code object).  Each included file holds one stage of the path.
 #include "ffn_decode.hip"
 #include "route.hip"
+#include "router.hip"
 #include "quant.hip"
 #include "ffn_mfma.hip"
 #include "ffn_int8.hip"

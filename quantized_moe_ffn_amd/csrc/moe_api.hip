@@ -253,6 +253,19 @@ moe_status moe_quantize_act(const float* x, int32_t T, int32_t H, int8_t* xq, fl
     return from_hip(moe::launch_quantize_act(x, T, H, xq, xd, stream), "moe_quantize_act launch");
 }
 
+moe_status moe_router_logits(const float* x, int32_t T, int32_t H, const float* w_router, int32_t E,
+                             float* logits, hipStream_t stream) {
+    if (!x || !w_router || !logits) return fail(MOE_ERR_INVALID_ARGUMENT, "x, w_router or logits is NULL");
+    if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d: need at least one token", T);
+    if (E < 1 || E > kMaxExperts) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d: need 1..%d", E, kMaxExperts);
+    if (H < 8 || H % 8 != 0 || H > moe::kRouterMaxH)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "H = %d: must be a positive multiple of 8, at most %d", H,
+                    moe::kRouterMaxH);
+    if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(logits, 4))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "x and w_router must be 16-byte aligned, logits 4-byte aligned");
+    return from_hip(moe::launch_router(x, T, H, w_router, E, logits, stream), "moe_router_logits launch");
+}
+
 size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t flags) {
     if (!L || T < 1 || k < 1) return 0;
     return ffn_ws_layout(L, T, k, resolve_path(flags, T)).total;

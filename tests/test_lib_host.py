@@ -174,3 +174,21 @@ def test_workspace_sizes_cover_the_stages(T, flags, shape):
     assert fwd >= ffn + route + T * L.hidden + T * (L.hidden // 256) * 4
     if flags != 0:
         assert lib.moe_ffn_workspace_bytes(ctypes.byref(L), 2 * T, k, flags) >= ffn
+
+
+@pytest.mark.parametrize("T,H,E,msg", [
+    (0, 256, 8, "T = 0"), (1, 256, 0, "E = 0"), (1, 256, 2048, "E = 2048"), (1, 100, 8, "H = 100"),
+    (1, 16384, 8, "H = 16384"), (1, 0, 8, "H = 0"),
+])
+def test_router_rejects_bad_shapes(T, H, E, msg):
+    lib = qm.load_library()
+    st = lib.moe_router_logits(ctypes.c_void_p(256), T, H, ctypes.c_void_p(4096), E, ctypes.c_void_p(8192), None)
+    assert st == 1 and msg in qm.moe_last_error()
+
+
+def test_router_rejects_null_and_misaligned():
+    lib = qm.load_library()
+    st = lib.moe_router_logits(None, 1, 256, ctypes.c_void_p(4096), 8, ctypes.c_void_p(8192), None)
+    assert st == 1 and "NULL" in qm.moe_last_error()
+    st = lib.moe_router_logits(ctypes.c_void_p(264), 1, 256, ctypes.c_void_p(4096), 8, ctypes.c_void_p(8192), None)
+    assert st == 1 and "16-byte aligned" in qm.moe_last_error()
