@@ -61,6 +61,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", choices=["on", "off"], default="on", help="replay each step as a HIP graph")
+    ap.add_argument("--router", action="store_true",
+                    help="compute each layer's logits on the GPU from x and a seeded fp32 [E][H] router "
+                         "matrix (moe_router_logits) inside the timed step")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -101,11 +104,25 @@ def main() -> int:
             row.append((torch.from_numpy(lg).to(dev), torch.from_numpy(x).to(dev)))
         inputs.append(row)
     bufs = qm.LayerBuffers(stack[0].layer, T, k, flags, device=dev)
+    routers = None
+    if args.router:
+        # seeded N(0, 1/H) fp32 router rows, one matrix per layer; the logits of
+        # every layer call then come from the GPU router stage
+        routers = [torch.from_numpy((np.random.default_rng((0, l, 0x52)).standard_normal((E, H))
+                                     / np.sqrt(H)).astype(np.float32)).to(dev) for l in range(L)]
+        lgbuf = torch.empty((T, E), dtype=torch.float32, device=dev)
+        for r in range(R):
+            for l in range(L):
+                qm.moe_router_logits(inputs[r][l][1], routers[l], lgbuf)
+                inputs[r][l] = (lgbuf.clone(), inputs[r][l][1])
 
     def run_replay(r, stream):
         row = inputs[r]
         for l in range(L):
             lg, x = row[l]
+            if routers is not None:
+                qm.moe_router_logits(x, routers[l], lgbuf, stream)
+                lg = lgbuf
             qm.forward(stack[l].layer, lg, x, k, bufs, flags=flags, stream=stream)
 
     # unique experts per (replay, layer): algorithmic bytes of each layer call
@@ -120,6 +137,8 @@ def main() -> int:
     per_expert = w.expert_bytes()
     shared_bytes = w.expert_bytes() if w.shared else 0
     bytes_rl = uniq * per_expert + shared_bytes           # expert weight bytes each layer call streams
+    if routers is not None:
+        bytes_rl = bytes_rl + E * H * 4                   # and the router matrix
 
     graphs = None
     if args.graph == "on":
@@ -177,19 +196,23 @@ def main() -> int:
         achieved = ops / (avg_us / 1e6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profiles(w.name),
-                "kernel": "moe_forward (int8 path: route, quantize, gate/up, requantize, down, combine)",
+                "kernel": ("moe_router_logits + " if routers is not None else "") +
+                          "moe_forward (int8 path: route, quantize, gate/up, requantize, down, combine)",
                 "ops_per_launch": ops, "avg_launch_us": round(avg_us, 3)}
     else:
         achieved = dom_bytes / (ms_total / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(w.name),
-                "kernel": "moe_forward (decode: route+gate/up+SiLU kernel, down+combine kernel)",
+                "kernel": ("moe_router_logits + " if routers is not None else "") +
+                          "moe_forward (decode: route+gate/up+SiLU kernel, down+combine kernel)",
                 "bytes_per_launch": round(dom_bytes / n_launch), "avg_launch_us": round(avg_us, 3)}
     log("[bench] layer call: %.2f us, %s %s" % (avg_us, roof["achieved"], roof["unit"]))
 
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
+        # with --router the oracle takes the logits the GPU router produced
+        # (untimed, above) as its input
         cpu, parity = cpu_baseline(w, stack, inputs, bufs, flags, k, args.cpu_seconds)
 
     rec = {
@@ -208,7 +231,8 @@ def main() -> int:
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "inter": I,
                    "shared_expert": w.shared, "layers": L, "replays": R,
                    "formats": {"gate": fmt(w.qt_gate), "up": fmt(w.qt_up), "down": fmt(w.qt_down)},
-                   "parallelism": "single GPU", "graphs": args.graph},
+                   "parallelism": "single GPU", "graphs": args.graph,
+                   "router": "fp32 [E][H], moe_router_logits in the timed step" if routers is not None else None},
         "hbm_GBps_end_to_end": round(dom_bytes / (ms_total / 1e3) / 1e9, 1),
         "roofline": roof,
         "cpu_baseline": cpu,
