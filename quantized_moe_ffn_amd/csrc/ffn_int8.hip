@@ -42,12 +42,10 @@ hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s) {
         m.hs = a.hs;
         m.y_pair = a.y_pair;
         m.y_shared = a.y_shared;
-        const int mt = mfma_tile_rows(a.H, a.I);
         const size_t half = (mfma_tiles_bytes(a.T, a.k, a.E, a.has_shared, a.H, a.I) - 256) / 2;
         m.tile_e = a.tiles;
         m.tile_m0 = a.tiles + half / sizeof(int32_t);
         m.n_tiles = a.tiles + 2 * (half / sizeof(int32_t));
-        (void)mt;
         return launch_ffn_mfma(m, s);
     }
     hipError_t e = launch_gateup(a, 1, s);

@@ -27,7 +27,7 @@
 // Work.  A tile is (expert, 32*MTILES tokens of its bucket).  Gate/up:
 // workgroups of 8 waves take (tile, 256 rows of I); each wave owns 32 rows and
 // runs them through gate, then up (so SiLU(gate)*up and the requantisation of
-// h happen in registers).  Down: workgroups take (tile, up to 1024 rows of H),
+// h happen in registers).  Down: workgroups take (tile, 256 or 1024 rows of H),
 // each wave 32 rows per round.  The tile's int8 activations, their per-256
 // scales and per-32 sums sit in LDS for the whole K loop; weights stream from
 // global memory into registers one 256-block ahead of use.  Work items are
@@ -482,7 +482,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     }
 }
 
-constexpr int kDownRounds = 4;  // 256-row rounds per down workgroup
+constexpr int kDownRoundsMax = 4;  // 256-row rounds per down workgroup (large batches)
 
 template <int MTILES>
 __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
@@ -492,7 +492,8 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(16))) float s_sc[MT];
 
     const int H = a.H, I = a.I, nsb = I / 256;
-    const int NB = (H / 256 + kDownRounds - 1) / kDownRounds;
+    const int R = a.down_rounds;
+    const int NB = (H / 256 + R - 1) / R;
     int u, ob;
     if (!work_item(a.n_tiles, NB, u, ob)) return;
     const int e = a.tile_e[u], m0 = a.tile_m0[u];
@@ -511,8 +512,8 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     const int n = lane & 31, h = lane >> 5;
     const QMat D = shared ? a.sdown : a.down;
     const int64_t eo = shared ? 0 : (int64_t)e;
-    const int r0 = ob * kDownRounds;
-    const int nr = min(kDownRounds, H / 256 - r0);
+    const int r0 = ob * R;
+    const int nr = min(R, H / 256 - r0);
     const uint8_t* base = D.data + eo * D.expert_bytes + (int64_t)(r0 * 256 + wave * 32 + n) * D.row_bytes;
     const int64_t round_stride = 256 * D.row_bytes;
     const int npairs = a.T * a.k;
@@ -635,8 +636,14 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     const size_t lds_gu = std::max(tile_lds_bytes<MTILES>(a.H), (size_t)MT * kHStride * sizeof(float));
     gateup_mfma_kernel<MTILES><<<grid_for(maxt * (a.I / 256)), kMThreads, lds_gu, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int nb_down = (a.H / 256 + kDownRounds - 1) / kDownRounds;
-    down_mfma_kernel<MTILES><<<grid_for(maxt * nb_down), kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(a);
+    // rounds of 256 output rows per down workgroup: four amortise the tile's LDS
+    // load over 1,024 rows when there are work items to spare; small batches (a
+    // few tokens per expert, few tiles) take one round so that the grid covers
+    // the CUs
+    MfmaArgs d = a;
+    d.down_rounds = (int64_t)maxt * ((a.H / 256 + kDownRoundsMax - 1) / kDownRoundsMax) >= 1024 ? kDownRoundsMax : 1;
+    const int nb_down = (a.H / 256 + d.down_rounds - 1) / d.down_rounds;
+    down_mfma_kernel<MTILES><<<grid_for(maxt * nb_down), kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(d);
     return hipGetLastError();
 }
 
@@ -652,15 +659,20 @@ bool mfma_rows_fit(int T, int k, int H, int I) {
     return rows * (H > I ? H : I) < ((int64_t)1 << 31);
 }
 
-int mfma_tile_rows(int H, int I) { return (H <= 2048 && I <= 2048) ? 64 : 32; }
+// Tokens per tile: 64 when the LDS holds them (H, I <= 2048) and the experts
+// average more than 32 tokens; else 32, so a batch of a few tokens per expert
+// does not pay the MFMA and VALU work of 64 mostly empty rows.
+int mfma_tile_rows(int T, int k, int E, int H, int I) {
+    return (H <= 2048 && I <= 2048 && (int64_t)T * k > 32 * (int64_t)E) ? 64 : 32;
+}
 
 size_t mfma_tiles_bytes(int T, int k, int E, int has_shared, int H, int I) {
-    const int mt = mfma_tile_rows(H, I);
+    const int mt = mfma_tile_rows(T, k, E, H, I);
     return 2 * sizeof(int32_t) * (size_t)max_tiles(T, k, E, has_shared, mt) + 256;
 }
 
 hipError_t launch_ffn_mfma(const MfmaArgs& a, hipStream_t s) {
-    if (mfma_tile_rows(a.H, a.I) == 64) return launch_mfma_path<2>(a, s);
+    if (mfma_tile_rows(a.T, a.k, a.E, a.H, a.I) == 64) return launch_mfma_path<2>(a, s);
     return launch_mfma_path<1>(a, s);
 }
 

@@ -72,11 +72,12 @@ struct MfmaArgs {
     int32_t* tile_e;
     int32_t* tile_m0;
     int32_t* n_tiles;
+    int down_rounds;               // 256-row rounds per down workgroup (set by the launcher)
 };
 
 bool mfma_path_supported(int H, int I, int qg, int qu, int qd);
 bool mfma_rows_fit(int T, int k, int H, int I);
-int mfma_tile_rows(int H, int I);
+int mfma_tile_rows(int T, int k, int E, int H, int I);
 size_t mfma_tiles_bytes(int T, int k, int E, int has_shared, int H, int I);
 hipError_t launch_ffn_mfma(const MfmaArgs& a, hipStream_t s);
 
