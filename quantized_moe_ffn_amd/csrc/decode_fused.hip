@@ -481,9 +481,10 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
 // super-block (32 weights) or one 34-byte Q8_0 block (32 weights); NS slices
 // per row, 64/NS rows per wave pass, PS passes per workgroup.  Slots
 // are the (token, rank) pairs p = t*k + j (expert sel[p], h row p) and, with a
-// shared expert, one slot per token t (h row T*k + t).  Each wave takes SM
-// slots at a time with all their weight and activation loads in flight
-// together (the launcher uses SM = 1); results go to LDS and the combine is
+// shared expert, one slot per token t (h row T*k + t).  Each wave takes one
+// slot at a time, all PS passes of it, with its weight and activation loads in
+// flight together.  (Spreading a slot's passes over two waves, 16 waves for
+// top-8 at one token, measured slower.)  Results go to LDS and the combine is
 // formed in slot order.
 // ---------------------------------------------------------------------------
 constexpr int kK2MinPasses = 2;   // passes per workgroup: enough to cover H with
@@ -491,7 +492,7 @@ constexpr int kK2MaxPasses = 3;   // about one workgroup per CU
 constexpr int kDecCUs = 256;      // compute units of an MI355X
 constexpr int kK2MaxThreads = 1024;
 
-template <int QD, int NS, int SM, int PS>
+template <int QD, int NS, int PS>
 __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
     constexpr int RP = kWave / NS;              // rows per wave pass
     constexpr int RO = RP * PS;                 // output rows of the workgroup
@@ -519,105 +520,92 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
         c_hi = 32 * sl + 16;
     }
 
-    for (int base = wave; base < n_slots; base += nwaves * SM) {
-        int hrow[SM];
-        bool live[SM];
-        const uint8_t* Db[SM];
-        int64_t rowb[SM];
-#pragma unroll
-        for (int m = 0; m < SM; ++m) {
-            const int u = base + m * nwaves;
-            live[m] = u < n_slots;
-            const bool shared = live[m] && u >= P;
-            int e = 0;
-            if (live[m] && !shared) {
-                e = R.sel[u];
-                if (e < 0 || e >= a.E) {   // corrupted table: nothing is read through it
-                    if (lane == 0) raise_error(kErrExpertRange);
-                    live[m] = false;
-                    e = 0;
-                }
+    // one slot u at a time per wave: its PS passes of RP rows
+    for (int u = wave; u < n_slots; u += nwaves) {
+        bool live = true;
+        const bool shared = u >= P;
+        int e = 0;
+        if (!shared) {
+            e = R.sel[u];
+            if (e < 0 || e >= a.E) {   // corrupted table: nothing is read through it
+                if (lane == 0) raise_error(kErrExpertRange);
+                live = false;
+                e = 0;
             }
-            const QMat D = shared ? a.sdown : a.down;
-            Db[m] = D.data + (int64_t)e * D.expert_bytes;
-            rowb[m] = D.row_bytes;
-            hrow[m] = live[m] ? u : 0;   // the h row of slot u is u
         }
+        const QMat D = shared ? a.sdown : a.down;
+        const uint8_t* Db = D.data + (int64_t)e * D.expert_bytes;
+        const int64_t rowb = D.row_bytes;
+        const int hrow = live ? u : 0;   // the h row of slot u is u
         // all weight loads, then the h loads
-        uint4 w0[SM][PS], w1[SM][PS];
-        uint32_t w2[SM][PS];
+        uint4 w0[PS], w1[PS];
+        uint32_t w2[PS];
 #pragma unroll
-        for (int m = 0; m < SM; ++m) {
-#pragma unroll
-            for (int ps = 0; ps < PS; ++ps) {   // dead slots load expert 0's rows, never used
-                w2[m][ps] = 0;
-                const int o = o0 + ps * RP + rr;
-                const int oc = o < a.H ? o : a.H - 1;
-                const uint8_t* row = Db[m] + (int64_t)oc * rowb[m];
-                if constexpr (QD == kQ4_K) {
-                    const uint8_t* blk = row + (int64_t)(sl >> 3) * 144;
-                    w0[m][ps] = *reinterpret_cast<const uint4*>(blk);
-                    w1[m][ps] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (sl & 7));
-                } else {
-                    // 34-byte block at a 2-byte aligned offset: 36 bytes from the dword below it
-                    const uint8_t* blk = row + (int64_t)sl * 34;
-                    const uint32_t* dw = reinterpret_cast<const uint32_t*>((uintptr_t)blk & ~(uintptr_t)3);
-                    w0[m][ps] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
-                    w1[m][ps] = make_uint4(dw[4], dw[5], dw[6], dw[7]);
-                    w2[m][ps] = dw[8];
-                }
+        for (int pp = 0; pp < PS; ++pp) {   // a dead slot loads expert 0's rows, never used
+            w2[pp] = 0;
+            const int o = o0 + pp * RP + rr;
+            const int oc = o < a.H ? o : a.H - 1;
+            const uint8_t* row = Db + (int64_t)oc * rowb;
+            if constexpr (QD == kQ4_K) {
+                const uint8_t* blk = row + (int64_t)(sl >> 3) * 144;
+                w0[pp] = *reinterpret_cast<const uint4*>(blk);
+                w1[pp] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (sl & 7));
+            } else {
+                // 34-byte block at a 2-byte aligned offset: 36 bytes from the dword below it
+                const uint8_t* blk = row + (int64_t)sl * 34;
+                const uint32_t* dw = reinterpret_cast<const uint32_t*>((uintptr_t)blk & ~(uintptr_t)3);
+                w0[pp] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+                w1[pp] = make_uint4(dw[4], dw[5], dw[6], dw[7]);
+                w2[pp] = dw[8];
             }
         }
-        float4 hl4[SM][4], hh4[SM][4];
-#pragma unroll
-        for (int m = 0; m < SM; ++m) {
-            const float4* pl = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m] * a.I + c_lo);
-            const float4* ph = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[m] * a.I + c_hi);
+        float4 hl4[4], hh4[4];
+        {
+            const float4* pl = reinterpret_cast<const float4*>(a.h + (int64_t)hrow * a.I + c_lo);
+            const float4* ph = reinterpret_cast<const float4*>(a.h + (int64_t)hrow * a.I + c_hi);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                hl4[m][v] = pl[v];
-                hh4[m][v] = ph[v];
+                hl4[v] = pl[v];
+                hh4[v] = ph[v];
             }
         }
+        if (!live) continue;
+        float hl[1][16], hh[1][16], shl[1], shh[1];
+        unpack_f4<1>(hl4, hl[0]);
+        unpack_f4<1>(hh4, hh[0]);
+        shl[0] = shh[0] = 0.f;
 #pragma unroll
-        for (int m = 0; m < SM; ++m) {
-            if (!live[m]) continue;
-            float hl[1][16], hh[1][16], shl[1], shh[1];
-            unpack_f4<1>(hl4[m], hl[0]);
-            unpack_f4<1>(hh4[m], hh[0]);
-            shl[0] = shh[0] = 0.f;
+        for (int j = 0; j < 16; ++j) {
+            shl[0] += hl[0][j];
+            shh[0] += hh[0][j];
+        }
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                shl[0] += hl[0][j];
-                shh[0] += hh[0][j];
-            }
+        for (int pp = 0; pp < PS; ++pp) {
+            const int ps = pp;
+            float acc[1];
+            if constexpr (QD == kQ4_K) {
+                q4k_slice_dot<1>(w0[pp], w1[pp], kit, 1, hl, hh, shl, shh, acc);
+            } else {
+                const uint32_t dw[9] = {w0[pp].x, w0[pp].y, w0[pp].z, w0[pp].w,
+                                        w1[pp].x, w1[pp].y, w1[pp].z, w1[pp].w, w2[pp]};
+                const bool odd = (sl & 1) != 0;   // 34*sl is 2 mod 4 exactly for odd sl (rows 4-byte aligned)
+                const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
+                const float d = f16_bits_to_f32(odd ? (dw[0] >> 16) : (dw[0] & 0xFFFFu));
+                float s0 = 0.f;
 #pragma unroll
-            for (int ps = 0; ps < PS; ++ps) {
-                float acc[1];
-                if constexpr (QD == kQ4_K) {
-                    q4k_slice_dot<1>(w0[m][ps], w1[m][ps], kit, 1, hl, hh, shl, shh, acc);
-                } else {
-                    const uint32_t dw[9] = {w0[m][ps].x, w0[m][ps].y, w0[m][ps].z, w0[m][ps].w,
-                                            w1[m][ps].x, w1[m][ps].y, w1[m][ps].z, w1[m][ps].w, w2[m][ps]};
-                    const bool odd = (sl & 1) != 0;   // 34*sl is 2 mod 4 exactly for odd sl (rows 4-byte aligned)
-                    const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
-                    const float d = f16_bits_to_f32(odd ? (dw[0] >> 16) : (dw[0] & 0xFFFFu));
-                    float s0 = 0.f;
-#pragma unroll
-                    for (int i4 = 0; i4 < 8; ++i4) {
-                        const uint32_t q4 = __builtin_amdgcn_perm(dw[i4 + 1], dw[i4], sel) ^ 0x80808080u;  // q + 128
-                        const float* hv = i4 < 4 ? hl[0] : hh[0];
-                        const int j0 = 4 * (i4 & 3);
-                        s0 = fmaf(ubyte_f32<0>(q4), hv[j0 + 0], s0);
-                        s0 = fmaf(ubyte_f32<1>(q4), hv[j0 + 1], s0);
-                        s0 = fmaf(ubyte_f32<2>(q4), hv[j0 + 2], s0);
-                        s0 = fmaf(ubyte_f32<3>(q4), hv[j0 + 3], s0);
-                    }
-                    acc[0] = d * (s0 - 128.0f * (shl[0] + shh[0]));
+                for (int i4 = 0; i4 < 8; ++i4) {
+                    const uint32_t q4 = __builtin_amdgcn_perm(dw[i4 + 1], dw[i4], sel) ^ 0x80808080u;  // q + 128
+                    const float* hv = i4 < 4 ? hl[0] : hh[0];
+                    const int j0 = 4 * (i4 & 3);
+                    s0 = fmaf(ubyte_f32<0>(q4), hv[j0 + 0], s0);
+                    s0 = fmaf(ubyte_f32<1>(q4), hv[j0 + 1], s0);
+                    s0 = fmaf(ubyte_f32<2>(q4), hv[j0 + 2], s0);
+                    s0 = fmaf(ubyte_f32<3>(q4), hv[j0 + 3], s0);
                 }
-                acc[0] = segment_sum<NS>(acc[0]);
-                if (sl == NS - 1) s_y[hrow[m] * RO + ps * RP + rr] = acc[0];
+                acc[0] = d * (s0 - 128.0f * (shl[0] + shh[0]));
             }
+            acc[0] = segment_sum<NS>(acc[0]);
+            if (sl == NS - 1) s_y[hrow * RO + ps * RP + rr] = acc[0];
         }
     }
     __syncthreads();
@@ -719,10 +707,9 @@ hipError_t launch_k2p(const DecArgs& a, hipStream_t s) {
     constexpr int RO = (kWave / NS) * PS;
     const int slots = a.T * a.k + (a.has_shared ? a.T : 0);
     const int max_waves = kK2MaxThreads / kWave;
-    // one slot per wave in flight (more spill at this workgroup size); slots
-    // beyond 16 take a second round on some waves
+    // one slot per wave in flight; slots beyond 16 take further rounds
     const int waves = slots < 4 ? 4 : (slots > max_waves ? max_waves : slots);
-    dec_down_kernel<QD, NS, 1, PS><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
+    dec_down_kernel<QD, NS, PS><<<(a.H + RO - 1) / RO, waves * kWave, 0, s>>>(a);
     return hipGetLastError();
 }
 
