@@ -198,3 +198,36 @@ def test_decode_batches_up_to_eight_tokens(name, T, over, fused):
     dl = layers.make_layer(w, seed=18, index=0, device=DEV)
     logits, x = layers.inputs_np(w, seed=18)
     _check(m, dl, w, logits, x, m.MOE_FFN_DECODE, fused, TOL_DECODE)
+
+
+@pytest.mark.parametrize("path,fused", PATHS)
+@pytest.mark.parametrize("T", [1, 3, 12])
+def test_plain_softmax_and_shared_scale_through_the_layer(T, path, fused):
+    """Routing weights from the plain softmax over all E (no renormalisation) and a
+    per-token scale on the shared expert, through the whole layer (the two-kernel
+    decode layer forms both in its down kernel), against the oracle."""
+    m = qm()
+    if path == "decode" and T > 8:
+        pytest.skip("the decode path covers up to 8 tokens")
+    dl, w = _layer(n_experts=16, top_k=4, tokens=T, shared=True)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=30 + T)
+    scale = np.random.default_rng(31).uniform(0.1, 2.0, T).astype(np.float32)
+    lg = torch.from_numpy(logits).to(DEV)
+    xt = torch.from_numpy(x).to(DEV)
+    st = torch.from_numpy(scale).to(DEV)
+    bufs = m.forward(dl.layer, lg, xt, w.top_k, flags=_flags(m, path), renorm=False, shared_scale=st,
+                     fused=fused)
+    m.moe_check_device_errors()
+    mode = 1 if path == "int8" else 0
+    idx, wts = oracle.route_topk(logits, w.top_k, renorm=False)
+    assert np.array_equal(bufs.routing.idx.cpu().numpy(), idx)
+    assert np.allclose(bufs.routing.w.cpu().numpy(), wts, rtol=0, atol=1e-6)
+    assert wts.sum(axis=1).max() < 1.0    # the plain softmax leaves mass on the unselected experts
+    y, hb = oracle_pairs(dl, idx.reshape(-1), np.repeat(np.arange(T), w.top_k), x, mode)
+    ys = oracle_shared(dl, hb, np.arange(T), x, mode)
+    out = oracle.combine(y, wts, ys, scale.astype(np.float64))
+    tol = TOL_INT8 if path == "int8" else TOL_DECODE
+    e = normwise_err(bufs.out.cpu().numpy(), out)
+    _say("  plain softmax + shared scale, out err max %.3e" % e.max())
+    assert e.max() <= tol
