@@ -27,8 +27,9 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 Q8_0 = 8
 Q4_K = 12
-BLOCK_WEIGHTS = {Q4_K: 256, Q8_0: 32}
-BLOCK_BYTES = {Q4_K: 144, Q8_0: 34}
+Q5_K = 13
+BLOCK_WEIGHTS = {Q4_K: 256, Q5_K: 256, Q8_0: 32}
+BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q8_0: 34}
 
 _lib = None
 
@@ -59,6 +60,9 @@ def _load():
     lib.orc_q4k_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16, P, P, P, P]
     lib.orc_q4k_dequant.argtypes = [P, i64, P]
     lib.orc_q80_dequant.argtypes = [P, i64, P]
+    lib.orc_q5k_unpack.argtypes = [P, P, P, P, P, P]
+    lib.orc_q5k_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16, P, P, P, P]
+    lib.orc_q5k_dequant.argtypes = [P, i64, P]
     lib.orc_route_topk.argtypes = [P, i32, i32, i32, i32, P, P]
     lib.orc_router_logits.argtypes = [P, i32, i32, P, i32, P]
     lib.orc_bucket.argtypes = [P, i32, i32, i32, P, P, P, P, P]
@@ -136,8 +140,44 @@ def q80_dequant(blocks) -> np.ndarray:
     return out
 
 
+def q5k_unpack(block) -> dict:
+    """One 176-byte Q5_K super-block -> its fields (d, dmin bits; sc[8]; m[8]; q[256] in 0..31)."""
+    lib = _load()
+    blk = np.ascontiguousarray(np.frombuffer(bytes(block), dtype=np.uint8))
+    assert blk.size == 176
+    d = np.zeros(1, np.uint16)
+    dm = np.zeros(1, np.uint16)
+    sc = np.zeros(8, np.int32)
+    m = np.zeros(8, np.int32)
+    q = np.zeros(256, np.int32)
+    lib.orc_q5k_unpack(_ptr(blk), _ptr(d), _ptr(dm), _ptr(sc), _ptr(m), _ptr(q))
+    return {"d_bits": int(d[0]), "dmin_bits": int(dm[0]), "sc": sc, "m": m, "q": q}
+
+
+def q5k_pack(d_bits, dmin_bits, sc, m, q) -> np.ndarray:
+    """Fields -> one 176-byte Q5_K super-block (inverse of ``q5k_unpack``)."""
+    lib = _load()
+    sc = np.ascontiguousarray(sc, dtype=np.int32)
+    m = np.ascontiguousarray(m, dtype=np.int32)
+    q = np.ascontiguousarray(q, dtype=np.int32)
+    out = np.zeros(176, np.uint8)
+    lib.orc_q5k_pack(int(d_bits), int(dmin_bits), _ptr(sc), _ptr(m), _ptr(q), _ptr(out))
+    return out
+
+
+def q5k_dequant(blocks) -> np.ndarray:
+    """Q5_K blocks (uint8, a multiple of 176 bytes) -> fp64 weights."""
+    lib = _load()
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).ravel()
+    assert b.size % 176 == 0
+    n = b.size // 176
+    out = np.zeros(n * 256, np.float64)
+    lib.orc_q5k_dequant(_ptr(b), n, _ptr(out))
+    return out
+
+
 def dequant(blocks, qtype: int) -> np.ndarray:
-    return q4k_dequant(blocks) if qtype == Q4_K else q80_dequant(blocks)
+    return {Q4_K: q4k_dequant, Q5_K: q5k_dequant, Q8_0: q80_dequant}[qtype](blocks)
 
 
 def router_logits(x, w_router) -> np.ndarray:

@@ -30,7 +30,9 @@
  *  - "Strata v0.1.39" release notes (fixes): the activations quantized for the
  *    GPU dot products are kept finite.
  * The readings taken where the pages are silent (each function says which):
- *  R-layout  Q4_K and Q8_0 byte layouts are the public GGUF ones.
+ *  R-layout  Q4_K, Q5_K and Q8_0 byte layouts are the public GGUF ones
+ *            (Q5_K: among the expert formats of the Unsloth UD-Q4_K_XL files
+ *            the "Strata v0.1.31" release notes say run natively).
  *  R-topk    top-k by logit, descending, ties to the lower expert index,
  *            IEEE comparison (so -0 == +0 is a tie).
  *  R-softmax routing weights are the softmax over the k selected logits
@@ -61,6 +63,7 @@
 
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
 
 int orc_threads(void) {
 #ifdef _OPENMP
@@ -167,6 +170,85 @@ void orc_q4k_dequant(const uint8_t* blocks, int64_t n_blocks, double* out) {
 }
 
 /* ------------------------------------------------------------------------- */
+/* Q5_K super-block (R-layout): 176 bytes for 256 weights.                   */
+/*   [0:2]    d     fp16                                                    */
+/*   [2:4]    dmin  fp16                                                    */
+/*   [4:16]   s[12] the 6-bit scales and mins, packed as in Q4_K            */
+/*   [16:48]  qh[32] the fifth (high) bit of every quant                    */
+/*   [48:176] qs[128] the low 4 bits, laid out as Q4_K's quants             */
+/* Quant of weight 64c+l:    (qs[32c+l] & 15) + 16 * bit 2c   of qh[l]      */
+/* Quant of weight 64c+32+l: (qs[32c+l] >> 4) + 16 * bit 2c+1 of qh[l]      */
+/* (c = 0..3, l = 0..31); q in 0..31.  Weight value: w = d*sc*q - dmin*m.    */
+/* ------------------------------------------------------------------------- */
+void orc_q5k_unpack(const uint8_t* blk, uint16_t* d_bits, uint16_t* dmin_bits,
+                    int32_t* sc, int32_t* m, int32_t* q) {
+    const uint8_t* s = blk + 4;
+    const uint8_t* qh = blk + 16;
+    const uint8_t* qs = blk + 48;
+    *d_bits = rd16(blk);
+    *dmin_bits = rd16(blk + 2);
+    for (int j = 0; j < 8; ++j) {
+        if (j < 4) {
+            sc[j] = s[j] & 63;
+            m[j] = s[j + 4] & 63;
+        } else {
+            sc[j] = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+            m[j] = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+        }
+    }
+    for (int c = 0; c < 4; ++c) {
+        for (int l = 0; l < 32; ++l) {
+            q[64 * c + l] = (qs[32 * c + l] & 15) + 16 * ((qh[l] >> (2 * c)) & 1);
+            q[64 * c + 32 + l] = (qs[32 * c + l] >> 4) + 16 * ((qh[l] >> (2 * c + 1)) & 1);
+        }
+    }
+}
+
+/* Inverse of orc_q5k_unpack: fields (sc, m in 0..63, q in 0..31) -> 176
+ * bytes; with unpack a bijection (the 8 qh bits of byte l are the fifth bits
+ * of weights l, 32+l, 64+l, ..., 224+l in that order). */
+void orc_q5k_pack(uint16_t d_bits, uint16_t dmin_bits, const int32_t* sc,
+                  const int32_t* m, const int32_t* q, uint8_t* blk) {
+    uint8_t* s = blk + 4;
+    uint8_t* qh = blk + 16;
+    uint8_t* qs = blk + 48;
+    blk[0] = (uint8_t)(d_bits & 0xFF);
+    blk[1] = (uint8_t)(d_bits >> 8);
+    blk[2] = (uint8_t)(dmin_bits & 0xFF);
+    blk[3] = (uint8_t)(dmin_bits >> 8);
+    for (int j = 0; j < 4; ++j) {
+        s[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+        s[j + 4] = (uint8_t)((m[j] & 63) | ((m[j + 4] >> 4) << 6));
+        s[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
+    }
+    for (int l = 0; l < 32; ++l) {
+        int h = 0;
+        for (int c = 0; c < 4; ++c) {
+            h |= ((q[64 * c + l] >> 4) & 1) << (2 * c);
+            h |= ((q[64 * c + 32 + l] >> 4) & 1) << (2 * c + 1);
+        }
+        qh[l] = (uint8_t)h;
+    }
+    for (int c = 0; c < 4; ++c)
+        for (int l = 0; l < 32; ++l)
+            qs[32 * c + l] = (uint8_t)((q[64 * c + l] & 15) | ((q[64 * c + 32 + l] & 15) << 4));
+}
+
+/* Dequantize n_blocks Q5_K super-blocks (exact in fp64, as for Q4_K). */
+void orc_q5k_dequant(const uint8_t* blocks, int64_t n_blocks, double* out) {
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        uint16_t db, dmb;
+        int32_t sc[8], m[8], q[256];
+        orc_q5k_unpack(blocks + 176 * b, &db, &dmb, sc, m, q);
+        double d = orc_fp16_to_f64(db), dmin = orc_fp16_to_f64(dmb);
+        for (int i = 0; i < 256; ++i) {
+            int j = i / 32;
+            out[256 * b + i] = d * sc[j] * q[i] - dmin * m[j];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Q8_0 block (R-layout): 34 bytes for 32 weights: fp16 d, then 32 int8 q.   */
 /* Weight value: w = d*q.                                                    */
 /* ------------------------------------------------------------------------- */
@@ -179,14 +261,16 @@ void orc_q80_dequant(const uint8_t* blocks, int64_t n_blocks, double* out) {
     }
 }
 
-static int blk_weights(int qtype) { return qtype == ORC_Q4_K ? 256 : 32; }
-static int blk_bytes(int qtype) { return qtype == ORC_Q4_K ? 144 : 34; }
+static int blk_weights(int qtype) { return qtype == ORC_Q8_0 ? 32 : 256; }
+static int blk_bytes(int qtype) { return qtype == ORC_Q4_K ? 144 : (qtype == ORC_Q5_K ? 176 : 34); }
 
 /* One row of a quantized matrix (cols weights) -> fp64. */
 static void dequant_row(const uint8_t* row, int qtype, int cols, double* out) {
     int64_t nb = cols / blk_weights(qtype);
     if (qtype == ORC_Q4_K)
         orc_q4k_dequant(row, nb, out);
+    else if (qtype == ORC_Q5_K)
+        orc_q5k_dequant(row, nb, out);
     else
         orc_q80_dequant(row, nb, out);
 }

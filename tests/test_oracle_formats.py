@@ -155,3 +155,83 @@ def test_q4k_block_e_distinct_fields():
     assert np.array_equal(oracle.q4k_dequant(blk), (sc[j] * q - m[j]).astype(np.float64))
     # and the packer reproduces the hand-worked bytes
     assert np.array_equal(oracle.q4k_pack(0x3C00, 0x3C00, sc, m, q), blk)
+
+
+# ---------------------------------------------------------------------------- Q5_K
+# Q5_K is among the expert formats of the Unsloth UD-Q4_K_XL files that the
+# "Strata v0.1.31" release notes say run natively; its bytes follow the public
+# GGUF layout (reading R-layout in the oracle).
+
+def test_q5k_unpack_pack_roundtrip_random_bytes():
+    g = np.random.default_rng(11)
+    for _ in range(300):
+        blk = g.integers(0, 256, 176, dtype=np.uint8)
+        f = oracle.q5k_unpack(blk.tobytes())
+        assert f["q"].min() >= 0 and f["q"].max() <= 31
+        back = oracle.q5k_pack(f["d_bits"], f["dmin_bits"], f["sc"], f["m"], f["q"])
+        assert np.array_equal(back, blk)
+
+
+def test_q5k_pack_unpack_roundtrip_random_fields():
+    g = np.random.default_rng(12)
+    for _ in range(300):
+        d, dm = (int(v) for v in g.integers(0, 65536, 2))
+        sc, m, q = g.integers(0, 64, 8), g.integers(0, 64, 8), g.integers(0, 32, 256)
+        f = oracle.q5k_unpack(oracle.q5k_pack(d, dm, sc, m, q).tobytes())
+        assert f["d_bits"] == d and f["dmin_bits"] == dm
+        assert np.array_equal(f["sc"], sc) and np.array_equal(f["m"], m) and np.array_equal(f["q"], q)
+
+
+def test_q5k_block_f_closed_form():
+    blk = load_block("q5k_block_f.txt")
+    f = oracle.q5k_unpack(blk.tobytes())
+    assert np.array_equal(f["sc"], [1, 3, 5, 7, 17, 34, 51, 62])
+    assert np.array_equal(f["m"], [0, 1, 2, 3, 20, 33, 48, 63])
+    i = np.arange(256)
+    j = i // 32
+    assert np.array_equal(f["q"], (3 * i + 5 * j) % 32)
+    w = oracle.q5k_dequant(blk)
+    sc = np.array([1, 3, 5, 7, 17, 34, 51, 62])[j]
+    m = np.array([0, 1, 2, 3, 20, 33, 48, 63])[j]
+    assert np.array_equal(w, 0.5 * sc * ((3 * i + 5 * j) % 32) - 2.0 * m)
+    assert (w[0], w[33], w[200], w[255]) == (0.0, 10.0, 465.0, -126.0)
+    assert w.sum() == 33760.0
+
+
+def test_q5k_without_fifth_bits_is_q4k():
+    """qh = 0: a Q5_K block is the Q4_K block with the same header and low nibbles."""
+    g = np.random.default_rng(13)
+    for _ in range(50):
+        q4 = g.integers(0, 256, 144, dtype=np.uint8)
+        q4[1] &= 0x3B   # finite d and dmin
+        q4[3] &= 0x3B
+        q5 = np.concatenate([q4[:16], np.zeros(32, np.uint8), q4[16:]])
+        assert np.array_equal(oracle.q5k_dequant(q5), oracle.q4k_dequant(q4))
+
+
+def test_q5k_all_fifth_bits_add_16_d_sc():
+    """qh = 0xFF: every quant gains 16, so every weight gains 16*d*sc_j (exact)."""
+    g = np.random.default_rng(14)
+    for _ in range(50):
+        q4 = g.integers(0, 256, 144, dtype=np.uint8)
+        q4[1] &= 0x3B
+        q4[3] &= 0x3B
+        q5 = np.concatenate([q4[:16], np.full(32, 0xFF, np.uint8), q4[16:]])
+        f = oracle.q4k_unpack(q4.tobytes())
+        d = oracle.fp16_to_f64(np.array([f["d_bits"]], np.uint16))[0]
+        bump = np.repeat(16.0 * d * f["sc"], 32)
+        assert np.array_equal(oracle.q5k_dequant(q5), oracle.q4k_dequant(q4) + bump)
+
+
+def test_q5k_single_bit_sensitivity():
+    """Flipping qh bit b of byte l changes exactly one weight, index 32*b + l, by 16*d*sc_b."""
+    blk = load_block("q5k_block_f.txt")
+    base = oracle.q5k_dequant(blk)
+    f = oracle.q5k_unpack(blk.tobytes())
+    for l, b in [(0, 0), (5, 3), (17, 6), (31, 7)]:
+        mod = blk.copy()
+        mod[16 + l] ^= 1 << b
+        w = oracle.q5k_dequant(mod)
+        diff = np.nonzero(w != base)[0]
+        assert list(diff) == [32 * b + l]
+        assert abs(w[32 * b + l] - base[32 * b + l]) == 16 * 0.5 * f["sc"][b]
