@@ -54,14 +54,21 @@ typedef enum moe_status {
     MOE_ERR_DEVICE = 4            /* a HIP call failed, or a kernel set the error word */
 } moe_status;
 
-/* Block formats, numbered as in GGUF.  The pages name both formats (the
+/* Block formats, numbered as in GGUF.  The pages name these formats (the
  * "Strata v0.1.31" Unsloth bullet; Q4_K down experts on the Sage-A1.5 card) and
  * give no byte layout; the public GGUF layouts are used:
  *   MOE_Q4_K: 144-byte super-block of 256 weights: fp16 d, fp16 dmin, 12 bytes
  *             packing eight 6-bit scales and eight 6-bit mins, 128 bytes of
  *             4-bit quants; w = d*sc*q - dmin*m per 32-weight sub-block.
- *   MOE_Q8_0: 34-byte block of 32 weights: fp16 d, 32 int8 q; w = d*q. */
-enum { MOE_Q8_0 = 8, MOE_Q4_K = 12 };
+ *   MOE_Q5_K: 176-byte super-block of 256 weights: Q4_K's header, then 32
+ *             bytes holding the fifth bit of every quant, then the low 4 bits
+ *             as Q4_K's quants; q in 0..31, w = d*sc*q - dmin*m.
+ *   MOE_Q8_0: 34-byte block of 32 weights: fp16 d, 32 int8 q; w = d*q.
+ * Q4_K and Q5_K banks must be 16-byte aligned, Q8_0 banks 2-byte aligned.
+ * The two-kernel decode layer and the int8 MFMA GEMMs take Q4_K gate/up (and
+ * Q4_K or Q8_0 down, resp. Q4_K down); other mixes, Q5_K among them, run on
+ * the general kernels of the chosen path. */
+enum { MOE_Q8_0 = 8, MOE_Q4_K = 12, MOE_Q5_K = 13 };
 
 /* moe_route_topk flags */
 enum { MOE_ROUTE_RENORM = 1u }; /* weights = softmax over the k selected logits */
@@ -177,7 +184,7 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_
  * result of moe_route_topk for the same T, k and E (read on the device: no host
  * synchronisation).
  * Checks: shapes consistent with L; H, I multiples of 256; qtypes supported
- * (gate/up/down: Q4_K or Q8_0); alignment; workspace size. */
+ * (gate/up/down: Q4_K, Q5_K or Q8_0); alignment; workspace size. */
 moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T, int32_t k,
                             const float* x, const int8_t* xq, const float* xd, uint32_t flags,
                             float* y_pair, float* y_shared, void* workspace, size_t ws_bytes,

@@ -19,6 +19,7 @@ namespace moe {
 
 constexpr int kQ8_0 = 8;
 constexpr int kQ4_K = 12;
+constexpr int kQ5_K = 13;
 constexpr int kWave = 64;
 
 // Bits of the per-device error word.

@@ -732,7 +732,7 @@ hipError_t launch_k2(const DecArgs& a, hipStream_t s) {
 // (I = 256, 512 or 1024); T <= 4, T*k <= 64.
 bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd) {
     if (T < 1 || T > kDecMaxT || T * k > kDecMaxPairs) return false;
-    if (qg != kQ4_K || qu != kQ4_K) return false;
+    if (qg != kQ4_K || qu != kQ4_K || (qd != kQ4_K && qd != kQ8_0)) return false;
     const int nb = H / 256;
     if (!(nb == 1 || nb == 2 || nb == 4 || nb == 8 || nb == 10)) return false;
     const int ns = (qd == kQ4_K) ? 8 * (I / 256) : I / 32;

@@ -65,6 +65,35 @@ __device__ __forceinline__ void row_partial(const uint8_t* __restrict__ row, int
                           s.dmin * ((float)s.m_lo * xlo + (float)s.m_hi * xhi);
             }
         }
+    } else if constexpr (QT == kQ5_K) {
+        const int nslices = (cols >> 8) * 8;
+        for (int sidx = lane; sidx < nslices; sidx += kWave) {
+            const int b = sidx >> 3, part = sidx & 7;
+            Q5KSlice s;
+            q5k_load_slice(row + (int64_t)b * 176, part, s);
+            float qlo[16], qhi[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                qlo[i] = (float)q5k_slice_qlo(s, i);
+                qhi[i] = (float)q5k_slice_qhi(s, i);
+            }
+            const int clo = 256 * b + q4k_slice_col_lo(part);
+            const int chi = 256 * b + q4k_slice_col_hi(part);
+            for (int t = 0; t < nt; ++t) {
+                const float* xv = xs + t * xstride;
+                float slo = 0.f, shi = 0.f, xlo = 0.f, xhi = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float a = xv[clo + i], c = xv[chi + i];
+                    slo = fmaf(qlo[i], a, slo);
+                    shi = fmaf(qhi[i], c, shi);
+                    xlo += a;
+                    xhi += c;
+                }
+                acc[t] += s.s.d * ((float)s.s.sc_lo * slo + (float)s.s.sc_hi * shi) -
+                          s.s.dmin * ((float)s.s.m_lo * xlo + (float)s.s.m_hi * xhi);
+            }
+        }
     } else {
         const int nblocks = cols >> 5;
         for (int b = lane; b < nblocks; b += kWave) {
@@ -264,16 +293,26 @@ hipError_t launch_down_q(const FfnArgs& a, int hmode, hipStream_t s) {
 // templates dispatch on the routed formats, and the kernels read the shared
 // matrices' formats from the same template parameters, so both must agree
 // (checked by the API layer).
+namespace {
+
+template <int QG>
+hipError_t launch_gateup_g(const FfnArgs& a, int xmode, hipStream_t s) {
+    if (a.up.qtype == kQ4_K) return launch_gateup_q<QG, kQ4_K>(a, xmode, s);
+    if (a.up.qtype == kQ5_K) return launch_gateup_q<QG, kQ5_K>(a, xmode, s);
+    return launch_gateup_q<QG, kQ8_0>(a, xmode, s);
+}
+
+}  // namespace
+
 hipError_t launch_gateup(const FfnArgs& a, int xmode, hipStream_t s) {
-    const int g = a.gate.qtype, u = a.up.qtype;
-    if (g == kQ4_K && u == kQ4_K) return launch_gateup_q<kQ4_K, kQ4_K>(a, xmode, s);
-    if (g == kQ8_0 && u == kQ8_0) return launch_gateup_q<kQ8_0, kQ8_0>(a, xmode, s);
-    if (g == kQ4_K && u == kQ8_0) return launch_gateup_q<kQ4_K, kQ8_0>(a, xmode, s);
-    return launch_gateup_q<kQ8_0, kQ4_K>(a, xmode, s);
+    if (a.gate.qtype == kQ4_K) return launch_gateup_g<kQ4_K>(a, xmode, s);
+    if (a.gate.qtype == kQ5_K) return launch_gateup_g<kQ5_K>(a, xmode, s);
+    return launch_gateup_g<kQ8_0>(a, xmode, s);
 }
 
 hipError_t launch_down(const FfnArgs& a, int hmode, hipStream_t s) {
     if (a.down.qtype == kQ4_K) return launch_down_q<kQ4_K>(a, hmode, s);
+    if (a.down.qtype == kQ5_K) return launch_down_q<kQ5_K>(a, hmode, s);
     return launch_down_q<kQ8_0>(a, hmode, s);
 }
 
@@ -367,6 +406,25 @@ __global__ void __launch_bounds__(256) dequant_q4k_kernel(const uint8_t* __restr
     }
 }
 
+__global__ void __launch_bounds__(256) dequant_q5k_kernel(const uint8_t* __restrict__ blocks,
+                                                          int64_t n_slices, float* __restrict__ out) {
+    const int64_t sidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (sidx >= n_slices) return;
+    const int64_t b = sidx >> 3;
+    const int part = (int)(sidx & 7);
+    Q5KSlice s;
+    q5k_load_slice(blocks + b * 176, part, s);
+    const float dlo = s.s.d * (float)s.s.sc_lo, mlo = s.s.dmin * (float)s.s.m_lo;
+    const float dhi = s.s.d * (float)s.s.sc_hi, mhi = s.s.dmin * (float)s.s.m_hi;
+    float* o = out + b * 256;
+    const int clo = q4k_slice_col_lo(part), chi = q4k_slice_col_hi(part);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        o[clo + i] = dlo * (float)q5k_slice_qlo(s, i) - mlo;
+        o[chi + i] = dhi * (float)q5k_slice_qhi(s, i) - mhi;
+    }
+}
+
 __global__ void __launch_bounds__(256) dequant_q80_kernel(const uint8_t* __restrict__ blocks,
                                                           int64_t n_blocks, float* __restrict__ out) {
     const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -381,6 +439,9 @@ hipError_t launch_dequant(const void* blocks, int qtype, int64_t n_weights, floa
     if (qtype == kQ4_K) {
         const int64_t n = n_weights / 256 * 8;
         dequant_q4k_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint8_t*)blocks, n, out);
+    } else if (qtype == kQ5_K) {
+        const int64_t n = n_weights / 256 * 8;
+        dequant_q5k_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint8_t*)blocks, n, out);
     } else {
         const int64_t n = n_weights / 32;
         dequant_q80_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint8_t*)blocks, n, out);

@@ -33,8 +33,10 @@ moe_status from_hip(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int blk_weights(int qt) { return qt == MOE_Q4_K ? 256 : 32; }
-int blk_bytes(int qt) { return qt == MOE_Q4_K ? 144 : 34; }
+bool known_qtype(int qt) { return qt == MOE_Q4_K || qt == MOE_Q5_K || qt == MOE_Q8_0; }
+int blk_weights(int qt) { return qt == MOE_Q8_0 ? 32 : 256; }
+int blk_bytes(int qt) { return qt == MOE_Q4_K ? 144 : (qt == MOE_Q5_K ? 176 : 34); }
+size_t blk_align(int qt) { return qt == MOE_Q8_0 ? 2 : 16; }   // Q4_K, Q5_K blocks are 16-byte multiples
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
@@ -46,9 +48,9 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Validates one projection; rows x cols weights per expert, n_experts experts.
 moe_status check_qmatrix(const moe_qmatrix& m, const char* name, int rows, int cols, int n_experts) {
     if (!m.data) return fail(MOE_ERR_INVALID_ARGUMENT, "%s.data is NULL", name);
-    if (m.qtype != MOE_Q4_K && m.qtype != MOE_Q8_0)
-        return fail(MOE_ERR_UNSUPPORTED, "%s.qtype = %d: supported are Q4_K (%d) and Q8_0 (%d)", name,
-                    m.qtype, MOE_Q4_K, MOE_Q8_0);
+    if (!known_qtype(m.qtype))
+        return fail(MOE_ERR_UNSUPPORTED, "%s.qtype = %d: supported are Q4_K (%d), Q5_K (%d) and Q8_0 (%d)", name,
+                    m.qtype, MOE_Q4_K, MOE_Q5_K, MOE_Q8_0);
     if (m.rows != rows || m.cols != cols)
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s is %d x %d, expected %d x %d", name, m.rows, m.cols,
                     rows, cols);
@@ -62,7 +64,7 @@ moe_status check_qmatrix(const moe_qmatrix& m, const char* name, int rows, int c
     if (n_experts > 1 && m.expert_bytes < (int64_t)rows * rb)
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s.expert_bytes = %lld < rows*row_bytes = %lld", name,
                     (long long)m.expert_bytes, (long long)rows * rb);
-    const size_t al = m.qtype == MOE_Q4_K ? 16 : 2;
+    const size_t al = blk_align(m.qtype);
     if (!aligned(m.data, al) || (m.expert_bytes % (int64_t)al) != 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s: data and expert_bytes must be %zu-byte aligned", name, al);
     return MOE_OK;
@@ -414,13 +416,14 @@ moe_status moe_combine(const float* y_pair, const float* w, const float* y_share
 
 moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, float* out, hipStream_t stream) {
     if (!blocks || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "blocks or out is NULL");
-    if (qtype != MOE_Q4_K && qtype != MOE_Q8_0)
-        return fail(MOE_ERR_UNSUPPORTED, "qtype = %d: supported are Q4_K (%d) and Q8_0 (%d)", qtype, MOE_Q4_K, MOE_Q8_0);
+    if (!known_qtype(qtype))
+        return fail(MOE_ERR_UNSUPPORTED, "qtype = %d: supported are Q4_K (%d), Q5_K (%d) and Q8_0 (%d)", qtype,
+                    MOE_Q4_K, MOE_Q5_K, MOE_Q8_0);
     if (n_weights < 0 || n_weights % blk_weights(qtype) != 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "n_weights = %lld is not a multiple of the block size %d",
                     (long long)n_weights, blk_weights(qtype));
-    if (!aligned(blocks, qtype == MOE_Q4_K ? 16 : 2))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "blocks must be %d-byte aligned", qtype == MOE_Q4_K ? 16 : 2);
+    if (!aligned(blocks, blk_align(qtype)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "blocks must be %d-byte aligned", (int)blk_align(qtype));
     if (n_weights == 0) return ok();
     return from_hip(moe::launch_dequant(blocks, qtype, n_weights, out, stream), "moe_dequant_q launch");
 }

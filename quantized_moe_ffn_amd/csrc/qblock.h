@@ -1,4 +1,4 @@
-// qblock.h — device-side unpacking of Q4_K and Q8_0 blocks, shared by the FFN
+// qblock.h — device-side unpacking of Q4_K, Q5_K and Q8_0 blocks, shared by the FFN
 // kernels and the dequantization test hook (so the hook exercises the exact
 // loads, nibble splits and scale decoding the FFN kernels use).
 #pragma once
@@ -43,6 +43,44 @@ __device__ __forceinline__ int q4k_slice_qlo(const Q4KSlice& s, int i) {
 }
 __device__ __forceinline__ int q4k_slice_qhi(const Q4KSlice& s, int i) {
     return (int)((s.q[i >> 2] >> (8 * (i & 3) + 4)) & 15u);
+}
+
+// A Q5_K slice: the Q4_K slice of the same part (Q5_K keeps Q4_K's header and
+// quant layout, the quants 32 bytes further on) plus the 16 fifth-bit bytes of
+// its weights: qh[16*half + i] holds the fifth bit of the low-nibble weight i
+// in bit 2c and of the high-nibble weight i in bit 2c+1 (176-byte blocks:
+// d, dmin, 12 scale bytes, qh[32], qs[128]).
+struct Q5KSlice {
+    Q4KSlice s;        // header fields and the 16 low-bit bytes
+    uint32_t h[4];     // the 16 fifth-bit bytes
+    int c;             // 64-weight chunk of the slice
+};
+
+__device__ __forceinline__ void q5k_load_slice(const uint8_t* __restrict__ blk, int part, Q5KSlice& s) {
+    const uint4 hv = *reinterpret_cast<const uint4*>(blk);
+    const uint4 bv = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (part & 1));
+    const uint4 qv = *reinterpret_cast<const uint4*>(blk + 48 + 16 * part);
+    const Q4KHead h{hv.x, hv.y, hv.z, hv.w};
+    s.s.q[0] = qv.x;
+    s.s.q[1] = qv.y;
+    s.s.q[2] = qv.z;
+    s.s.q[3] = qv.w;
+    s.s.d = q4k_d(h);
+    s.s.dmin = q4k_dmin(h);
+    s.c = part >> 1;
+    q4k_scale_min(h, 2 * s.c, s.s.sc_lo, s.s.m_lo);
+    q4k_scale_min(h, 2 * s.c + 1, s.s.sc_hi, s.s.m_hi);
+    s.h[0] = bv.x;
+    s.h[1] = bv.y;
+    s.h[2] = bv.z;
+    s.h[3] = bv.w;
+}
+
+__device__ __forceinline__ int q5k_slice_qlo(const Q5KSlice& s, int i) {
+    return q4k_slice_qlo(s.s, i) + 16 * (int)((s.h[i >> 2] >> (8 * (i & 3) + 2 * s.c)) & 1u);
+}
+__device__ __forceinline__ int q5k_slice_qhi(const Q5KSlice& s, int i) {
+    return q4k_slice_qhi(s.s, i) + 16 * (int)((s.h[i >> 2] >> (8 * (i & 3) + 2 * s.c + 1)) & 1u);
 }
 
 // Q8_0 block: 2-byte aligned (34-byte blocks), read as 17 halfwords.

@@ -5,8 +5,10 @@ holds none of the method's arithmetic (no unpacking, no dot products, no
 routing).  A Q4_K block is 144 random bytes with its two leading fp16 fields
 (d, dmin) overwritten: random bytes make every 4-bit quant uniform on 0..15 and
 every 6-bit scale and min uniform on 0..63, because the twelve packed scale
-bytes and the 128 quant bytes are bijective images of those fields.  A Q8_0
-block is an fp16 scale followed by 32 int8 values uniform on -127..127.
+bytes and the 128 quant bytes are bijective images of those fields; a Q5_K
+block (176 bytes) is drawn the same way, its 32 fifth-bit bytes included, so
+every 5-bit quant is uniform on 0..31.  A Q8_0 block is an fp16 scale
+followed by 32 int8 values uniform on -127..127.
 d, dmin and the Q8_0 scale are fp16(|N(0,1)| * 0.01) (round to nearest even).
 
 Host arrays come from numpy's PCG64; large banks are drawn on the device with
@@ -23,8 +25,9 @@ import numpy as np
 
 Q8_0 = 8
 Q4_K = 12
-BLOCK_WEIGHTS = {Q4_K: 256, Q8_0: 32}
-BLOCK_BYTES = {Q4_K: 144, Q8_0: 34}
+Q5_K = 13
+BLOCK_WEIGHTS = {Q4_K: 256, Q5_K: 256, Q8_0: 32}
+BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q8_0: 34}
 
 
 def row_bytes(qtype: int, cols: int) -> int:
@@ -52,8 +55,9 @@ def _scale_f16(g: np.random.Generator, n: int) -> np.ndarray:
     return v.astype(np.float16)
 
 
-def q4k_blocks_np(g: np.random.Generator, n_blocks: int) -> np.ndarray:
-    b = g.integers(0, 256, size=(n_blocks, 144), dtype=np.uint8)
+def q4k_blocks_np(g: np.random.Generator, n_blocks: int, nbytes: int = 144) -> np.ndarray:
+    """Q4_K blocks (or, with nbytes = 176, Q5_K blocks: the same leading fp16 pair)."""
+    b = g.integers(0, 256, size=(n_blocks, nbytes), dtype=np.uint8)
     b[:, 0:4] = _scale_f16(g, 2 * n_blocks).view(np.uint8).reshape(n_blocks, 4)
     return b
 
@@ -68,7 +72,7 @@ def q80_blocks_np(g: np.random.Generator, n_blocks: int) -> np.ndarray:
 def bank_np(g: np.random.Generator, qtype: int, n_experts: int, rows: int, cols: int) -> np.ndarray:
     """[n_experts][rows][row_bytes] uint8."""
     nb = n_experts * rows * (cols // BLOCK_WEIGHTS[qtype])
-    blocks = q4k_blocks_np(g, nb) if qtype == Q4_K else q80_blocks_np(g, nb)
+    blocks = q80_blocks_np(g, nb) if qtype == Q8_0 else q4k_blocks_np(g, nb, BLOCK_BYTES[qtype])
     return blocks.reshape(n_experts, rows, row_bytes(qtype, cols))
 
 
@@ -107,9 +111,9 @@ def bank_torch(gen, qtype: int, n_experts: int, rows: int, cols: int, device):
     for s0 in range(0, nb, step):
         n = min(step, nb - s0)
         sl = out[s0:s0 + n]
-        sc = (torch.randn((n, 2 if qtype == Q4_K else 1), generator=gen, device=device,
+        sc = (torch.randn((n, 1 if qtype == Q8_0 else 2), generator=gen, device=device,
                           dtype=torch.float32).abs_() * 0.01).to(torch.float16)
-        if qtype == Q4_K:
+        if qtype != Q8_0:
             sl.copy_(torch.randint(0, 256, (n, bb), generator=gen, device=device, dtype=torch.uint8))
             sl[:, 0:4] = sc.view(torch.uint8).view(n, 4)
         else:

@@ -33,15 +33,15 @@ def _say(*a):
 # --------------------------------------------------------------------------- dequantization
 
 def _finite_scale_blocks(g, n, qt):
-    b = synth.q4k_blocks_np(g, n) if qt == oracle.Q4_K else synth.q80_blocks_np(g, n)
+    b = synth.q80_blocks_np(g, n) if qt == oracle.Q8_0 else synth.q4k_blocks_np(g, n, oracle.BLOCK_BYTES[qt])
     # random fp16 scale bit patterns, finite (subnormals included)
-    bits = g.integers(0, 0x7C00, size=(n, 2 if qt == oracle.Q4_K else 1), dtype=np.uint16)
+    bits = g.integers(0, 0x7C00, size=(n, 1 if qt == oracle.Q8_0 else 2), dtype=np.uint16)
     bits |= (g.integers(0, 2, size=bits.shape, dtype=np.uint16) << 15)
     b[:, : 2 * bits.shape[1]] = bits.view(np.uint8).reshape(n, -1)
     return b
 
 
-@pytest.mark.parametrize("qt", [oracle.Q4_K, oracle.Q8_0])
+@pytest.mark.parametrize("qt", [oracle.Q4_K, oracle.Q5_K, oracle.Q8_0])
 def test_dequant_bit_exact(qt):
     m = qm()
     from tests.golden import load_block
@@ -50,6 +50,8 @@ def test_dequant_bit_exact(qt):
     if qt == oracle.Q4_K:
         gold = np.stack([load_block(f) for f in ("q4k_block_a.txt", "q4k_block_b.txt", "q4k_block_c.txt",
                                                   "q4k_block_e.txt")])
+    elif qt == oracle.Q5_K:
+        gold = load_block("q5k_block_f.txt")[None]
     else:
         gold = load_block("q80_block.txt")[None]
     blocks = np.concatenate([gold, blocks])
@@ -209,7 +211,14 @@ def test_decode_layer_parity(name, fused):
 @pytest.mark.parametrize("over", [dict(hidden=256, inter=768, n_experts=3, top_k=3, tokens=5),
                                   dict(hidden=768, inter=256, n_experts=70, top_k=4, tokens=9, qt_down=oracle.Q8_0),
                                   dict(hidden=512, inter=512, n_experts=16, top_k=2, tokens=1, qt_gate=oracle.Q8_0,
-                                       qt_up=oracle.Q8_0)])
+                                       qt_up=oracle.Q8_0),
+                                  # Q5_K experts (the "Strata v0.1.31" Unsloth bullet): all Q5_K, and Q5_K
+                                  # gate/up with Q4_K down, with and without a shared expert
+                                  dict(hidden=512, inter=256, n_experts=16, top_k=4, tokens=3, qt_gate=oracle.Q5_K,
+                                       qt_up=oracle.Q5_K, qt_down=oracle.Q5_K),
+                                  dict(hidden=768, inter=512, n_experts=12, top_k=3, tokens=2, qt_gate=oracle.Q5_K,
+                                       qt_up=oracle.Q5_K, shared=True),
+                                  dict(hidden=256, inter=512, n_experts=8, top_k=2, tokens=1, qt_down=oracle.Q5_K)])
 @pytest.mark.parametrize("fused", [True, False])
 def test_decode_ragged_shapes(over, fused):
     m = qm()
@@ -253,6 +262,8 @@ def test_int8_prefill_chunk_sampled():
     dict(hidden=768, inter=512, n_experts=40, top_k=4, tokens=130, shared=True),   # shared expert, 3 blocks along H
     dict(hidden=2560, inter=512, n_experts=16, top_k=2, tokens=40),                # 32-token tiles (hidden > 2048)
     dict(hidden=512, inter=256, n_experts=8, top_k=2, tokens=20, qt_down=oracle.Q8_0),  # Q8_0 down: in-register path
+    dict(hidden=512, inter=256, n_experts=8, top_k=2, tokens=20, qt_gate=oracle.Q5_K, qt_up=oracle.Q5_K,
+         qt_down=oracle.Q5_K, shared=True),                                          # Q5_K experts: in-register path
 ])
 @pytest.mark.parametrize("fused", [True, False])
 def test_int8_ragged_shapes(over, fused):
