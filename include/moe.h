@@ -65,9 +65,9 @@ typedef enum moe_status {
  *             as Q4_K's quants; q in 0..31, w = d*sc*q - dmin*m.
  *   MOE_Q8_0: 34-byte block of 32 weights: fp16 d, 32 int8 q; w = d*q.
  * Q4_K and Q5_K banks must be 16-byte aligned, Q8_0 banks 2-byte aligned.
- * The two-kernel decode layer and the int8 MFMA GEMMs take Q4_K gate/up (and
- * Q4_K or Q8_0 down, resp. Q4_K down); other mixes, Q5_K among them, run on
- * the general kernels of the chosen path. */
+ * The two-kernel decode layer takes Q4_K or Q5_K gate/up (one format for
+ * both) with Q4_K, Q5_K or Q8_0 down; the int8 MFMA GEMMs take Q4_K
+ * throughout; other mixes run on the general kernels of the chosen path. */
 enum { MOE_Q8_0 = 8, MOE_Q4_K = 12, MOE_Q5_K = 13 };
 
 /* moe_route_topk flags */
@@ -205,12 +205,13 @@ size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uin
 /* The whole layer: routing (as moe_route_topk, results written to r), expert
  * FFN (as moe_expert_ffn_q, from fp32 x; on the int8 path x is quantized with
  * moe_quantize_act's rule into the workspace) and combine (as moe_combine),
- * enqueued on one stream.  For decode batches (T <= 8, T*k <= 64, Q4_K
- * gate/up with H/256 in {1,2,4,8,10}, down rows of 8, 16 or 32 32-weight
- * blocks, 16-byte aligned banks) the layer runs as two kernels: routing fused
- * into the gate/up kernel (each workgroup recomputes the top-k of its token)
- * and the combine fused into the down kernel (formed in slot order in LDS);
- * other shapes run the separate stages.  Same results contract as the three calls (bitwise
+ * enqueued on one stream.  For decode batches (T <= 8, T*k <= 64, Q4_K or
+ * Q5_K gate/up with H/256 in {1,2,4,8,10}, Q4_K, Q5_K or Q8_0 down rows of 8,
+ * 16 or 32 32-weight blocks, 16-byte aligned banks) the layer runs as two
+ * kernels: routing fused into the gate/up kernel (each wave recomputes the
+ * top-k of its token) and the combine fused into the down kernel (formed in
+ * slot order in LDS); other shapes run the separate stages.  Same results
+ * contract as the three calls (bitwise
  * deterministic; combine in slot order).  y_pair [T*k][H] is always written;
  * y_shared [T][H] is required iff the layer has a shared expert;
  * shared_scale [T] or NULL.  x must be 16-byte aligned.  Checks: those of

@@ -25,7 +25,7 @@
 //
 // Weight streaming (K1): a "slice" is 16 quant bytes of a Q4_K super-block =
 // 16 weights of sub-block 2c (low nibbles) and 16 of sub-block 2c+1 (high
-// nibbles).  A unit of W waves covers P rows x (8*NB) slices per pass with
+// nibbles); a Q5_K slice adds the 16 bytes holding those weights' fifth bits.  A unit of W waves covers P rows x (8*NB) slices per pass with
 // 64*W == P*8*NB, so every lane keeps the same 32 columns for the whole kernel
 // and holds those activations in registers (no LDS traffic for x).  Per slice a
 // lane issues two 16-byte loads (super-block header + quants), decodes the two
@@ -132,16 +132,53 @@ struct K1Shape {
 //   min word:                             ((h2 >> sa) & ma) | ((h3 >> 4) & mb),
 // each holding the 6-bit values of sub-blocks 0-3 (c < 2) or 4-7 (c >= 2) in
 // its bytes; sub-blocks 2c, 2c+1 are bytes 2(c%2), 2(c%2)+1, brought down by sh.
+// For Q5_K also: the fifth bits of the slice's low- and high-nibble weights
+// are bits 2c and 2c+1 of its qh bytes (f_lo, f_hi), isolated by m_one.
 struct SliceKit {
-    uint32_t m_lo, m_hi, sa, ma, mb, sh;
+    uint32_t m_lo, m_hi, sa, ma, mb, sh, f_lo, f_hi, m_one;
 };
 
+// (the fifth-bit fields are kept only where a Q5_K slice uses them: three
+// more live registers push some Q4_K kernels past an occupancy step)
+template <bool kFifth = false>
 __device__ __forceinline__ SliceKit slice_kit(int part) {
     const bool upper = part >= 4;
+    const uint32_t c = (uint32_t)(part >> 1);
     SliceKit k{0x0F0F0F0Fu, 0xF0F0F0F0u, upper ? 2u : 0u, upper ? 0x30303030u : 0x3F3F3F3Fu,
-               upper ? 0x0F0F0F0Fu : 0u, 8u * (uint32_t)(part & 2)};
+               upper ? 0x0F0F0F0Fu : 0u, 8u * (uint32_t)(part & 2), 2u * c, 2u * c + 1u, 0x01010101u};
     asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.sa), "+v"(k.ma), "+v"(k.mb), "+v"(k.sh));
+    if constexpr (kFifth) asm volatile("" : "+v"(k.f_lo), "+v"(k.f_hi), "+v"(k.m_one));
     return k;
+}
+
+// Super-block geometry of the k-quant formats the fused kernels stream: the
+// block size and where a slice's 16 quant bytes start (Q4_K: after the 16-byte
+// header; Q5_K: after the header and the 32 fifth-bit bytes).  A Q5_K slice
+// also needs the 16 fifth-bit bytes of its weights, at 16 + 16*(part & 1).
+template <int QT>
+struct KQuant;
+template <>
+struct KQuant<kQ4_K> {
+    static constexpr int kBytes = 144, kQs = 16;
+    static constexpr bool kFifth = false;
+};
+template <>
+struct KQuant<kQ5_K> {
+    static constexpr int kBytes = 176, kQs = 48;
+    static constexpr bool kFifth = true;
+};
+
+// The registers one slice of a k-quant row takes: header, quant bytes and, for
+// Q5_K, the fifth-bit bytes.
+struct KSlice {
+    uint4 hdr, q, hb;
+};
+
+template <int QT>
+__device__ __forceinline__ void kslice_load(const uint8_t* blk, int part, KSlice& r) {
+    r.hdr = *reinterpret_cast<const uint4*>(blk);
+    r.q = *reinterpret_cast<const uint4*>(blk + KQuant<QT>::kQs + 16 * part);
+    if constexpr (KQuant<QT>::kFifth) r.hb = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (part & 1));
 }
 
 // Dot products of one slice (16 quant bytes + its super-block header) with the
@@ -189,6 +226,61 @@ __device__ __forceinline__ void q4k_slice_dot(const uint4 hv, const uint4 qv, co
     }
 }
 
+// Q5_K: as q4k_slice_dot, with each quant's fifth bit OR-ed into bit 4 of
+// its byte (q in 0..31, no in-place 16*q scaling for the high nibbles).
+template <int TT>
+__device__ __forceinline__ void q5k_slice_dot(const uint4 hv, const uint4 qv, const uint4 bv, const SliceKit& kit,
+                                              int nt, const float (&xl)[TT][16], const float (&xh)[TT][16],
+                                              const float (&sxl)[TT], const float (&sxh)[TT], float (&acc)[TT]) {
+    const uint32_t scw = ((hv.y >> kit.sa) & kit.ma) | (hv.w & kit.mb);
+    const uint32_t mnw = ((hv.z >> kit.sa) & kit.ma) | ((hv.w >> 4) & kit.mb);
+    const uint32_t sc2 = scw >> kit.sh, mn2 = mnw >> kit.sh;
+    const float d = f16_bits_to_f32(hv.x & 0xFFFFu), dmin = f16_bits_to_f32(hv.x >> 16);
+    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+    const uint32_t hw[4] = {bv.x, bv.y, bv.z, bv.w};
+    float ql[16], qh[16];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+        const uint32_t lo = (qw[i4] & kit.m_lo) | (((hw[i4] >> kit.f_lo) & kit.m_one) << 4);
+        const uint32_t hi = ((qw[i4] >> 4) & kit.m_lo) | (((hw[i4] >> kit.f_hi) & kit.m_one) << 4);
+        ql[4 * i4 + 0] = ubyte_f32<0>(lo);
+        ql[4 * i4 + 1] = ubyte_f32<1>(lo);
+        ql[4 * i4 + 2] = ubyte_f32<2>(lo);
+        ql[4 * i4 + 3] = ubyte_f32<3>(lo);
+        qh[4 * i4 + 0] = ubyte_f32<0>(hi);
+        qh[4 * i4 + 1] = ubyte_f32<1>(hi);
+        qh[4 * i4 + 2] = ubyte_f32<2>(hi);
+        qh[4 * i4 + 3] = ubyte_f32<3>(hi);
+    }
+    const float dsl = d * ubyte_f32<0>(sc2), dsh = d * ubyte_f32<1>(sc2);
+    const float mml = dmin * ubyte_f32<0>(mn2), mmh = dmin * ubyte_f32<1>(mn2);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        acc[t] = 0.f;
+        if (t < nt) {
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                s0 = fmaf(ql[j], xl[t][j], s0);
+                s1 = fmaf(ql[j + 1], xl[t][j + 1], s1);
+                s2 = fmaf(qh[j], xh[t][j], s2);
+                s3 = fmaf(qh[j + 1], xh[t][j + 1], s3);
+            }
+            acc[t] = dsl * (s0 + s1) + dsh * (s2 + s3) - (mml * sxl[t] + mmh * sxh[t]);
+        }
+    }
+}
+
+template <int QT, int TT>
+__device__ __forceinline__ void kslice_dot(const KSlice& r, const SliceKit& kit, int nt, const float (&xl)[TT][16],
+                                           const float (&xh)[TT][16], const float (&sxl)[TT],
+                                           const float (&sxh)[TT], float (&acc)[TT]) {
+    if constexpr (KQuant<QT>::kFifth)
+        q5k_slice_dot<TT>(r.hdr, r.q, r.hb, kit, nt, xl, xh, sxl, sxh, acc);
+    else
+        q4k_slice_dot<TT>(r.hdr, r.q, kit, nt, xl, xh, sxl, sxh, acc);
+}
+
 template <int TT>
 __device__ __forceinline__ void unpack_f4(const float4 (&v)[4], float (&o)[16]) {
 #pragma unroll
@@ -203,7 +295,7 @@ __device__ __forceinline__ void unpack_f4(const float4 (&v)[4], float (&o)[16]) 
 // The streaming body of K1 for one expert slot: rows of gate and up of expert
 // e (bank G/U), applied to the nt tokens s_tok[] (their x already loaded into
 // xl4/xh4), h written to rows s_hrow[].
-template <int NB, int PASSES, int TT>
+template <int NB, int PASSES, int TT, int QG>
 __device__ __forceinline__ void dec_gateup_body(const DecArgs& a, const QMat& G, const QMat& U, int e, int nt,
                                                 const int (&s_hrow)[TT], float4 (&xl4)[TT][4], float4 (&xh4)[TT][4],
                                                 float* s_part) {
@@ -214,22 +306,18 @@ __device__ __forceinline__ void dec_gateup_body(const DecArgs& a, const QMat& G,
     const int rr = f / S::SLICES;                        // row inside the pass
     const int sl = f % S::SLICES;
     const int b = sl >> 3, part = sl & 7;
-    const SliceKit kit = slice_kit(part);
+    const SliceKit kit = slice_kit<KQuant<QG>::kFifth>(part);
     const int row0 = blockIdx.x * S::ROWS;
 
-    const uint8_t* Gb = G.data + (int64_t)e * G.expert_bytes + (int64_t)b * 144;
-    const uint8_t* Ub = U.data + (int64_t)e * U.expert_bytes + (int64_t)b * 144;
-    uint4 hg[PASSES], qg[PASSES], hu[PASSES], qu[PASSES];
+    const uint8_t* Gb = G.data + (int64_t)e * G.expert_bytes + (int64_t)b * KQuant<QG>::kBytes;
+    const uint8_t* Ub = U.data + (int64_t)e * U.expert_bytes + (int64_t)b * KQuant<QG>::kBytes;
+    KSlice rg[PASSES], ru[PASSES];
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
         const int i = row0 + (ps * S::UNITS + unit) * S::P + rr;
         const int ic = i < a.I ? i : a.I - 1;   // clamp: rows past I load a valid row and are not stored
-        const uint8_t* gr = Gb + (int64_t)ic * G.row_bytes;
-        const uint8_t* ur = Ub + (int64_t)ic * U.row_bytes;
-        hg[ps] = *reinterpret_cast<const uint4*>(gr);
-        qg[ps] = *reinterpret_cast<const uint4*>(gr + 16 + 16 * part);
-        hu[ps] = *reinterpret_cast<const uint4*>(ur);
-        qu[ps] = *reinterpret_cast<const uint4*>(ur + 16 + 16 * part);
+        kslice_load<QG>(Gb + (int64_t)ic * G.row_bytes, part, rg[ps]);
+        kslice_load<QG>(Ub + (int64_t)ic * U.row_bytes, part, ru[ps]);
     }
     float xl[TT][16], xh[TT][16], sxl[TT], sxh[TT];
 #pragma unroll
@@ -248,8 +336,8 @@ __device__ __forceinline__ void dec_gateup_body(const DecArgs& a, const QMat& G,
     for (int ps = 0; ps < PASSES; ++ps) {
         const int i = row0 + (ps * S::UNITS + unit) * S::P + rr;
         float pg[TT], pu[TT];
-        q4k_slice_dot<TT>(hg[ps], qg[ps], kit, nt, xl, xh, sxl, sxh, pg);
-        q4k_slice_dot<TT>(hu[ps], qu[ps], kit, nt, xl, xh, sxl, sxh, pu);
+        kslice_dot<QG, TT>(rg[ps], kit, nt, xl, xh, sxl, sxh, pg);
+        kslice_dot<QG, TT>(ru[ps], kit, nt, xl, xh, sxl, sxh, pu);
         if constexpr (S::IN_WAVE) {
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
@@ -334,7 +422,7 @@ __device__ __forceinline__ void load_x_slice(const DecArgs& a, int tok, int clo,
 // its rows.  Grid row 0 holds one more workgroup that publishes the routing
 // (and the table for K2); the groups take rows 1 and up.
 // ---------------------------------------------------------------------------
-template <int NB, int V, int TT, int SM>
+template <int NB, int V, int TT, int SM, int QG>
 __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_kernel(DecArgs a, int Gk) {
     using S = K1Shape<NB, 1>;
     static_assert(TT <= kShTok, "shared-expert groups of at most kShTok tokens");
@@ -359,7 +447,7 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
     const int rr = f / S::SLICES;
     const int sl = f % S::SLICES;
     const int b = sl >> 3, part = sl & 7;
-    const SliceKit kit = slice_kit(part);
+    const SliceKit kit = slice_kit<KQuant<QG>::kFifth>(part);
     const int clo = 256 * b + q4k_slice_col_lo(part);
     const int chi = 256 * b + q4k_slice_col_hi(part);
     const int i = blockIdx.x * S::ROWS + unit * S::P + rr;
@@ -377,7 +465,7 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
             load_x_slice<TT>(a, tc, clo, chi, xl4[t], xh4[t]);
             hrows[t] = a.T * a.k + tc;
         }
-        dec_gateup_body<NB, 1, TT>(a, a.sgate, a.sup, 0, nt, hrows, xl4, xh4, s_part);
+        dec_gateup_body<NB, 1, TT, QG>(a, a.sgate, a.sup, 0, nt, hrows, xl4, xh4, s_part);
         return;
     }
 
@@ -391,16 +479,14 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
     float4 xl4[1][4], xh4[1][4];
     load_x_slice<1>(a, tok, clo, chi, xl4[0], xh4[0]);
     (void)ex.keys(a.E, xv);
-    uint4 hg[SM], qg[SM], hu[SM], qu[SM];
+    KSlice rg[SM], ru[SM];
     auto issue = [&](int m, int e) {
         const uint8_t* gr = a.gate.data + (int64_t)e * a.gate.expert_bytes + (int64_t)ic * a.gate.row_bytes +
-                            (int64_t)b * 144;
-        const uint8_t* ur =
-            a.up.data + (int64_t)e * a.up.expert_bytes + (int64_t)ic * a.up.row_bytes + (int64_t)b * 144;
-        hg[m] = *reinterpret_cast<const uint4*>(gr);
-        qg[m] = *reinterpret_cast<const uint4*>(gr + 16 + 16 * part);
-        hu[m] = *reinterpret_cast<const uint4*>(ur);
-        qu[m] = *reinterpret_cast<const uint4*>(ur + 16 + 16 * part);
+                            (int64_t)b * KQuant<QG>::kBytes;
+        const uint8_t* ur = a.up.data + (int64_t)e * a.up.expert_bytes + (int64_t)ic * a.up.row_bytes +
+                            (int64_t)b * KQuant<QG>::kBytes;
+        kslice_load<QG>(gr, part, rg[m]);
+        kslice_load<QG>(ur, part, ru[m]);
     };
     int done = 0, win = 0;
 #pragma unroll
@@ -433,8 +519,8 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
         const int jt = q + m * Gk;
         if (jt >= a.k) continue;
         float pg[1], pu[1];
-        q4k_slice_dot<1>(hg[m], qg[m], kit, 1, xl, xh, sxl, sxh, pg);
-        q4k_slice_dot<1>(hu[m], qu[m], kit, 1, xl, xh, sxl, sxh, pu);
+        kslice_dot<QG, 1>(rg[m], kit, 1, xl, xh, sxl, sxh, pg);
+        kslice_dot<QG, 1>(ru[m], kit, 1, xl, xh, sxl, sxh, pu);
         if constexpr (S::IN_WAVE) {
             pg[0] = segment_sum<S::SLICES>(pg[0]);
             pu[0] = segment_sum<S::SLICES>(pu[0]);
@@ -510,9 +596,10 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
     __syncthreads();
     const int n_slots = P + (a.has_shared ? T : 0);
     const int rr = lane / NS, sl = lane % NS;
-    const SliceKit kit = slice_kit(sl & 7);   // used by the Q4_K rows
+    const SliceKit kit = slice_kit<QD == kQ5_K>(sl & 7);   // used by the k-quant rows
+    constexpr bool kq = QD != kQ8_0;
     int c_lo, c_hi;
-    if constexpr (QD == kQ4_K) {
+    if constexpr (kq) {
         c_lo = 256 * (sl >> 3) + q4k_slice_col_lo(sl & 7);
         c_hi = 256 * (sl >> 3) + q4k_slice_col_hi(sl & 7);
     } else {
@@ -540,16 +627,16 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
         // all weight loads, then the h loads
         uint4 w0[PS], w1[PS];
         uint32_t w2[PS];
+        KSlice rk[PS];
 #pragma unroll
         for (int pp = 0; pp < PS; ++pp) {   // a dead slot loads expert 0's rows, never used
             w2[pp] = 0;
             const int o = o0 + pp * RP + rr;
             const int oc = o < a.H ? o : a.H - 1;
             const uint8_t* row = Db + (int64_t)oc * rowb;
-            if constexpr (QD == kQ4_K) {
-                const uint8_t* blk = row + (int64_t)(sl >> 3) * 144;
-                w0[pp] = *reinterpret_cast<const uint4*>(blk);
-                w1[pp] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (sl & 7));
+            if constexpr (kq) {
+                kslice_load<kq ? QD : kQ4_K>(row + (int64_t)(sl >> 3) * KQuant<kq ? QD : kQ4_K>::kBytes, sl & 7,
+                                             rk[pp]);
             } else {
                 // 34-byte block at a 2-byte aligned offset: 36 bytes from the dword below it
                 const uint8_t* blk = row + (int64_t)sl * 34;
@@ -583,8 +670,8 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
         for (int pp = 0; pp < PS; ++pp) {
             const int ps = pp;
             float acc[1];
-            if constexpr (QD == kQ4_K) {
-                q4k_slice_dot<1>(w0[pp], w1[pp], kit, 1, hl, hh, shl, shh, acc);
+            if constexpr (kq) {
+                kslice_dot<kq ? QD : kQ4_K, 1>(rk[pp], kit, 1, hl, hh, shl, shh, acc);
             } else {
                 const uint32_t dw[9] = {w0[pp].x, w0[pp].y, w0[pp].z, w0[pp].w,
                                         w1[pp].x, w1[pp].y, w1[pp].z, w1[pp].w, w2[pp]};
@@ -637,7 +724,7 @@ namespace {
 // occupancy times CUs), looked up once per instance and device; 0 if unknown.
 constexpr int kDecMaxDevices = 64;
 
-template <int NB, int V, int TT, int SM>
+template <int NB, int V, int TT, int SM, int QG>
 int k1_capacity() {
     static std::atomic<int> cap[kDecMaxDevices];
     int dev = 0;
@@ -645,7 +732,7 @@ int k1_capacity() {
     int c = cap[dev].load(std::memory_order_relaxed);
     if (c == 0) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dec_gateup_pipe_kernel<NB, V, TT, SM>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dec_gateup_pipe_kernel<NB, V, TT, SM, QG>,
                                                          K1Shape<NB, 1>::THREADS, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -655,20 +742,19 @@ int k1_capacity() {
     return c;
 }
 
-template <int NB, int V, int TT, int SM>
-int k1_grid_rows(const DecArgs& a, int& Gk) {
+inline int k1_grid_rows(const DecArgs& a, int SM, int& Gk) {
     Gk = (a.k + SM - 1) / SM;                                         // groups per token
     const int n_sh = a.has_shared ? (a.T + kShTok - 1) / kShTok : 0;  // shared-expert groups
     return a.T * Gk + n_sh + 1;
 }
 
-template <int NB, int V, int TT, int SM>
+template <int NB, int V, int TT, int SM, int QG>
 hipError_t launch_k1_sm(const DecArgs& a, hipStream_t s) {
     using S = K1Shape<NB, 1>;
     int Gk;
-    const int rows = k1_grid_rows<NB, V, TT, SM>(a, Gk);
+    const int rows = k1_grid_rows(a, SM, Gk);
     dim3 grid((a.I + S::ROWS - 1) / S::ROWS, rows);
-    dec_gateup_pipe_kernel<NB, V, TT, SM><<<grid, S::THREADS, 0, s>>>(a, Gk);
+    dec_gateup_pipe_kernel<NB, V, TT, SM, QG><<<grid, S::THREADS, 0, s>>>(a, Gk);
     return hipGetLastError();
 }
 
@@ -677,29 +763,34 @@ hipError_t launch_k1_sm(const DecArgs& a, hipStream_t s) {
 // SIMD overlap, but a grid that needs a second round of workgroups ends a
 // whole workgroup duration later (the 3-token window at two slots: 1,664
 // workgroups for 1,024 places).
-template <int NB, int V, int TT>
+template <int NB, int V, int TT, int QG>
 hipError_t launch_k1_pipe(const DecArgs& a, hipStream_t s) {
     using S = K1Shape<NB, 1>;
     const int cols = (a.I + S::ROWS - 1) / S::ROWS;
     int Gk;
-    if (cols * k1_grid_rows<NB, V, TT, 2>(a, Gk) <= k1_capacity<NB, V, TT, 2>()) return launch_k1_sm<NB, V, TT, 2>(a, s);
-    if (cols * k1_grid_rows<NB, V, TT, 3>(a, Gk) <= k1_capacity<NB, V, TT, 3>()) return launch_k1_sm<NB, V, TT, 3>(a, s);
-    return launch_k1_sm<NB, V, TT, 4>(a, s);
+    if (cols * k1_grid_rows(a, 2, Gk) <= k1_capacity<NB, V, TT, 2, QG>()) return launch_k1_sm<NB, V, TT, 2, QG>(a, s);
+    if (cols * k1_grid_rows(a, 3, Gk) <= k1_capacity<NB, V, TT, 3, QG>()) return launch_k1_sm<NB, V, TT, 3, QG>(a, s);
+    return launch_k1_sm<NB, V, TT, 4, QG>(a, s);
 }
 
-template <int NB, int V>
+template <int NB, int V, int QG>
 hipError_t launch_k1_v(const DecArgs& a, hipStream_t s) {
     // the 4-token shared-expert branch costs registers; it runs only when the
     // layer has a shared expert and more than one token
-    return (a.T == 1 || !a.has_shared) ? launch_k1_pipe<NB, V, 1>(a, s) : launch_k1_pipe<NB, V, kShTok>(a, s);
+    return (a.T == 1 || !a.has_shared) ? launch_k1_pipe<NB, V, 1, QG>(a, s) : launch_k1_pipe<NB, V, kShTok, QG>(a, s);
+}
+
+template <int NB, int QG>
+hipError_t launch_k1_q(const DecArgs& a, hipStream_t s) {
+    const int vpl = topk_vpl(a.E);
+    if (vpl == 4) return launch_k1_v<NB, 4, QG>(a, s);
+    if (vpl == 8) return launch_k1_v<NB, 8, QG>(a, s);
+    return launch_k1_v<NB, 16, QG>(a, s);
 }
 
 template <int NB>
 hipError_t launch_k1(const DecArgs& a, hipStream_t s) {
-    const int vpl = topk_vpl(a.E);
-    if (vpl == 4) return launch_k1_v<NB, 4>(a, s);
-    if (vpl == 8) return launch_k1_v<NB, 8>(a, s);
-    return launch_k1_v<NB, 16>(a, s);
+    return a.gate.qtype == kQ5_K ? launch_k1_q<NB, kQ5_K>(a, s) : launch_k1_q<NB, kQ4_K>(a, s);
 }
 
 template <int QD, int NS, int PS>
@@ -727,17 +818,31 @@ hipError_t launch_k2(const DecArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Shapes the fused decode path covers: Q4_K gate/up with H/256 in {1, 2, 4, 8,
-// 10}; down Q4_K or Q8_0 with 8, 16 or 32 slices of 32 weights per row
-// (I = 256, 512 or 1024); T <= 4, T*k <= 64.
+// Shapes the fused decode path covers: Q4_K or Q5_K gate/up (the same format
+// for both) with H/256 in {1, 2, 4, 8, 10}; down Q4_K, Q5_K or Q8_0 with 8, 16
+// or 32 slices of 32 weights per row (I = 256, 512 or 1024); T <= 8,
+// T*k <= 64.
 bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd) {
     if (T < 1 || T > kDecMaxT || T * k > kDecMaxPairs) return false;
-    if (qg != kQ4_K || qu != kQ4_K || (qd != kQ4_K && qd != kQ8_0)) return false;
+    if ((qg != kQ4_K && qg != kQ5_K) || qu != qg) return false;
+    if (qd != kQ4_K && qd != kQ5_K && qd != kQ8_0) return false;
     const int nb = H / 256;
     if (!(nb == 1 || nb == 2 || nb == 4 || nb == 8 || nb == 10)) return false;
-    const int ns = (qd == kQ4_K) ? 8 * (I / 256) : I / 32;
+    const int ns = (qd == kQ8_0) ? I / 32 : 8 * (I / 256);
     return ns == 8 || ns == 16 || ns == 32;
 }
+
+namespace {
+
+template <int QD>
+hipError_t launch_k2_q(const DecArgs& a, hipStream_t s) {
+    const int ns = (QD == kQ8_0) ? a.I / 32 : 8 * (a.I / 256);
+    if (ns == 8) return launch_k2<QD, 8>(a, s);
+    if (ns == 16) return launch_k2<QD, 16>(a, s);
+    return launch_k2<QD, 32>(a, s);
+}
+
+}  // namespace
 
 hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s) {
     hipError_t e;
@@ -749,15 +854,9 @@ hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s) {
         default: e = launch_k1<10>(a, s); break;
     }
     if (e != hipSuccess) return e;
-    const int ns = (a.down.qtype == kQ4_K) ? 8 * (a.I / 256) : a.I / 32;
-    if (a.down.qtype == kQ4_K) {
-        if (ns == 8) return launch_k2<kQ4_K, 8>(a, s);
-        if (ns == 16) return launch_k2<kQ4_K, 16>(a, s);
-        return launch_k2<kQ4_K, 32>(a, s);
-    }
-    if (ns == 8) return launch_k2<kQ8_0, 8>(a, s);
-    if (ns == 16) return launch_k2<kQ8_0, 16>(a, s);
-    return launch_k2<kQ8_0, 32>(a, s);
+    if (a.down.qtype == kQ4_K) return launch_k2_q<kQ4_K>(a, s);
+    if (a.down.qtype == kQ5_K) return launch_k2_q<kQ5_K>(a, s);
+    return launch_k2_q<kQ8_0>(a, s);
 }
 
 }  // namespace moe

@@ -161,6 +161,10 @@ WORKLOADS = {
     "flash_next_decode": Workload("flash_next_decode", 2560, 512, 10, 512, 1, qt_down=Q8_0,
                                   shared=True, layers=48,
                                   notes="10 routed + 1 shared, Q4_K gate/up, Q8_0 down"),
+    # Q5_K experts: among the formats of the Unsloth UD-Q4_K_XL files that the
+    # "Strata v0.1.31" release notes run natively; the Sage-like layer stands in
+    "sage_decode_q5k": Workload("sage_decode_q5k", 2048, 256, 8, 512, 1, qt_gate=Q5_K, qt_up=Q5_K, qt_down=Q5_K,
+                                layers=40, notes="the sage_decode layer with Q5_K gate/up/down"),
     "prefill_chunk": Workload("prefill_chunk", 2048, 256, 8, 512, 4096, zipf_s=1.1, layers=4,
                               int8_path=True,
                               notes="logits N(0,1) - 1.1 ln(e+1); int8 activations"),

@@ -441,3 +441,25 @@ def test_combine_vector_and_scalar_paths_agree():
     ref = oracle.combine(y.cpu().numpy().astype(np.float64), wts.cpu().numpy().astype(np.float64),
                          ys.cpu().numpy().astype(np.float64))
     assert np.abs(out_a.cpu().numpy() - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name,T,over", [
+    ("sage_decode", 1, dict(n_experts=64, qt_gate=oracle.Q5_K, qt_up=oracle.Q5_K, qt_down=oracle.Q5_K)),
+    ("sage_decode", 5, dict(n_experts=64, qt_gate=oracle.Q5_K, qt_up=oracle.Q5_K, qt_down=oracle.Q5_K)),
+    ("flash_next_decode", 2, dict(n_experts=64, qt_gate=oracle.Q5_K, qt_up=oracle.Q5_K)),   # Q8_0 down, shared
+    ("flash_next_decode", 1, dict(n_experts=64, qt_down=oracle.Q5_K)),                       # Q4_K gate/up
+])
+def test_q5k_decode_layers(name, T, over, fused):
+    """Q5_K experts (the "Strata v0.1.31" Unsloth bullet) at the decode shapes: the
+    two-kernel layer streams Q5_K slices (header, fifth-bit bytes, low nibbles);
+    the separate calls use the general kernels."""
+    m = qm()
+    _say("q5k decode", name, T, over, fused)
+    from quantized_moe_ffn_amd import layers
+    w = synth.Workload(**{**synth.WORKLOADS[name].__dict__, **over, "tokens": T})
+    dl = layers.make_layer(w, seed=21, index=0, device=DEV)
+    logits, x = layers.inputs_np(w, seed=21)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused)
+    _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
+    _check_routing(bufs.routing, logits, w.top_k)
