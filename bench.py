@@ -14,6 +14,7 @@ oracle timed on a bounded sample of the same workload.  Progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -64,6 +65,11 @@ def main() -> int:
     ap.add_argument("--router", action="store_true",
                     help="compute each layer's logits on the GPU from x and a seeded fp32 [E][H] router "
                          "matrix (moe_router_logits) inside the timed step")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the tokens per layer call (a decode batch or verify window of the "
+                         "same layer shape)")
+    ap.add_argument("--path", choices=["auto", "decode", "int8"], default=None,
+                    help="FFN path (default: the workload's own; auto takes the decode path up to 8 tokens)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -84,10 +90,22 @@ def main() -> int:
     torch.cuda.set_device(dev)
 
     w = synth.WORKLOADS[args.config]
+    if args.tokens is not None:
+        if args.tokens < 1:
+            print("--tokens must be at least 1", file=sys.stderr)
+            return 2
+        if args.tokens != w.tokens:
+            w = dataclasses.replace(w, name="%s_t%d" % (w.name, args.tokens), tokens=args.tokens)
     L = args.layers or w.layers
     R = max(1, args.replays)
     T, H, E, k, I = w.tokens, w.hidden, w.n_experts, w.top_k, w.inter
     flags = qm.MOE_FFN_INT8 if w.int8_path else qm.MOE_FFN_DECODE
+    if args.path is not None:
+        flags = {"auto": qm.MOE_FFN_AUTO, "decode": qm.MOE_FFN_DECODE, "int8": qm.MOE_FFN_INT8}[args.path]
+        int8 = flags == qm.MOE_FFN_INT8 or (flags == qm.MOE_FFN_AUTO and T > qm.AUTO_DECODE_MAX_T)
+        if int8 != w.int8_path:
+            # the roofline, the dtype and the oracle's quantisation points follow the path taken
+            w = dataclasses.replace(w, name="%s_%s" % (w.name, "int8" if int8 else "decode"), int8_path=int8)
 
     log("[bench] building %d layers of %s (%.2f GB of expert weights)"
         % (L, w.name, L * (E * w.expert_bytes() + (w.expert_bytes() if w.shared else 0)) / 1e9))

@@ -28,8 +28,9 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 Q8_0 = 8
 Q4_K = 12
 Q5_K = 13
-BLOCK_WEIGHTS = {Q4_K: 256, Q5_K: 256, Q8_0: 32}
-BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q8_0: 34}
+Q5_1 = 7
+BLOCK_WEIGHTS = {Q4_K: 256, Q5_K: 256, Q8_0: 32, Q5_1: 32}
+BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q8_0: 34, Q5_1: 24}
 
 _lib = None
 
@@ -63,6 +64,9 @@ def _load():
     lib.orc_q5k_unpack.argtypes = [P, P, P, P, P, P]
     lib.orc_q5k_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16, P, P, P, P]
     lib.orc_q5k_dequant.argtypes = [P, i64, P]
+    lib.orc_q51_unpack.argtypes = [P, P, P, P]
+    lib.orc_q51_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16, P, P]
+    lib.orc_q51_dequant.argtypes = [P, i64, P]
     lib.orc_route_topk.argtypes = [P, i32, i32, i32, i32, P, P]
     lib.orc_router_logits.argtypes = [P, i32, i32, P, i32, P]
     lib.orc_bucket.argtypes = [P, i32, i32, i32, P, P, P, P, P]
@@ -176,8 +180,41 @@ def q5k_dequant(blocks) -> np.ndarray:
     return out
 
 
+def q51_unpack(block) -> dict:
+    """One 24-byte Q5_1 block -> its fields (d and m bits; q[32] in 0..31)."""
+    lib = _load()
+    blk = np.ascontiguousarray(np.asarray(block, dtype=np.uint8).reshape(-1))
+    assert blk.size == 24
+    d = np.zeros(1, np.uint16)
+    m = np.zeros(1, np.uint16)
+    q = np.zeros(32, np.int32)
+    lib.orc_q51_unpack(_ptr(blk), _ptr(d), _ptr(m), _ptr(q))
+    return {"d_bits": int(d[0]), "m_bits": int(m[0]), "q": q}
+
+
+def q51_pack(d_bits, m_bits, q) -> np.ndarray:
+    """Fields -> one 24-byte Q5_1 block (inverse of ``q51_unpack``)."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.int32)
+    assert q.shape == (32,)
+    out = np.zeros(24, np.uint8)
+    lib.orc_q51_pack(int(d_bits), int(m_bits), _ptr(q), _ptr(out))
+    return out
+
+
+def q51_dequant(blocks) -> np.ndarray:
+    """Q5_1 blocks (uint8, a multiple of 24 bytes) -> fp64 weights."""
+    lib = _load()
+    b = np.ascontiguousarray(np.asarray(blocks, dtype=np.uint8).reshape(-1))
+    assert b.size % 24 == 0
+    n = b.size // 24
+    out = np.zeros(32 * n, np.float64)
+    lib.orc_q51_dequant(_ptr(b), n, _ptr(out))
+    return out
+
+
 def dequant(blocks, qtype: int) -> np.ndarray:
-    return {Q4_K: q4k_dequant, Q5_K: q5k_dequant, Q8_0: q80_dequant}[qtype](blocks)
+    return {Q4_K: q4k_dequant, Q5_K: q5k_dequant, Q8_0: q80_dequant, Q5_1: q51_dequant}[qtype](blocks)
 
 
 def router_logits(x, w_router) -> np.ndarray:

@@ -30,9 +30,10 @@
  *  - "Strata v0.1.39" release notes (fixes): the activations quantized for the
  *    GPU dot products are kept finite.
  * The readings taken where the pages are silent (each function says which):
- *  R-layout  Q4_K, Q5_K and Q8_0 byte layouts are the public GGUF ones
- *            (Q5_K: among the expert formats of the Unsloth UD-Q4_K_XL files
- *            the "Strata v0.1.31" release notes say run natively).
+ *  R-layout  Q4_K, Q5_K, Q5_1 and Q8_0 byte layouts are the public GGUF
+ *            ones (Q5_K and Q5_1: among the expert formats of the Unsloth
+ *            UD-Q4_K_XL files the "Strata v0.1.31" release notes say run
+ *            natively).
  *  R-topk    top-k by logit, descending, ties to the lower expert index,
  *            IEEE comparison (so -0 == +0 is a tie).
  *  R-softmax routing weights are the softmax over the k selected logits
@@ -61,6 +62,7 @@
 #include <omp.h>
 #endif
 
+#define ORC_Q5_1 7
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13
@@ -261,8 +263,58 @@ void orc_q80_dequant(const uint8_t* blocks, int64_t n_blocks, double* out) {
     }
 }
 
-static int blk_weights(int qtype) { return qtype == ORC_Q8_0 ? 32 : 256; }
-static int blk_bytes(int qtype) { return qtype == ORC_Q4_K ? 144 : (qtype == ORC_Q5_K ? 176 : 34); }
+/* ------------------------------------------------------------------------- */
+/* Q5_1 block (R-layout): 24 bytes for 32 weights.                           */
+/*   [0:2]  d   fp16                                                        */
+/*   [2:4]  m   fp16 (an offset added to every weight)                       */
+/*   [4:8]  qh  32-bit little-endian word: bit i is the fifth bit of weight i*/
+/*   [8:24] qs[16] the low 4 bits: byte l holds weight l in its low nibble   */
+/*          and weight 16+l in its high nibble                               */
+/* Quant of weight l:    (qs[l] & 15) + 16 * bit l      of qh                */
+/* Quant of weight 16+l: (qs[l] >> 4) + 16 * bit (16+l) of qh   (l = 0..15); */
+/* q in 0..31.  Weight value: w = d*q + m.                                   */
+/* ------------------------------------------------------------------------- */
+void orc_q51_unpack(const uint8_t* blk, uint16_t* d_bits, uint16_t* m_bits, int32_t* q) {
+    const uint8_t* qs = blk + 8;
+    uint32_t qh = (uint32_t)blk[4] | ((uint32_t)blk[5] << 8) | ((uint32_t)blk[6] << 16) | ((uint32_t)blk[7] << 24);
+    *d_bits = rd16(blk);
+    *m_bits = rd16(blk + 2);
+    for (int l = 0; l < 16; ++l) {
+        q[l] = (qs[l] & 15) + 16 * (int32_t)((qh >> l) & 1u);
+        q[16 + l] = (qs[l] >> 4) + 16 * (int32_t)((qh >> (16 + l)) & 1u);
+    }
+}
+
+/* Inverse of orc_q51_unpack: fields (q in 0..31) -> 24 bytes; with unpack a
+ * bijection between the bytes and (d bits, m bits, q[32]). */
+void orc_q51_pack(uint16_t d_bits, uint16_t m_bits, const int32_t* q, uint8_t* blk) {
+    uint32_t qh = 0;
+    blk[0] = (uint8_t)(d_bits & 0xFF);
+    blk[1] = (uint8_t)(d_bits >> 8);
+    blk[2] = (uint8_t)(m_bits & 0xFF);
+    blk[3] = (uint8_t)(m_bits >> 8);
+    for (int i = 0; i < 32; ++i) qh |= (uint32_t)((q[i] >> 4) & 1) << i;
+    for (int b = 0; b < 4; ++b) blk[4 + b] = (uint8_t)(qh >> (8 * b));
+    for (int l = 0; l < 16; ++l) blk[8 + l] = (uint8_t)((q[l] & 15) | ((q[16 + l] & 15) << 4));
+}
+
+/* Dequantize n_blocks Q5_1 blocks into 32*n_blocks fp64 weights.  d*q and m
+ * are multiples of 2^-24 below 2^21 in magnitude, so d*q + m is exact in
+ * fp64: each weight is the exact value of the definition. */
+void orc_q51_dequant(const uint8_t* blocks, int64_t n_blocks, double* out) {
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        uint16_t db, mb;
+        int32_t q[32];
+        orc_q51_unpack(blocks + 24 * b, &db, &mb, q);
+        double d = orc_fp16_to_f64(db), m = orc_fp16_to_f64(mb);
+        for (int i = 0; i < 32; ++i) out[32 * b + i] = d * q[i] + m;
+    }
+}
+
+static int blk_weights(int qtype) { return (qtype == ORC_Q8_0 || qtype == ORC_Q5_1) ? 32 : 256; }
+static int blk_bytes(int qtype) {
+    return qtype == ORC_Q4_K ? 144 : (qtype == ORC_Q5_K ? 176 : (qtype == ORC_Q5_1 ? 24 : 34));
+}
 
 /* One row of a quantized matrix (cols weights) -> fp64. */
 static void dequant_row(const uint8_t* row, int qtype, int cols, double* out) {
@@ -271,6 +323,8 @@ static void dequant_row(const uint8_t* row, int qtype, int cols, double* out) {
         orc_q4k_dequant(row, nb, out);
     else if (qtype == ORC_Q5_K)
         orc_q5k_dequant(row, nb, out);
+    else if (qtype == ORC_Q5_1)
+        orc_q51_dequant(row, nb, out);
     else
         orc_q80_dequant(row, nb, out);
 }

@@ -25,7 +25,9 @@
 //
 // Weight streaming (K1): a "slice" is 16 quant bytes of a Q4_K super-block =
 // 16 weights of sub-block 2c (low nibbles) and 16 of sub-block 2c+1 (high
-// nibbles); a Q5_K slice adds the 16 bytes holding those weights' fifth bits.  A unit of W waves covers P rows x (8*NB) slices per pass with
+// nibbles); a Q5_K slice adds the 16 bytes holding those weights' fifth bits;
+// a Q8_0 row's lane takes one 34-byte block (32 weights) instead.  A unit of W
+// waves covers P rows x (8*NB) slices per pass with
 // 64*W == P*8*NB, so every lane keeps the same 32 columns for the whole kernel
 // and holds those activations in registers (no LDS traffic for x).  Per slice a
 // lane issues two 16-byte loads (super-block header + quants), decodes the two
@@ -134,8 +136,9 @@ struct K1Shape {
 // its bytes; sub-blocks 2c, 2c+1 are bytes 2(c%2), 2(c%2)+1, brought down by sh.
 // For Q5_K also: the fifth bits of the slice's low- and high-nibble weights
 // are bits 2c and 2c+1 of its qh bytes (f_lo, f_hi), isolated by m_one.
+// A Q8_0 lane uses only sel8 and dsh8 (see q8_block_dot).
 struct SliceKit {
-    uint32_t m_lo, m_hi, sa, ma, mb, sh, f_lo, f_hi, m_one;
+    uint32_t m_lo, m_hi, sa, ma, mb, sh, f_lo, f_hi, m_one, sel8, dsh8;
 };
 
 // (the fifth-bit fields are kept only where a Q5_K slice uses them: three
@@ -145,7 +148,7 @@ __device__ __forceinline__ SliceKit slice_kit(int part) {
     const bool upper = part >= 4;
     const uint32_t c = (uint32_t)(part >> 1);
     SliceKit k{0x0F0F0F0Fu, 0xF0F0F0F0u, upper ? 2u : 0u, upper ? 0x30303030u : 0x3F3F3F3Fu,
-               upper ? 0x0F0F0F0Fu : 0u, 8u * (uint32_t)(part & 2), 2u * c, 2u * c + 1u, 0x01010101u};
+               upper ? 0x0F0F0F0Fu : 0u, 8u * (uint32_t)(part & 2), 2u * c, 2u * c + 1u, 0x01010101u, 0u, 0u};
     asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.sa), "+v"(k.ma), "+v"(k.mb), "+v"(k.sh));
     if constexpr (kFifth) asm volatile("" : "+v"(k.f_lo), "+v"(k.f_hi), "+v"(k.m_one));
     return k;
@@ -168,17 +171,71 @@ struct KQuant<kQ5_K> {
     static constexpr bool kFifth = true;
 };
 
-// The registers one slice of a k-quant row takes: header, quant bytes and, for
-// Q5_K, the fifth-bit bytes.
+// The registers one slice takes: for a k-quant the super-block header, the 16
+// quant bytes and, for Q5_K, the 16 fifth-bit bytes; for Q8_0 the nine dwords
+// that hold the lane's 34-byte block.
 struct KSlice {
     uint4 hdr, q, hb;
 };
 
+// Lane sl of a row: a k-quant row has 8 slices per 256-weight super-block
+// (super-block sl/8, part sl%8); a Q8_0 row has one 32-weight block per lane
+// (block sl, columns 32*sl .. 32*sl + 31).  Both give H/32 lanes per row.
 template <int QT>
-__device__ __forceinline__ void kslice_load(const uint8_t* blk, int part, KSlice& r) {
-    r.hdr = *reinterpret_cast<const uint4*>(blk);
-    r.q = *reinterpret_cast<const uint4*>(blk + KQuant<QT>::kQs + 16 * part);
-    if constexpr (KQuant<QT>::kFifth) r.hb = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (part & 1));
+__device__ __forceinline__ int kslice_block_off(int sl) {
+    if constexpr (QT == kQ8_0)
+        return 34 * sl;
+    else
+        return (sl >> 3) * KQuant<QT>::kBytes;
+}
+
+// First column of the lane's low and high halves (16 weights each).
+template <int QT>
+__device__ __forceinline__ int kslice_col_lo(int sl) {
+    if constexpr (QT == kQ8_0)
+        return 32 * sl;
+    else
+        return 256 * (sl >> 3) + q4k_slice_col_lo(sl & 7);
+}
+template <int QT>
+__device__ __forceinline__ int kslice_col_hi(int sl) {
+    if constexpr (QT == kQ8_0)
+        return 32 * sl + 16;
+    else
+        return 256 * (sl >> 3) + q4k_slice_col_hi(sl & 7);
+}
+
+// A Q8_0 block sits at 34*sl bytes into a row whose start is 4-byte aligned,
+// so it starts 2 bytes past a dword boundary exactly when sl is odd: the
+// selector of v_perm_b32 that brings its quants into place, and the half of
+// the first dword holding d.
+template <int QT>
+__device__ __forceinline__ SliceKit kslice_kit(int sl) {
+    if constexpr (QT == kQ8_0) {
+        SliceKit k{};
+        const bool odd = (sl & 1) != 0;
+        k.sel8 = odd ? 0x07060504u : 0x05040302u;
+        k.dsh8 = odd ? 16u : 0u;
+        return k;
+    } else {
+        return slice_kit<KQuant<QT>::kFifth>(sl & 7);
+    }
+}
+
+// blk = row start + kslice_block_off<QT>(sl)
+template <int QT>
+__device__ __forceinline__ void kslice_load(const uint8_t* blk, int sl, KSlice& r) {
+    if constexpr (QT == kQ8_0) {
+        const uint32_t* dw = reinterpret_cast<const uint32_t*>((uintptr_t)blk & ~(uintptr_t)3);
+        r.hdr = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+        r.q = make_uint4(dw[4], dw[5], dw[6], dw[7]);
+        r.hb = make_uint4(dw[8], 0u, 0u, 0u);
+    } else {
+        const int part = sl & 7;
+        r.hdr = *reinterpret_cast<const uint4*>(blk);
+        r.q = *reinterpret_cast<const uint4*>(blk + KQuant<QT>::kQs + 16 * part);
+        if constexpr (KQuant<QT>::kFifth) r.hb = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (part & 1));
+    }
 }
 
 // Dot products of one slice (16 quant bytes + its super-block header) with the
@@ -271,11 +328,48 @@ __device__ __forceinline__ void q5k_slice_dot(const uint4 hv, const uint4 qv, co
     }
 }
 
+// Q8_0: the block's 32 int8 quants, each biased by 128 (a sign-bit flip of
+// the byte) so it converts with v_cvt_f32_ubyteN; the bias comes back out as
+// 128 * sum(x): acc = d * (sum (q + 128) x - 128 sum x).
+template <int TT>
+__device__ __forceinline__ void q8_block_dot(const KSlice& r, const SliceKit& kit, int nt,
+                                             const float (&xl)[TT][16], const float (&xh)[TT][16],
+                                             const float (&sxl)[TT], const float (&sxh)[TT], float (&acc)[TT]) {
+    const uint32_t dw[9] = {r.hdr.x, r.hdr.y, r.hdr.z, r.hdr.w, r.q.x, r.q.y, r.q.z, r.q.w, r.hb.x};
+    const float d = f16_bits_to_f32((dw[0] >> kit.dsh8) & 0xFFFFu);
+    float q[32];
+#pragma unroll
+    for (int i4 = 0; i4 < 8; ++i4) {
+        const uint32_t q4 = __builtin_amdgcn_perm(dw[i4 + 1], dw[i4], kit.sel8) ^ 0x80808080u;
+        q[4 * i4 + 0] = ubyte_f32<0>(q4);
+        q[4 * i4 + 1] = ubyte_f32<1>(q4);
+        q[4 * i4 + 2] = ubyte_f32<2>(q4);
+        q[4 * i4 + 3] = ubyte_f32<3>(q4);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        acc[t] = 0.f;
+        if (t < nt) {
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                s0 = fmaf(q[j], xl[t][j], s0);
+                s1 = fmaf(q[j + 1], xl[t][j + 1], s1);
+                s2 = fmaf(q[16 + j], xh[t][j], s2);
+                s3 = fmaf(q[16 + j + 1], xh[t][j + 1], s3);
+            }
+            acc[t] = d * (((s0 + s1) + (s2 + s3)) - 128.0f * (sxl[t] + sxh[t]));
+        }
+    }
+}
+
 template <int QT, int TT>
 __device__ __forceinline__ void kslice_dot(const KSlice& r, const SliceKit& kit, int nt, const float (&xl)[TT][16],
                                            const float (&xh)[TT][16], const float (&sxl)[TT],
                                            const float (&sxh)[TT], float (&acc)[TT]) {
-    if constexpr (KQuant<QT>::kFifth)
+    if constexpr (QT == kQ8_0)
+        q8_block_dot<TT>(r, kit, nt, xl, xh, sxl, sxh, acc);
+    else if constexpr (KQuant<QT>::kFifth)
         q5k_slice_dot<TT>(r.hdr, r.q, r.hb, kit, nt, xl, xh, sxl, sxh, acc);
     else
         q4k_slice_dot<TT>(r.hdr, r.q, kit, nt, xl, xh, sxl, sxh, acc);
@@ -305,19 +399,18 @@ __device__ __forceinline__ void dec_gateup_body(const DecArgs& a, const QMat& G,
     const int f = (wave % S::W) * kWave + lane;         // flat lane inside the unit
     const int rr = f / S::SLICES;                        // row inside the pass
     const int sl = f % S::SLICES;
-    const int b = sl >> 3, part = sl & 7;
-    const SliceKit kit = slice_kit<KQuant<QG>::kFifth>(part);
+    const SliceKit kit = kslice_kit<QG>(sl);
     const int row0 = blockIdx.x * S::ROWS;
 
-    const uint8_t* Gb = G.data + (int64_t)e * G.expert_bytes + (int64_t)b * KQuant<QG>::kBytes;
-    const uint8_t* Ub = U.data + (int64_t)e * U.expert_bytes + (int64_t)b * KQuant<QG>::kBytes;
+    const uint8_t* Gb = G.data + (int64_t)e * G.expert_bytes + kslice_block_off<QG>(sl);
+    const uint8_t* Ub = U.data + (int64_t)e * U.expert_bytes + kslice_block_off<QG>(sl);
     KSlice rg[PASSES], ru[PASSES];
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
         const int i = row0 + (ps * S::UNITS + unit) * S::P + rr;
         const int ic = i < a.I ? i : a.I - 1;   // clamp: rows past I load a valid row and are not stored
-        kslice_load<QG>(Gb + (int64_t)ic * G.row_bytes, part, rg[ps]);
-        kslice_load<QG>(Ub + (int64_t)ic * U.row_bytes, part, ru[ps]);
+        kslice_load<QG>(Gb + (int64_t)ic * G.row_bytes, sl, rg[ps]);
+        kslice_load<QG>(Ub + (int64_t)ic * U.row_bytes, sl, ru[ps]);
     }
     float xl[TT][16], xh[TT][16], sxl[TT], sxh[TT];
 #pragma unroll
@@ -446,10 +539,9 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
     const int f = (wave % S::W) * kWave + lane;
     const int rr = f / S::SLICES;
     const int sl = f % S::SLICES;
-    const int b = sl >> 3, part = sl & 7;
-    const SliceKit kit = slice_kit<KQuant<QG>::kFifth>(part);
-    const int clo = 256 * b + q4k_slice_col_lo(part);
-    const int chi = 256 * b + q4k_slice_col_hi(part);
+    const SliceKit kit = kslice_kit<QG>(sl);
+    const int clo = kslice_col_lo<QG>(sl);
+    const int chi = kslice_col_hi<QG>(sl);
     const int i = blockIdx.x * S::ROWS + unit * S::P + rr;
     const int ic = i < a.I ? i : a.I - 1;   // rows past I load a valid row and are not stored
 
@@ -482,11 +574,11 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
     KSlice rg[SM], ru[SM];
     auto issue = [&](int m, int e) {
         const uint8_t* gr = a.gate.data + (int64_t)e * a.gate.expert_bytes + (int64_t)ic * a.gate.row_bytes +
-                            (int64_t)b * KQuant<QG>::kBytes;
+                            kslice_block_off<QG>(sl);
         const uint8_t* ur = a.up.data + (int64_t)e * a.up.expert_bytes + (int64_t)ic * a.up.row_bytes +
-                            (int64_t)b * KQuant<QG>::kBytes;
-        kslice_load<QG>(gr, part, rg[m]);
-        kslice_load<QG>(ur, part, ru[m]);
+                            kslice_block_off<QG>(sl);
+        kslice_load<QG>(gr, sl, rg[m]);
+        kslice_load<QG>(ur, sl, ru[m]);
     };
     int done = 0, win = 0;
 #pragma unroll
@@ -596,16 +688,8 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
     __syncthreads();
     const int n_slots = P + (a.has_shared ? T : 0);
     const int rr = lane / NS, sl = lane % NS;
-    const SliceKit kit = slice_kit<QD == kQ5_K>(sl & 7);   // used by the k-quant rows
-    constexpr bool kq = QD != kQ8_0;
-    int c_lo, c_hi;
-    if constexpr (kq) {
-        c_lo = 256 * (sl >> 3) + q4k_slice_col_lo(sl & 7);
-        c_hi = 256 * (sl >> 3) + q4k_slice_col_hi(sl & 7);
-    } else {
-        c_lo = 32 * sl;
-        c_hi = 32 * sl + 16;
-    }
+    const SliceKit kit = kslice_kit<QD>(sl);
+    const int c_lo = kslice_col_lo<QD>(sl), c_hi = kslice_col_hi<QD>(sl);
 
     // one slot u at a time per wave: its PS passes of RP rows
     for (int u = wave; u < n_slots; u += nwaves) {
@@ -625,26 +709,12 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
         const int64_t rowb = D.row_bytes;
         const int hrow = live ? u : 0;   // the h row of slot u is u
         // all weight loads, then the h loads
-        uint4 w0[PS], w1[PS];
-        uint32_t w2[PS];
         KSlice rk[PS];
 #pragma unroll
         for (int pp = 0; pp < PS; ++pp) {   // a dead slot loads expert 0's rows, never used
-            w2[pp] = 0;
             const int o = o0 + pp * RP + rr;
             const int oc = o < a.H ? o : a.H - 1;
-            const uint8_t* row = Db + (int64_t)oc * rowb;
-            if constexpr (kq) {
-                kslice_load<kq ? QD : kQ4_K>(row + (int64_t)(sl >> 3) * KQuant<kq ? QD : kQ4_K>::kBytes, sl & 7,
-                                             rk[pp]);
-            } else {
-                // 34-byte block at a 2-byte aligned offset: 36 bytes from the dword below it
-                const uint8_t* blk = row + (int64_t)sl * 34;
-                const uint32_t* dw = reinterpret_cast<const uint32_t*>((uintptr_t)blk & ~(uintptr_t)3);
-                w0[pp] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
-                w1[pp] = make_uint4(dw[4], dw[5], dw[6], dw[7]);
-                w2[pp] = dw[8];
-            }
+            kslice_load<QD>(Db + (int64_t)oc * rowb + kslice_block_off<QD>(sl), sl, rk[pp]);
         }
         float4 hl4[4], hh4[4];
         {
@@ -670,27 +740,7 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
         for (int pp = 0; pp < PS; ++pp) {
             const int ps = pp;
             float acc[1];
-            if constexpr (kq) {
-                kslice_dot<kq ? QD : kQ4_K, 1>(rk[pp], kit, 1, hl, hh, shl, shh, acc);
-            } else {
-                const uint32_t dw[9] = {w0[pp].x, w0[pp].y, w0[pp].z, w0[pp].w,
-                                        w1[pp].x, w1[pp].y, w1[pp].z, w1[pp].w, w2[pp]};
-                const bool odd = (sl & 1) != 0;   // 34*sl is 2 mod 4 exactly for odd sl (rows 4-byte aligned)
-                const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
-                const float d = f16_bits_to_f32(odd ? (dw[0] >> 16) : (dw[0] & 0xFFFFu));
-                float s0 = 0.f;
-#pragma unroll
-                for (int i4 = 0; i4 < 8; ++i4) {
-                    const uint32_t q4 = __builtin_amdgcn_perm(dw[i4 + 1], dw[i4], sel) ^ 0x80808080u;  // q + 128
-                    const float* hv = i4 < 4 ? hl[0] : hh[0];
-                    const int j0 = 4 * (i4 & 3);
-                    s0 = fmaf(ubyte_f32<0>(q4), hv[j0 + 0], s0);
-                    s0 = fmaf(ubyte_f32<1>(q4), hv[j0 + 1], s0);
-                    s0 = fmaf(ubyte_f32<2>(q4), hv[j0 + 2], s0);
-                    s0 = fmaf(ubyte_f32<3>(q4), hv[j0 + 3], s0);
-                }
-                acc[0] = d * (s0 - 128.0f * (shl[0] + shh[0]));
-            }
+            kslice_dot<QD, 1>(rk[pp], kit, 1, hl, hh, shl, shh, acc);
             acc[0] = segment_sum<NS>(acc[0]);
             if (sl == NS - 1) s_y[hrow * RO + ps * RP + rr] = acc[0];
         }
@@ -790,7 +840,9 @@ hipError_t launch_k1_q(const DecArgs& a, hipStream_t s) {
 
 template <int NB>
 hipError_t launch_k1(const DecArgs& a, hipStream_t s) {
-    return a.gate.qtype == kQ5_K ? launch_k1_q<NB, kQ5_K>(a, s) : launch_k1_q<NB, kQ4_K>(a, s);
+    if (a.gate.qtype == kQ5_K) return launch_k1_q<NB, kQ5_K>(a, s);
+    if (a.gate.qtype == kQ8_0) return launch_k1_q<NB, kQ8_0>(a, s);
+    return launch_k1_q<NB, kQ4_K>(a, s);
 }
 
 template <int QD, int NS, int PS>
@@ -818,13 +870,13 @@ hipError_t launch_k2(const DecArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Shapes the fused decode path covers: Q4_K or Q5_K gate/up (the same format
-// for both) with H/256 in {1, 2, 4, 8, 10}; down Q4_K, Q5_K or Q8_0 with 8, 16
-// or 32 slices of 32 weights per row (I = 256, 512 or 1024); T <= 8,
+// Shapes the fused decode path covers: Q4_K, Q5_K or Q8_0 gate/up (the same
+// format for both) with H/256 in {1, 2, 4, 8, 10}; down Q4_K, Q5_K or Q8_0 with
+// 8, 16 or 32 slices of 32 weights per row (I = 256, 512 or 1024); T <= 8,
 // T*k <= 64.
 bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd) {
     if (T < 1 || T > kDecMaxT || T * k > kDecMaxPairs) return false;
-    if ((qg != kQ4_K && qg != kQ5_K) || qu != qg) return false;
+    if ((qg != kQ4_K && qg != kQ5_K && qg != kQ8_0) || qu != qg) return false;
     if (qd != kQ4_K && qd != kQ5_K && qd != kQ8_0) return false;
     const int nb = H / 256;
     if (!(nb == 1 || nb == 2 || nb == 4 || nb == 8 || nb == 10)) return false;

@@ -10,6 +10,10 @@ block (176 bytes) is drawn the same way, its 32 fifth-bit bytes included, so
 every 5-bit quant is uniform on 0..31.  A Q8_0 block is an fp16 scale
 followed by 32 int8 values uniform on -127..127.
 d, dmin and the Q8_0 scale are fp16(|N(0,1)| * 0.01) (round to nearest even).
+A Q5_1 block is 24 random bytes (quants uniform on 0..31) with d =
+fp16(|N(0,1)| * 0.01) and offset m = fp16(-|N(0,1)| * 0.16): a block of
+weights spread over [min, max] stores m = min and d = (max - min)/31, so m
+sits near -16 d.
 
 Host arrays come from numpy's PCG64; large banks are drawn on the device with
 torch's generator so that tens of GB never cross PCIe.  The oracle reads back
@@ -26,8 +30,9 @@ import numpy as np
 Q8_0 = 8
 Q4_K = 12
 Q5_K = 13
-BLOCK_WEIGHTS = {Q4_K: 256, Q5_K: 256, Q8_0: 32}
-BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q8_0: 34}
+Q5_1 = 7
+BLOCK_WEIGHTS = {Q4_K: 256, Q5_K: 256, Q8_0: 32, Q5_1: 32}
+BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q8_0: 34, Q5_1: 24}
 
 
 def row_bytes(qtype: int, cols: int) -> int:
@@ -69,10 +74,23 @@ def q80_blocks_np(g: np.random.Generator, n_blocks: int) -> np.ndarray:
     return b
 
 
+def q51_blocks_np(g: np.random.Generator, n_blocks: int) -> np.ndarray:
+    b = g.integers(0, 256, size=(n_blocks, 24), dtype=np.uint8)
+    b[:, 0:2] = _scale_f16(g, n_blocks).view(np.uint8).reshape(n_blocks, 2)
+    m = (-np.abs(g.standard_normal(n_blocks, dtype=np.float32)) * np.float32(0.16)).astype(np.float16)
+    b[:, 2:4] = m.view(np.uint8).reshape(n_blocks, 2)
+    return b
+
+
 def bank_np(g: np.random.Generator, qtype: int, n_experts: int, rows: int, cols: int) -> np.ndarray:
     """[n_experts][rows][row_bytes] uint8."""
     nb = n_experts * rows * (cols // BLOCK_WEIGHTS[qtype])
-    blocks = q80_blocks_np(g, nb) if qtype == Q8_0 else q4k_blocks_np(g, nb, BLOCK_BYTES[qtype])
+    if qtype == Q8_0:
+        blocks = q80_blocks_np(g, nb)
+    elif qtype == Q5_1:
+        blocks = q51_blocks_np(g, nb)
+    else:
+        blocks = q4k_blocks_np(g, nb, BLOCK_BYTES[qtype])
     return blocks.reshape(n_experts, rows, row_bytes(qtype, cols))
 
 
@@ -113,6 +131,9 @@ def bank_torch(gen, qtype: int, n_experts: int, rows: int, cols: int, device):
         sl = out[s0:s0 + n]
         sc = (torch.randn((n, 1 if qtype == Q8_0 else 2), generator=gen, device=device,
                           dtype=torch.float32).abs_() * 0.01).to(torch.float16)
+        if qtype == Q5_1:
+            sc[:, 1:2] = (torch.randn((n, 1), generator=gen, device=device, dtype=torch.float32).abs_()
+                          * -0.16).to(torch.float16)
         if qtype != Q8_0:
             sl.copy_(torch.randint(0, 256, (n, bb), generator=gen, device=device, dtype=torch.uint8))
             sl[:, 0:4] = sc.view(torch.uint8).view(n, 4)

@@ -463,3 +463,26 @@ def test_q5k_decode_layers(name, T, over, fused):
     bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused)
     _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
     _check_routing(bufs.routing, logits, w.top_k)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name,T,over", [
+    ("sage_decode", 1, dict(n_experts=64, qt_gate=oracle.Q8_0, qt_up=oracle.Q8_0)),
+    ("sage_decode", 3, dict(n_experts=64, qt_gate=oracle.Q8_0, qt_up=oracle.Q8_0, qt_down=oracle.Q8_0)),
+    ("flash_next_decode", 1, dict(n_experts=64, qt_gate=oracle.Q8_0, qt_up=oracle.Q8_0)),   # Q8_0 down, shared
+    ("flash_next_decode", 6, dict(n_experts=64, qt_gate=oracle.Q8_0, qt_up=oracle.Q8_0, qt_down=oracle.Q5_K)),
+])
+def test_q8_gateup_decode_layers(name, T, over, fused):
+    """Q8_0 gate/up experts (the Q8_0 of the "Strata v0.1.31" Unsloth bullet, here
+    on the gate and up projections too): the two-kernel layer gives each lane one
+    34-byte block of a row (odd blocks start 2 bytes past a dword); the shared
+    expert's 4-token groups run at 6 tokens."""
+    m = qm()
+    _say("q8_0 gate/up decode", name, T, over, fused)
+    from quantized_moe_ffn_amd import layers
+    w = synth.Workload(**{**synth.WORKLOADS[name].__dict__, **over, "tokens": T})
+    dl = layers.make_layer(w, seed=23, index=0, device=DEV)
+    logits, x = layers.inputs_np(w, seed=23)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused)
+    _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
+    _check_routing(bufs.routing, logits, w.top_k)

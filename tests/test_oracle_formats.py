@@ -235,3 +235,84 @@ def test_q5k_single_bit_sensitivity():
         diff = np.nonzero(w != base)[0]
         assert list(diff) == [32 * b + l]
         assert abs(w[32 * b + l] - base[32 * b + l]) == 16 * 0.5 * f["sc"][b]
+
+
+# ---------------------------------------------------------------------------- Q5_1
+# Q5_1 is among the expert formats of the Unsloth UD-Q4_K_XL files that the
+# "Strata v0.1.31" release notes say run natively: 32-weight blocks with a
+# scale, an additive offset and five-bit quants (public GGUF layout, reading
+# R-layout in the oracle).
+
+def test_q51_unpack_pack_roundtrip_random_bytes():
+    g = np.random.default_rng(31)
+    for _ in range(300):
+        blk = g.integers(0, 256, 24, dtype=np.uint8)
+        f = oracle.q51_unpack(blk)
+        assert f["q"].min() >= 0 and f["q"].max() <= 31
+        assert np.array_equal(oracle.q51_pack(f["d_bits"], f["m_bits"], f["q"]), blk)
+
+
+def test_q51_pack_unpack_roundtrip_random_fields():
+    g = np.random.default_rng(32)
+    for _ in range(300):
+        d, m = (int(v) for v in g.integers(0, 65536, 2))
+        q = g.integers(0, 32, 32)
+        f = oracle.q51_unpack(oracle.q51_pack(d, m, q))
+        assert f["d_bits"] == d and f["m_bits"] == m and np.array_equal(f["q"], q)
+
+
+def test_q51_block_g_closed_form():
+    blk = load_block("q51_block_g.txt")
+    assert blk.size == 24
+    f = oracle.q51_unpack(blk)
+    i = np.arange(32)
+    assert np.array_equal(f["q"], (11 * i + 4 * (i // 16) + 3) % 32)
+    assert f["d_bits"] == 0x3400 and f["m_bits"] == 0xC200
+    w = oracle.q51_dequant(blk)
+    assert np.array_equal(w, 0.25 * ((11 * i + 4 * (i // 16) + 3) % 32) - 3.0)
+    assert (w[0], w[5], w[16], w[31]) == (-2.25, 3.5, 2.75, 4.0)
+    assert w.sum() == 28.0
+
+
+def test_q51_single_bit_sensitivity():
+    """Flipping bit i of qh changes weight i alone, by 16*d; flipping bit b of qs[l]
+    changes weight l (b < 4) or 16+l (b >= 4) alone, by 2^(b mod 4)*d."""
+    blk = load_block("q51_block_g.txt")
+    base = oracle.q51_dequant(blk)
+    for i in [0, 1, 7, 15, 16, 20, 31]:
+        mod = blk.copy()
+        mod[4 + i // 8] ^= 1 << (i % 8)
+        w = oracle.q51_dequant(mod)
+        assert list(np.nonzero(w != base)[0]) == [i]
+        assert abs(w[i] - base[i]) == 16 * 0.25
+    for l, b in [(0, 0), (3, 2), (9, 4), (15, 7)]:
+        mod = blk.copy()
+        mod[8 + l] ^= 1 << b
+        w = oracle.q51_dequant(mod)
+        idx = l if b < 4 else 16 + l
+        assert list(np.nonzero(w != base)[0]) == [idx]
+        assert abs(w[idx] - base[idx]) == 2 ** (b % 4) * 0.25
+
+
+def test_q51_with_offset_minus_16d_is_q80():
+    """m = -16*d turns a Q5_1 block into the Q8_0 block with the same d and quants
+    q - 16 (in -16..15): the two formats' definitions agree value for value."""
+    g = np.random.default_rng(33)
+    for d_bits, m_bits in [(0x2C00, 0xBC00), (0x3400, 0xC400), (0x1E00, 0xAE00)]:   # d, -16 d
+        d = oracle.fp16_to_f64(np.array([d_bits], np.uint16))[0]
+        assert oracle.fp16_to_f64(np.array([m_bits], np.uint16))[0] == -16 * d
+        for _ in range(20):
+            q = g.integers(0, 32, 32)
+            q5 = oracle.q51_pack(d_bits, m_bits, q)
+            q8 = np.concatenate([np.array([d_bits & 0xFF, d_bits >> 8], np.uint8),
+                                 (q - 16).astype(np.int8).view(np.uint8)])
+            assert np.array_equal(oracle.q51_dequant(q5), oracle.q80_dequant(q8))
+
+
+def test_q51_dequant_is_exact_at_the_extremes():
+    """Largest |d*q| against the smallest offset: the sum needs 44 bits, still exact in fp64."""
+    q = np.full(32, 31)
+    blk = oracle.q51_pack(0x7BFF, 0x0001, q)           # d = 65504, m = 2^-24
+    w = oracle.q51_dequant(blk)
+    assert np.all(w == 65504.0 * 31 + 2.0 ** -24)
+    assert np.all(w - 65504.0 * 31 == 2.0 ** -24)
