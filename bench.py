@@ -262,7 +262,7 @@ def main() -> int:
 
 
 def fmt(qt):
-    return {8: "Q8_0", 12: "Q4_K", 13: "Q5_K"}[qt]
+    return {7: "Q5_1", 8: "Q8_0", 12: "Q4_K", 13: "Q5_K"}[qt]
 
 
 def cpu_baseline(w, stack, inputs, bufs, flags, k, budget_s):

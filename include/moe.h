@@ -64,11 +64,16 @@ typedef enum moe_status {
  *             bytes holding the fifth bit of every quant, then the low 4 bits
  *             as Q4_K's quants; q in 0..31, w = d*sc*q - dmin*m.
  *   MOE_Q8_0: 34-byte block of 32 weights: fp16 d, 32 int8 q; w = d*q.
- * Q4_K and Q5_K banks must be 16-byte aligned, Q8_0 banks 2-byte aligned.
- * The two-kernel decode layer takes Q4_K or Q5_K gate/up (one format for
- * both) with Q4_K, Q5_K or Q8_0 down; the int8 MFMA GEMMs take Q4_K
- * throughout; other mixes run on the general kernels of the chosen path. */
-enum { MOE_Q8_0 = 8, MOE_Q4_K = 12, MOE_Q5_K = 13 };
+ *   MOE_Q5_1: 24-byte block of 32 weights: fp16 d, fp16 m, a 32-bit
+ *             little-endian word whose bit i is the fifth bit of quant i, 16
+ *             bytes of low 4 bits (byte l: quant l in the low nibble, quant
+ *             16+l in the high nibble); q in 0..31, w = d*q + m.
+ * Q4_K and Q5_K banks must be 16-byte aligned, Q5_1 banks 8-byte aligned,
+ * Q8_0 banks 2-byte aligned.  The two-kernel decode layer takes gate/up in
+ * any of the four formats (one format for both) with down in any of them;
+ * the int8 MFMA GEMMs take Q4_K throughout; other mixes run on the general
+ * kernels of the chosen path. */
+enum { MOE_Q5_1 = 7, MOE_Q8_0 = 8, MOE_Q4_K = 12, MOE_Q5_K = 13 };
 
 /* moe_route_topk flags */
 enum { MOE_ROUTE_RENORM = 1u }; /* weights = softmax over the k selected logits */
@@ -184,7 +189,7 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_
  * result of moe_route_topk for the same T, k and E (read on the device: no host
  * synchronisation).
  * Checks: shapes consistent with L; H, I multiples of 256; qtypes supported
- * (gate/up/down: Q4_K, Q5_K or Q8_0); alignment; workspace size. */
+ * (gate/up/down: Q4_K, Q5_K, Q8_0 or Q5_1); alignment; workspace size. */
 moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T, int32_t k,
                             const float* x, const int8_t* xq, const float* xd, uint32_t flags,
                             float* y_pair, float* y_shared, void* workspace, size_t ws_bytes,
@@ -205,9 +210,9 @@ size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uin
 /* The whole layer: routing (as moe_route_topk, results written to r), expert
  * FFN (as moe_expert_ffn_q, from fp32 x; on the int8 path x is quantized with
  * moe_quantize_act's rule into the workspace) and combine (as moe_combine),
- * enqueued on one stream.  For decode batches (T <= 8, T*k <= 64, Q4_K or
- * Q5_K gate/up with H/256 in {1,2,4,8,10}, Q4_K, Q5_K or Q8_0 down rows of 8,
- * 16 or 32 32-weight blocks, 16-byte aligned banks) the layer runs as two
+ * enqueued on one stream.  For decode batches (T <= 8, T*k <= 64, gate/up of
+ * one format with H/256 in {1,2,4,8,10}, down rows of 8, 16 or 32 32-weight
+ * blocks, 16-byte aligned banks) the layer runs as two
  * kernels: routing fused into the gate/up kernel (each wave recomputes the
  * top-k of its token) and the combine fused into the down kernel (formed in
  * slot order in LDS); other shapes run the separate stages.  Same results
@@ -223,8 +228,8 @@ moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, 
 
 /* Test hook: dequantize n_weights weights of contiguous blocks to fp32 with the
  * same device unpacking helpers the FFN kernels use.  Each value is the exact
- * d*sc*q - dmin*m (Q4_K) or d*q (Q8_0) rounded once to fp32.  n_weights must
- * be a multiple of the block size. */
+ * d*sc*q - dmin*m (Q4_K, Q5_K), d*q (Q8_0) or d*q + m (Q5_1) rounded once to
+ * fp32.  n_weights must be a multiple of the block size. */
 moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, float* out,
                          hipStream_t stream);
 

@@ -24,14 +24,15 @@ MOE_OK = 0
 MOE_Q8_0 = 8
 MOE_Q4_K = 12
 MOE_Q5_K = 13
+MOE_Q5_1 = 7
 MOE_ROUTE_RENORM = 1
 MOE_FFN_AUTO = 0
 AUTO_DECODE_MAX_T = 8   # MOE_FFN_AUTO takes the fp-activation path up to this many tokens
 MOE_FFN_DECODE = 1
 MOE_FFN_INT8 = 2
 
-BLOCK_WEIGHTS = {MOE_Q4_K: 256, MOE_Q5_K: 256, MOE_Q8_0: 32}
-BLOCK_BYTES = {MOE_Q4_K: 144, MOE_Q5_K: 176, MOE_Q8_0: 34}
+BLOCK_WEIGHTS = {MOE_Q4_K: 256, MOE_Q5_K: 256, MOE_Q8_0: 32, MOE_Q5_1: 32}
+BLOCK_BYTES = {MOE_Q4_K: 144, MOE_Q5_K: 176, MOE_Q8_0: 34, MOE_Q5_1: 24}
 
 EXPORTS = (
     "moe_abi_version", "moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",

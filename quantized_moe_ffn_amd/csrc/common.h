@@ -17,6 +17,7 @@
 
 namespace moe {
 
+constexpr int kQ5_1 = 7;
 constexpr int kQ8_0 = 8;
 constexpr int kQ4_K = 12;
 constexpr int kQ5_K = 13;

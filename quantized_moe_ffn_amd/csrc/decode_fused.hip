@@ -26,7 +26,7 @@
 // Weight streaming (K1): a "slice" is 16 quant bytes of a Q4_K super-block =
 // 16 weights of sub-block 2c (low nibbles) and 16 of sub-block 2c+1 (high
 // nibbles); a Q5_K slice adds the 16 bytes holding those weights' fifth bits;
-// a Q8_0 row's lane takes one 34-byte block (32 weights) instead.  A unit of W
+// a Q8_0 or Q5_1 row's lane takes one 34- or 24-byte block (32 weights) instead.  A unit of W
 // waves covers P rows x (8*NB) slices per pass with
 // 64*W == P*8*NB, so every lane keeps the same 32 columns for the whole kernel
 // and holds those activations in registers (no LDS traffic for x).  Per slice a
@@ -181,10 +181,16 @@ struct KSlice {
 // Lane sl of a row: a k-quant row has 8 slices per 256-weight super-block
 // (super-block sl/8, part sl%8); a Q8_0 row has one 32-weight block per lane
 // (block sl, columns 32*sl .. 32*sl + 31).  Both give H/32 lanes per row.
+// (Q5_1 rows, 24-byte blocks of 32 weights, are laid out per lane as Q8_0's.)
+template <int QT>
+constexpr bool kBlock32 = (QT == kQ8_0 || QT == kQ5_1);
+
 template <int QT>
 __device__ __forceinline__ int kslice_block_off(int sl) {
     if constexpr (QT == kQ8_0)
         return 34 * sl;
+    else if constexpr (QT == kQ5_1)
+        return 24 * sl;
     else
         return (sl >> 3) * KQuant<QT>::kBytes;
 }
@@ -192,14 +198,14 @@ __device__ __forceinline__ int kslice_block_off(int sl) {
 // First column of the lane's low and high halves (16 weights each).
 template <int QT>
 __device__ __forceinline__ int kslice_col_lo(int sl) {
-    if constexpr (QT == kQ8_0)
+    if constexpr (kBlock32<QT>)
         return 32 * sl;
     else
         return 256 * (sl >> 3) + q4k_slice_col_lo(sl & 7);
 }
 template <int QT>
 __device__ __forceinline__ int kslice_col_hi(int sl) {
-    if constexpr (QT == kQ8_0)
+    if constexpr (kBlock32<QT>)
         return 32 * sl + 16;
     else
         return 256 * (sl >> 3) + q4k_slice_col_hi(sl & 7);
@@ -217,6 +223,8 @@ __device__ __forceinline__ SliceKit kslice_kit(int sl) {
         k.sel8 = odd ? 0x07060504u : 0x05040302u;
         k.dsh8 = odd ? 16u : 0u;
         return k;
+    } else if constexpr (QT == kQ5_1) {
+        return SliceKit{};
     } else {
         return slice_kit<KQuant<QT>::kFifth>(sl & 7);
     }
@@ -230,6 +238,12 @@ __device__ __forceinline__ void kslice_load(const uint8_t* blk, int sl, KSlice& 
         r.hdr = make_uint4(dw[0], dw[1], dw[2], dw[3]);
         r.q = make_uint4(dw[4], dw[5], dw[6], dw[7]);
         r.hb = make_uint4(dw[8], 0u, 0u, 0u);
+    } else if constexpr (QT == kQ5_1) {
+        // 24 bytes at an 8-byte aligned offset: {d | m << 16, qh, qs[0..15]}
+        const uint2* p = reinterpret_cast<const uint2*>(blk);
+        const uint2 v0 = p[0], v1 = p[1], v2 = p[2];
+        r.hdr = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        r.q = make_uint4(v2.x, v2.y, 0u, 0u);
     } else {
         const int part = sl & 7;
         r.hdr = *reinterpret_cast<const uint4*>(blk);
@@ -363,12 +377,59 @@ __device__ __forceinline__ void q8_block_dot(const KSlice& r, const SliceKit& ki
     }
 }
 
+// Q5_1: quant l of the block = low nibble of qs byte l + 16 * qh bit l, quant
+// 16 + l = its high nibble + 16 * qh bit 16 + l.  Four qh bits go to bit 4 of
+// four bytes at once: (v & 15) * 0x00204081 puts bit i of v at bit 8i (i + 7i)
+// with no overlap between the shifted copies below bit 32 that survive the
+// 0x01010101 mask.  acc = d * sum q x + m * sum x.
+__device__ __forceinline__ uint32_t q51_spread4(uint32_t v) { return ((v & 15u) * 0x00204081u) & 0x01010101u; }
+
+template <int TT>
+__device__ __forceinline__ void q51_block_dot(const KSlice& r, int nt, const float (&xl)[TT][16],
+                                              const float (&xh)[TT][16], const float (&sxl)[TT],
+                                              const float (&sxh)[TT], float (&acc)[TT]) {
+    const float d = f16_bits_to_f32(r.hdr.x & 0xFFFFu), m = f16_bits_to_f32(r.hdr.x >> 16);
+    const uint32_t qh = r.hdr.y;
+    const uint32_t qw[4] = {r.hdr.z, r.hdr.w, r.q.x, r.q.y};
+    float ql[16], qv[16];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+        const uint32_t lo = (qw[i4] & 0x0F0F0F0Fu) | (q51_spread4(qh >> (4 * i4)) << 4);
+        const uint32_t hi = ((qw[i4] >> 4) & 0x0F0F0F0Fu) | (q51_spread4(qh >> (16 + 4 * i4)) << 4);
+        ql[4 * i4 + 0] = ubyte_f32<0>(lo);
+        ql[4 * i4 + 1] = ubyte_f32<1>(lo);
+        ql[4 * i4 + 2] = ubyte_f32<2>(lo);
+        ql[4 * i4 + 3] = ubyte_f32<3>(lo);
+        qv[4 * i4 + 0] = ubyte_f32<0>(hi);
+        qv[4 * i4 + 1] = ubyte_f32<1>(hi);
+        qv[4 * i4 + 2] = ubyte_f32<2>(hi);
+        qv[4 * i4 + 3] = ubyte_f32<3>(hi);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        acc[t] = 0.f;
+        if (t < nt) {
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                s0 = fmaf(ql[j], xl[t][j], s0);
+                s1 = fmaf(ql[j + 1], xl[t][j + 1], s1);
+                s2 = fmaf(qv[j], xh[t][j], s2);
+                s3 = fmaf(qv[j + 1], xh[t][j + 1], s3);
+            }
+            acc[t] = d * ((s0 + s1) + (s2 + s3)) + m * (sxl[t] + sxh[t]);
+        }
+    }
+}
+
 template <int QT, int TT>
 __device__ __forceinline__ void kslice_dot(const KSlice& r, const SliceKit& kit, int nt, const float (&xl)[TT][16],
                                            const float (&xh)[TT][16], const float (&sxl)[TT],
                                            const float (&sxh)[TT], float (&acc)[TT]) {
     if constexpr (QT == kQ8_0)
         q8_block_dot<TT>(r, kit, nt, xl, xh, sxl, sxh, acc);
+    else if constexpr (QT == kQ5_1)
+        q51_block_dot<TT>(r, nt, xl, xh, sxl, sxh, acc);
     else if constexpr (KQuant<QT>::kFifth)
         q5k_slice_dot<TT>(r.hdr, r.q, r.hb, kit, nt, xl, xh, sxl, sxh, acc);
     else
@@ -842,6 +903,7 @@ template <int NB>
 hipError_t launch_k1(const DecArgs& a, hipStream_t s) {
     if (a.gate.qtype == kQ5_K) return launch_k1_q<NB, kQ5_K>(a, s);
     if (a.gate.qtype == kQ8_0) return launch_k1_q<NB, kQ8_0>(a, s);
+    if (a.gate.qtype == kQ5_1) return launch_k1_q<NB, kQ5_1>(a, s);
     return launch_k1_q<NB, kQ4_K>(a, s);
 }
 
@@ -870,17 +932,17 @@ hipError_t launch_k2(const DecArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Shapes the fused decode path covers: Q4_K, Q5_K or Q8_0 gate/up (the same
-// format for both) with H/256 in {1, 2, 4, 8, 10}; down Q4_K, Q5_K or Q8_0 with
-// 8, 16 or 32 slices of 32 weights per row (I = 256, 512 or 1024); T <= 8,
-// T*k <= 64.
+// Shapes the fused decode path covers: Q4_K, Q5_K, Q8_0 or Q5_1 gate/up (the
+// same format for both) with H/256 in {1, 2, 4, 8, 10}; down in any of those
+// formats with 8, 16 or 32 lanes of 32 weights per row (I = 256, 512 or 1024);
+// T <= 8, T*k <= 64.
 bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd) {
+    auto known = [](int q) { return q == kQ4_K || q == kQ5_K || q == kQ8_0 || q == kQ5_1; };
     if (T < 1 || T > kDecMaxT || T * k > kDecMaxPairs) return false;
-    if ((qg != kQ4_K && qg != kQ5_K && qg != kQ8_0) || qu != qg) return false;
-    if (qd != kQ4_K && qd != kQ5_K && qd != kQ8_0) return false;
+    if (!known(qg) || qu != qg || !known(qd)) return false;
     const int nb = H / 256;
     if (!(nb == 1 || nb == 2 || nb == 4 || nb == 8 || nb == 10)) return false;
-    const int ns = (qd == kQ8_0) ? I / 32 : 8 * (I / 256);
+    const int ns = I / 32;   // lanes per down row, every format
     return ns == 8 || ns == 16 || ns == 32;
 }
 
@@ -888,7 +950,7 @@ namespace {
 
 template <int QD>
 hipError_t launch_k2_q(const DecArgs& a, hipStream_t s) {
-    const int ns = (QD == kQ8_0) ? a.I / 32 : 8 * (a.I / 256);
+    const int ns = a.I / 32;
     if (ns == 8) return launch_k2<QD, 8>(a, s);
     if (ns == 16) return launch_k2<QD, 16>(a, s);
     return launch_k2<QD, 32>(a, s);
@@ -908,6 +970,7 @@ hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (a.down.qtype == kQ4_K) return launch_k2_q<kQ4_K>(a, s);
     if (a.down.qtype == kQ5_K) return launch_k2_q<kQ5_K>(a, s);
+    if (a.down.qtype == kQ5_1) return launch_k2_q<kQ5_1>(a, s);
     return launch_k2_q<kQ8_0>(a, s);
 }
 

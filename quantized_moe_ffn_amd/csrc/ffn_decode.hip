@@ -94,6 +94,26 @@ __device__ __forceinline__ void row_partial(const uint8_t* __restrict__ row, int
                           s.s.dmin * ((float)s.s.m_lo * xlo + (float)s.s.m_hi * xhi);
             }
         }
+    } else if constexpr (QT == kQ5_1) {
+        // sum w x = d * sum q x + m * sum x over the block's 32 weights
+        const int nblocks = cols >> 5;
+        for (int b = lane; b < nblocks; b += kWave) {
+            Q51Block blk;
+            q51_load(row + (int64_t)b * 24, blk);
+            float q[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) q[i] = (float)q51_quant(blk, i);
+            for (int t = 0; t < nt; ++t) {
+                const float* xv = xs + t * xstride + 32 * b;
+                float sq = 0.f, sx = 0.f;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    sq = fmaf(q[i], xv[i], sq);
+                    sx += xv[i];
+                }
+                acc[t] += blk.d * sq + blk.m * sx;
+            }
+        }
     } else {
         const int nblocks = cols >> 5;
         for (int b = lane; b < nblocks; b += kWave) {
@@ -299,6 +319,7 @@ template <int QG>
 hipError_t launch_gateup_g(const FfnArgs& a, int xmode, hipStream_t s) {
     if (a.up.qtype == kQ4_K) return launch_gateup_q<QG, kQ4_K>(a, xmode, s);
     if (a.up.qtype == kQ5_K) return launch_gateup_q<QG, kQ5_K>(a, xmode, s);
+    if (a.up.qtype == kQ5_1) return launch_gateup_q<QG, kQ5_1>(a, xmode, s);
     return launch_gateup_q<QG, kQ8_0>(a, xmode, s);
 }
 
@@ -307,12 +328,14 @@ hipError_t launch_gateup_g(const FfnArgs& a, int xmode, hipStream_t s) {
 hipError_t launch_gateup(const FfnArgs& a, int xmode, hipStream_t s) {
     if (a.gate.qtype == kQ4_K) return launch_gateup_g<kQ4_K>(a, xmode, s);
     if (a.gate.qtype == kQ5_K) return launch_gateup_g<kQ5_K>(a, xmode, s);
+    if (a.gate.qtype == kQ5_1) return launch_gateup_g<kQ5_1>(a, xmode, s);
     return launch_gateup_g<kQ8_0>(a, xmode, s);
 }
 
 hipError_t launch_down(const FfnArgs& a, int hmode, hipStream_t s) {
     if (a.down.qtype == kQ4_K) return launch_down_q<kQ4_K>(a, hmode, s);
     if (a.down.qtype == kQ5_K) return launch_down_q<kQ5_K>(a, hmode, s);
+    if (a.down.qtype == kQ5_1) return launch_down_q<kQ5_1>(a, hmode, s);
     return launch_down_q<kQ8_0>(a, hmode, s);
 }
 
@@ -435,6 +458,18 @@ __global__ void __launch_bounds__(256) dequant_q80_kernel(const uint8_t* __restr
     for (int i = 0; i < 32; ++i) out[b * 32 + i] = blk.d * (float)q80_quant(blk, i);
 }
 
+// w = fmaf(d, q, m): d*q is exact in fp32 (11 + 5 significant bits), so the
+// weight is d*q + m rounded once.
+__global__ void __launch_bounds__(256) dequant_q51_kernel(const uint8_t* __restrict__ blocks,
+                                                          int64_t n_blocks, float* __restrict__ out) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n_blocks) return;
+    Q51Block blk;
+    q51_load(blocks + b * 24, blk);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) out[b * 32 + i] = fmaf(blk.d, (float)q51_quant(blk, i), blk.m);
+}
+
 hipError_t launch_dequant(const void* blocks, int qtype, int64_t n_weights, float* out, hipStream_t s) {
     if (qtype == kQ4_K) {
         const int64_t n = n_weights / 256 * 8;
@@ -442,6 +477,9 @@ hipError_t launch_dequant(const void* blocks, int qtype, int64_t n_weights, floa
     } else if (qtype == kQ5_K) {
         const int64_t n = n_weights / 256 * 8;
         dequant_q5k_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint8_t*)blocks, n, out);
+    } else if (qtype == kQ5_1) {
+        const int64_t n = n_weights / 32;
+        dequant_q51_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint8_t*)blocks, n, out);
     } else {
         const int64_t n = n_weights / 32;
         dequant_q80_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint8_t*)blocks, n, out);

@@ -33,10 +33,11 @@ moe_status from_hip(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool known_qtype(int qt) { return qt == MOE_Q4_K || qt == MOE_Q5_K || qt == MOE_Q8_0; }
-int blk_weights(int qt) { return qt == MOE_Q8_0 ? 32 : 256; }
-int blk_bytes(int qt) { return qt == MOE_Q4_K ? 144 : (qt == MOE_Q5_K ? 176 : 34); }
-size_t blk_align(int qt) { return qt == MOE_Q8_0 ? 2 : 16; }   // Q4_K, Q5_K blocks are 16-byte multiples
+bool known_qtype(int qt) { return qt == MOE_Q4_K || qt == MOE_Q5_K || qt == MOE_Q8_0 || qt == MOE_Q5_1; }
+int blk_weights(int qt) { return (qt == MOE_Q8_0 || qt == MOE_Q5_1) ? 32 : 256; }
+int blk_bytes(int qt) { return qt == MOE_Q4_K ? 144 : (qt == MOE_Q5_K ? 176 : (qt == MOE_Q5_1 ? 24 : 34)); }
+// Q4_K, Q5_K blocks are 16-byte multiples; Q5_1 blocks (24 bytes) are read as 8-byte words
+size_t blk_align(int qt) { return qt == MOE_Q8_0 ? 2 : (qt == MOE_Q5_1 ? 8 : 16); }
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
@@ -49,8 +50,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 moe_status check_qmatrix(const moe_qmatrix& m, const char* name, int rows, int cols, int n_experts) {
     if (!m.data) return fail(MOE_ERR_INVALID_ARGUMENT, "%s.data is NULL", name);
     if (!known_qtype(m.qtype))
-        return fail(MOE_ERR_UNSUPPORTED, "%s.qtype = %d: supported are Q4_K (%d), Q5_K (%d) and Q8_0 (%d)", name,
-                    m.qtype, MOE_Q4_K, MOE_Q5_K, MOE_Q8_0);
+        return fail(MOE_ERR_UNSUPPORTED, "%s.qtype = %d: supported are Q4_K (%d), Q5_K (%d), Q8_0 (%d) and Q5_1 (%d)",
+                    name, m.qtype, MOE_Q4_K, MOE_Q5_K, MOE_Q8_0, MOE_Q5_1);
     if (m.rows != rows || m.cols != cols)
         return fail(MOE_ERR_INVALID_ARGUMENT, "%s is %d x %d, expected %d x %d", name, m.rows, m.cols,
                     rows, cols);
@@ -417,8 +418,8 @@ moe_status moe_combine(const float* y_pair, const float* w, const float* y_share
 moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, float* out, hipStream_t stream) {
     if (!blocks || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "blocks or out is NULL");
     if (!known_qtype(qtype))
-        return fail(MOE_ERR_UNSUPPORTED, "qtype = %d: supported are Q4_K (%d), Q5_K (%d) and Q8_0 (%d)", qtype,
-                    MOE_Q4_K, MOE_Q5_K, MOE_Q8_0);
+        return fail(MOE_ERR_UNSUPPORTED, "qtype = %d: supported are Q4_K (%d), Q5_K (%d), Q8_0 (%d) and Q5_1 (%d)",
+                    qtype, MOE_Q4_K, MOE_Q5_K, MOE_Q8_0, MOE_Q5_1);
     if (n_weights < 0 || n_weights % blk_weights(qtype) != 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "n_weights = %lld is not a multiple of the block size %d",
                     (long long)n_weights, blk_weights(qtype));

@@ -1,4 +1,4 @@
-// qblock.h — device-side unpacking of Q4_K, Q5_K and Q8_0 blocks, shared by the FFN
+// qblock.h — device-side unpacking of Q4_K, Q5_K, Q8_0 and Q5_1 blocks, shared by the FFN
 // kernels and the dequantization test hook (so the hook exercises the exact
 // loads, nibble splits and scale decoding the FFN kernels use).
 #pragma once
@@ -98,6 +98,35 @@ __device__ __forceinline__ void q80_load(const uint8_t* __restrict__ blk, Q80Blo
 
 __device__ __forceinline__ int q80_quant(const Q80Block& b, int i) {
     return (int)(int8_t)((b.q[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+}
+
+// Q5_1 block: 24 bytes, 8-byte aligned (row starts and 24-byte blocks):
+// fp16 d, fp16 m, a 32-bit word qh whose bit i is the fifth bit of quant i, and
+// 16 bytes qs whose byte l holds the low four bits of quant l (low nibble) and
+// of quant 16 + l (high nibble); w = d*q + m.
+struct Q51Block {
+    float d, m;
+    uint32_t qh;
+    uint32_t qs[4];
+};
+
+__device__ __forceinline__ void q51_load(const uint8_t* __restrict__ blk, Q51Block& b) {
+    const uint2* p = reinterpret_cast<const uint2*>(blk);
+    const uint2 v0 = p[0], v1 = p[1], v2 = p[2];
+    b.d = f16_bits_to_f32(v0.x & 0xFFFFu);
+    b.m = f16_bits_to_f32(v0.x >> 16);
+    b.qh = v0.y;
+    b.qs[0] = v1.x;
+    b.qs[1] = v1.y;
+    b.qs[2] = v2.x;
+    b.qs[3] = v2.y;
+}
+
+__device__ __forceinline__ int q51_quant(const Q51Block& b, int i) {
+    const int l = i & 15;
+    const uint32_t byte = (b.qs[l >> 2] >> (8 * (l & 3))) & 0xFFu;
+    const uint32_t low4 = i < 16 ? (byte & 15u) : (byte >> 4);
+    return (int)(low4 | (((b.qh >> i) & 1u) << 4));
 }
 
 }  // namespace moe

@@ -33,7 +33,12 @@ def _say(*a):
 # --------------------------------------------------------------------------- dequantization
 
 def _finite_scale_blocks(g, n, qt):
-    b = synth.q80_blocks_np(g, n) if qt == oracle.Q8_0 else synth.q4k_blocks_np(g, n, oracle.BLOCK_BYTES[qt])
+    if qt == oracle.Q8_0:
+        b = synth.q80_blocks_np(g, n)
+    elif qt == oracle.Q5_1:
+        b = synth.q51_blocks_np(g, n)
+    else:
+        b = synth.q4k_blocks_np(g, n, oracle.BLOCK_BYTES[qt])
     # random fp16 scale bit patterns, finite (subnormals included)
     bits = g.integers(0, 0x7C00, size=(n, 1 if qt == oracle.Q8_0 else 2), dtype=np.uint16)
     bits |= (g.integers(0, 2, size=bits.shape, dtype=np.uint16) << 15)
@@ -41,7 +46,7 @@ def _finite_scale_blocks(g, n, qt):
     return b
 
 
-@pytest.mark.parametrize("qt", [oracle.Q4_K, oracle.Q5_K, oracle.Q8_0])
+@pytest.mark.parametrize("qt", [oracle.Q4_K, oracle.Q5_K, oracle.Q8_0, oracle.Q5_1])
 def test_dequant_bit_exact(qt):
     m = qm()
     from tests.golden import load_block
@@ -52,6 +57,8 @@ def test_dequant_bit_exact(qt):
                                                   "q4k_block_e.txt")])
     elif qt == oracle.Q5_K:
         gold = load_block("q5k_block_f.txt")[None]
+    elif qt == oracle.Q5_1:
+        gold = load_block("q51_block_g.txt")[None]
     else:
         gold = load_block("q80_block.txt")[None]
     blocks = np.concatenate([gold, blocks])
@@ -264,6 +271,8 @@ def test_int8_prefill_chunk_sampled():
     dict(hidden=512, inter=256, n_experts=8, top_k=2, tokens=20, qt_down=oracle.Q8_0),  # Q8_0 down: in-register path
     dict(hidden=512, inter=256, n_experts=8, top_k=2, tokens=20, qt_gate=oracle.Q5_K, qt_up=oracle.Q5_K,
          qt_down=oracle.Q5_K, shared=True),                                          # Q5_K experts: in-register path
+    dict(hidden=768, inter=512, n_experts=10, top_k=3, tokens=24, qt_gate=oracle.Q5_1, qt_up=oracle.Q5_1,
+         qt_down=oracle.Q5_1, shared=True),                                          # Q5_1 experts: in-register path
 ])
 @pytest.mark.parametrize("fused", [True, False])
 def test_int8_ragged_shapes(over, fused):
@@ -483,6 +492,30 @@ def test_q8_gateup_decode_layers(name, T, over, fused):
     w = synth.Workload(**{**synth.WORKLOADS[name].__dict__, **over, "tokens": T})
     dl = layers.make_layer(w, seed=23, index=0, device=DEV)
     logits, x = layers.inputs_np(w, seed=23)
+    bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused)
+    _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
+    _check_routing(bufs.routing, logits, w.top_k)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name,T,over", [
+    ("sage_decode", 1, dict(n_experts=64, qt_gate=oracle.Q5_1, qt_up=oracle.Q5_1, qt_down=oracle.Q5_1)),
+    ("sage_decode", 4, dict(n_experts=64, qt_gate=oracle.Q5_1, qt_up=oracle.Q5_1)),                 # Q4_K down
+    ("flash_next_decode", 1, dict(n_experts=64, qt_gate=oracle.Q5_1, qt_up=oracle.Q5_1)),           # Q8_0 down, shared
+    ("flash_next_decode", 5, dict(n_experts=64, qt_down=oracle.Q5_1)),                              # Q4_K gate/up
+    ("tiny", 3, dict(hidden=256, inter=256, qt_gate=oracle.Q5_1, qt_up=oracle.Q5_1, qt_down=oracle.Q5_1,
+                     shared=True)),
+])
+def test_q51_decode_layers(name, T, over, fused):
+    """Q5_1 experts (a format of the "Strata v0.1.31" Unsloth bullet): the two-kernel
+    layer gives each lane one 24-byte block (fifth bits moved to bit 4 of each
+    byte four at a time); the separate calls use the general kernels."""
+    m = qm()
+    _say("q5_1 decode", name, T, over, fused)
+    from quantized_moe_ffn_amd import layers
+    w = synth.Workload(**{**synth.WORKLOADS[name].__dict__, **over, "tokens": T})
+    dl = layers.make_layer(w, seed=25, index=0, device=DEV)
+    logits, x = layers.inputs_np(w, seed=25)
     bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, fused)
     _check_layer(m, dl, w, logits, x, bufs, 0, TOL_DECODE)
     _check_routing(bufs.routing, logits, w.top_k)

@@ -108,6 +108,30 @@ def test_dequant_validation():
     assert lib.moe_dequant_q(ctypes.c_void_p(257), 12, 256, ctypes.c_void_p(256), None) == 1
     assert lib.moe_dequant_q(ctypes.c_void_p(256), 2, 256, ctypes.c_void_p(256), None) == 2
     assert lib.moe_dequant_q(ctypes.c_void_p(256), 8, 0, ctypes.c_void_p(256), None) == 0
+    # Q5_1: 32-weight blocks of 24 bytes, read as 8-byte words
+    assert lib.moe_dequant_q(ctypes.c_void_p(256), 7, 48, ctypes.c_void_p(256), None) == 1
+    assert lib.moe_dequant_q(ctypes.c_void_p(260), 7, 32, ctypes.c_void_p(256), None) == 1
+    assert "8-byte aligned" in qm.moe_last_error()
+    assert lib.moe_dequant_q(ctypes.c_void_p(264), 7, 0, ctypes.c_void_p(256), None) == 0
+
+
+def test_q51_banks_validated():
+    lib = qm.load_library()
+    r = _routing_null()
+    L = _layer()
+    L.down = _qm(qm.MOE_Q5_1, 512, 256)
+    assert L.down.row_bytes == 256 // 32 * 24
+    need = lib.moe_ffn_workspace_bytes(ctypes.byref(L), 2, 2, 1)
+    args = lambda L: (ctypes.byref(L), ctypes.byref(r), 2, 2, ctypes.c_void_p(256), None, None, 1,
+                      ctypes.c_void_p(256), None, ctypes.c_void_p(4096), need, None)
+    bad = _layer()
+    bad.down = _qm(qm.MOE_Q5_1, 512, 256)
+    bad.down.data = 4100
+    assert lib.moe_expert_ffn_q(*args(bad)) == 1 and "8-byte aligned" in qm.moe_last_error()
+    bad = _layer()
+    bad.down = _qm(qm.MOE_Q5_1, 512, 256)
+    bad.down.row_bytes = 256 // 32 * 34
+    assert lib.moe_expert_ffn_q(*args(bad)) == 1 and "down.row_bytes" in qm.moe_last_error()
 
 
 def _forward_args(L, r, T=2, k=2, x=4096, ws=None, ws_bytes=None, route_flags=0, ffn_flags=0, y_shared=None):
