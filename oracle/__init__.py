@@ -76,6 +76,8 @@ def _load():
     lib.orc_expert_ffn.argtypes = [P, P, P, i32, i32, i32, i64, i64, i64, i32, i32, i32,
                                    P, P, i32, P, P]
     lib.orc_combine.argtypes = [P, P, P, P, i32, i32, i32, P]
+    lib.orc_combine_ep.argtypes = [P, P, P, P, P, P, i32, i32, i32, P]
+    lib.orc_shared_gate.argtypes = [P, i32, i32, P, P]
     _lib = lib
     return lib
 
@@ -310,28 +312,45 @@ def expert_ffn(gate, up, down, qtypes, H: int, I: int, pair_expert, pair_token, 
     return y
 
 
-def combine(y_pair, w, y_shared=None, shared_scale=None) -> np.ndarray:
-    """Routing-weighted combine in slot order, plus the shared expert (reading R-combine)."""
+def combine(y_pair, w, y_shared=None, shared_scale=None, shared_gate=None, residual=None) -> np.ndarray:
+    """Routing-weighted combine in slot order, plus the shared expert (reading R-combine)
+    scaled by shared_scale[t] * shared_gate[t], plus the residual (reading R-epilogue)."""
     lib = _load()
     wa = np.ascontiguousarray(w, dtype=np.float64)
     T, k = wa.shape
     yp = np.ascontiguousarray(y_pair, dtype=np.float64)
     H = yp.shape[1]
     assert yp.shape[0] == T * k
-    ys = None if y_shared is None else np.ascontiguousarray(y_shared, dtype=np.float64)
-    ss = None if shared_scale is None else np.ascontiguousarray(shared_scale, dtype=np.float64)
+    f64 = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+    ys, ss, sg, rs = f64(y_shared), f64(shared_scale), f64(shared_gate), f64(residual)
+    assert rs is None or rs.shape == (T, H)
+    assert sg is None or sg.shape == (T,)
     out = np.zeros((T, H), np.float64)
-    lib.orc_combine(_ptr(yp), _ptr(wa), None if ys is None else _ptr(ys),
-                    None if ss is None else _ptr(ss), T, k, H, _ptr(out))
+    p = lambda a: None if a is None else _ptr(a)
+    lib.orc_combine_ep(_ptr(yp), _ptr(wa), p(ys), p(ss), p(sg), p(rs), T, k, H, _ptr(out))
+    return out
+
+
+def shared_gate(x, g) -> np.ndarray:
+    """Sigmoid gate of the shared expert per token, 1/(1 + exp(-(g . x_t))), fp64 (reading R-epilogue)."""
+    lib = _load()
+    xa = np.ascontiguousarray(x, dtype=np.float32)
+    ga = np.ascontiguousarray(g, dtype=np.float32).reshape(-1)
+    T, H = xa.shape
+    assert ga.size == H
+    out = np.zeros(T, np.float64)
+    lib.orc_shared_gate(_ptr(xa), T, H, _ptr(ga), _ptr(out))
     return out
 
 
 def moe_layer(logits, x, gate, up, down, qtypes, k: int, renorm: bool = True, mode: int = 0,
-              shared=None, shared_qtypes=None, shared_scale=None) -> dict:
+              shared=None, shared_qtypes=None, shared_scale=None, shared_gate_w=None, residual=None) -> dict:
     """The whole hot path for one layer: route -> bucket -> expert FFN -> combine.
 
     ``gate/up/down`` hold every expert the routing may touch, indexed by expert id.
     ``shared`` = (gate, up, down) arrays with a leading dimension of 1, or None.
+    ``shared_gate_w`` [H] gates the shared expert by a sigmoid of its dot with the
+    token; ``residual`` [T][H] is added to the output (reading R-epilogue).
     """
     logits = np.asarray(logits, dtype=np.float32)
     x = np.asarray(x, dtype=np.float32)
@@ -348,7 +367,8 @@ def moe_layer(logits, x, gate, up, down, qtypes, k: int, renorm: bool = True, mo
         sg, su, sd = shared
         y_sh = expert_ffn(sg, su, sd, shared_qtypes or qtypes, H, I,
                           np.zeros(T, np.int32), np.arange(T, dtype=np.int32), x, mode)
-    out = combine(y_pair, w, y_sh, shared_scale)
-    res = {"idx": idx, "w": w, "y_pair": y_pair, "y_shared": y_sh, "out": out}
+    sgv = None if shared_gate_w is None else shared_gate(x, shared_gate_w)
+    out = combine(y_pair, w, y_sh, shared_scale, sgv, residual)
+    res = {"idx": idx, "w": w, "y_pair": y_pair, "y_shared": y_sh, "out": out, "shared_gate": sgv}
     res.update(b)
     return res

@@ -42,7 +42,12 @@
  *  R-ffn     expert FFN = W_down * (silu(W_gate x) .* (W_up x)),
  *            silu(g) = g / (1 + exp(-g)).
  *  R-combine out_t = sum_j w_tj * y_tj (slot order) + s_t * y_shared_t; no
- *            residual, norm or bias.
+ *            norm or bias.
+ *  R-epilogue the layer's optional epilogue: the shared expert scaled by a
+ *            sigmoid gate 1/(1 + exp(-(g . x_t))) of the token's hidden state
+ *            (one vector g per layer; the pages keep shared experts and the
+ *            "gated-residual" weights on the GPU, "Strata - the details", "How
+ *            it works"), and the residual stream added to the layer output.
  *  R-router  router logits are a plain projection of the token's hidden
  *            state by an fp32 [E][H] router matrix: logit_e = sum_h W[e][h]
  *            x[h], no bias ("Strata - the details", "How it works": routers
@@ -537,18 +542,41 @@ void orc_expert_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
 /* y_pair [T*k][H] (pair p = t*k + j), w [T][k], y_shared [T][H] or NULL,    */
 /* shared_scale [T] or NULL (= 1).  out [T][H].                              */
 /* ------------------------------------------------------------------------- */
-void orc_combine(const double* y_pair, const double* w, const double* y_shared,
-                 const double* shared_scale, int32_t T, int32_t k, int32_t H, double* out) {
+/* Combine with the layer epilogue (R-epilogue): the shared expert's weight is
+ * s_t = shared_scale[t] * gate[t] (each factor 1 when its array is NULL; gate
+ * holds the sigmoid values of orc_shared_gate), and the residual stream, when
+ * given, is added last:
+ *   out_t = sum_j w_tj * y_tj + s_t * y_shared_t + residual_t. */
+void orc_combine_ep(const double* y_pair, const double* w, const double* y_shared,
+                    const double* shared_scale, const double* gate, const double* residual,
+                    int32_t T, int32_t k, int32_t H, double* out) {
     for (int32_t t = 0; t < T; ++t) {
         for (int32_t o = 0; o < H; ++o) {
             double acc = 0.0;
             for (int32_t j = 0; j < k; ++j)
                 acc += w[(int64_t)t * k + j] * y_pair[((int64_t)t * k + j) * H + o];
             if (y_shared) {
-                double s = shared_scale ? shared_scale[t] : 1.0;
+                double s = (shared_scale ? shared_scale[t] : 1.0) * (gate ? gate[t] : 1.0);
                 acc += s * y_shared[(int64_t)t * H + o];
             }
+            if (residual) acc += residual[(int64_t)t * H + o];
             out[(int64_t)t * H + o] = acc;
         }
+    }
+}
+
+void orc_combine(const double* y_pair, const double* w, const double* y_shared,
+                 const double* shared_scale, int32_t T, int32_t k, int32_t H, double* out) {
+    orc_combine_ep(y_pair, w, y_shared, shared_scale, NULL, NULL, T, k, H, out);
+}
+
+/* Sigmoid gate of the shared expert (R-epilogue): one weight vector g [H]
+ * per layer, gate_t = 1 / (1 + exp(-(g . x_t))) with the dot a sequential fp64
+ * sum over h.  x fp32 [T][H], g fp32 [H] -> out fp64 [T]. */
+void orc_shared_gate(const float* x, int32_t T, int32_t H, const float* g, double* out) {
+    for (int32_t t = 0; t < T; ++t) {
+        double z = 0.0;
+        for (int32_t h = 0; h < H; ++h) z += (double)g[h] * (double)x[(int64_t)t * H + h];
+        out[t] = 1.0 / (1.0 + exp(-z));
     }
 }
