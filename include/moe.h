@@ -204,6 +204,29 @@ moe_status moe_combine(const float* y_pair, const float* w, const float* y_share
                        const float* shared_scale, int32_t T, int32_t k, int32_t H, float* out,
                        hipStream_t stream);
 
+/* Routing-weighted combine with the layer epilogue:
+ *   out[t] = sum_{j<k} w[t][j] * y_pair[t*k+j] + s_t * y_shared[t] + residual[t]
+ * in that order (slot order, then the shared expert, then the residual), with
+ * s_t = shared_scale[t] * shared_gate_s[t] (a NULL factor is 1; both need
+ * y_shared).  shared_gate_s [T] holds the gate values moe_shared_gate writes.
+ * residual [T][H] or NULL; out may be the residual array itself (an in-place
+ * update of the residual stream) but must not alias y_pair or y_shared.  With
+ * shared_gate_s and residual NULL this is moe_combine, bit for bit. */
+moe_status moe_combine_ep(const float* y_pair, const float* w, const float* y_shared,
+                          const float* shared_scale, const float* shared_gate_s, const float* residual,
+                          int32_t T, int32_t k, int32_t H, float* out, hipStream_t stream);
+
+/* Sigmoid gate of a shared expert ("Strata - the details", "How it works":
+ * shared experts and the gated-residual weights stay on the GPU; the gate's
+ * form is a reading: one fp32 weight vector per layer):
+ *   s[t] = 1 / (1 + exp(-(gate_w . x[t])))
+ * x fp32 [T][H] and gate_w fp32 [H], both 16-byte aligned; s fp32 [T].  The dot
+ * is summed in a fixed order by one wave per token; moe_forward_ep computes the
+ * same bits inside the decode layer.  Checks: T >= 1, H a positive multiple of
+ * 4, non-null pointers, alignment. */
+moe_status moe_shared_gate(const float* x, int32_t T, int32_t H, const float* gate_w, float* s,
+                           hipStream_t stream);
+
 /* Bytes of device workspace moe_forward needs (for the path ffn_flags selects). */
 size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t ffn_flags);
 
@@ -225,6 +248,26 @@ moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, 
                        uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
                        float* y_shared, const float* shared_scale, float* out, void* workspace,
                        size_t ws_bytes, hipStream_t stream);
+
+/* The layer epilogue of moe_forward_ep.  NULL members drop their term. */
+typedef struct moe_epilogue {
+    const float* residual;    /* fp32 [T][H]: added to out last; may be out itself */
+    const float* shared_gate; /* fp32 [H], 16-byte aligned: the shared expert is scaled by
+                                 sigmoid(shared_gate . x_t) (times shared_scale[t] when given);
+                                 needs a layer with a shared expert */
+} moe_epilogue;
+
+/* moe_forward followed by the epilogue (ep NULL: moe_forward exactly): the
+ * combine becomes moe_combine_ep's, with the gate values computed from x as
+ * moe_shared_gate does.  On the two-kernel decode layer both are fused: the
+ * routing workgroup of the gate/up kernel computes the gate, the down kernel
+ * adds the residual while it forms the combine; elsewhere a gate kernel and
+ * the combine kernel do it.  Same bits on both.  Extra checks: shared_gate
+ * needs has_shared; residual must not alias y_pair or y_shared. */
+moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
+                          uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
+                          float* y_shared, const float* shared_scale, const moe_epilogue* ep, float* out,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Test hook: dequantize n_weights weights of contiguous blocks to fp32 with the
  * same device unpacking helpers the FFN kernels use.  Each value is the exact

@@ -7,7 +7,8 @@ kernels.  There is no CPU fallback: if ``libmoe.so`` is missing or cannot be
 loaded, the first call raises.
 
 Entry points keep the C names: ``moe_route_topk``, ``moe_quantize_act``,
-``moe_router_logits``, ``moe_expert_ffn_q``, ``moe_combine``, ``moe_forward``, ``moe_dequant_q``,
+``moe_router_logits``, ``moe_expert_ffn_q``, ``moe_combine``, ``moe_combine_ep``, ``moe_shared_gate``,
+``moe_forward``, ``moe_forward_ep``, ``moe_dequant_q``,
 ``moe_check_device_errors``, ``moe_last_error``, ``moe_abi_version``,
 ``moe_route_workspace_bytes``, ``moe_ffn_workspace_bytes``,
 ``moe_forward_workspace_bytes``.
@@ -38,7 +39,7 @@ EXPORTS = (
     "moe_abi_version", "moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
     "moe_quantize_act", "moe_ffn_workspace_bytes", "moe_expert_ffn_q", "moe_combine",
     "moe_dequant_q", "moe_check_device_errors", "moe_forward_workspace_bytes", "moe_forward",
-    "moe_router_logits",
+    "moe_router_logits", "moe_combine_ep", "moe_shared_gate", "moe_forward_ep",
 )
 
 
@@ -59,6 +60,10 @@ class moe_layer(ctypes.Structure):
                 ("has_shared", ctypes.c_int32), ("gate", moe_qmatrix), ("up", moe_qmatrix),
                 ("down", moe_qmatrix), ("sh_gate", moe_qmatrix), ("sh_up", moe_qmatrix),
                 ("sh_down", moe_qmatrix)]
+
+
+class moe_epilogue(ctypes.Structure):
+    _fields_ = [("residual", ctypes.c_void_p), ("shared_gate", ctypes.c_void_p)]
 
 
 class moe_routing(ctypes.Structure):
@@ -103,6 +108,13 @@ def load_library(path: str = LIB_PATH):
     lib.moe_forward.argtypes = [ctypes.POINTER(moe_layer), P, P, i32, i32, u32, u32, ctypes.POINTER(moe_routing),
                                 P, P, P, P, P, sz, P]
     lib.moe_forward.restype = st
+    lib.moe_forward_ep.argtypes = [ctypes.POINTER(moe_layer), P, P, i32, i32, u32, u32,
+                                   ctypes.POINTER(moe_routing), P, P, P, ctypes.POINTER(moe_epilogue), P, P, sz, P]
+    lib.moe_forward_ep.restype = st
+    lib.moe_combine_ep.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P]
+    lib.moe_combine_ep.restype = st
+    lib.moe_shared_gate.argtypes = [P, i32, i32, P, P, P]
+    lib.moe_shared_gate.restype = st
     lib.moe_check_device_errors.argtypes = [P]
     lib.moe_check_device_errors.restype = st
     _lib = lib
@@ -240,6 +252,22 @@ def moe_combine(y_pair, w, out, y_shared=None, shared_scale=None, stream=None):
                                       _ptr(out), _stream(stream)), "moe_combine")
 
 
+def moe_combine_ep(y_pair, w, out, y_shared=None, shared_scale=None, shared_gate_s=None, residual=None,
+                   stream=None):
+    T, k = w.shape
+    H = out.shape[1]
+    _check(load_library().moe_combine_ep(_ptr(y_pair), _ptr(w), _ptr(y_shared), _ptr(shared_scale),
+                                         _ptr(shared_gate_s), _ptr(residual), T, k, H, _ptr(out),
+                                         _stream(stream)), "moe_combine_ep")
+
+
+def moe_shared_gate(x, gate_w, s, stream=None):
+    """s[t] = sigmoid(gate_w . x[t]) (fp32 device tensors)."""
+    T, H = x.shape
+    _check(load_library().moe_shared_gate(_ptr(x), T, H, _ptr(gate_w), _ptr(s), _stream(stream)),
+           "moe_shared_gate")
+
+
 def moe_dequant_q(blocks, qtype: int, n_weights: int, out, stream=None):
     _check(load_library().moe_dequant_q(_ptr(blocks), qtype, n_weights, _ptr(out), _stream(stream)),
            "moe_dequant_q")
@@ -258,6 +286,19 @@ def moe_forward(layer: Layer, logits, x, k: int, routing: Routing, y_pair, out, 
                                     _ptr(y_pair), _ptr(y_shared), _ptr(shared_scale), _ptr(out), _ptr(workspace),
                                     nbytes, _stream(stream))
     _check(st, "moe_forward")
+
+
+def moe_forward_ep(layer: Layer, logits, x, k: int, routing: Routing, y_pair, out, y_shared=None,
+                   shared_scale=None, residual=None, shared_gate=None, renorm: bool = True,
+                   flags: int = MOE_FFN_AUTO, workspace=None, stream=None):
+    T = x.shape[0]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ep = moe_epilogue(_ptr(residual), _ptr(shared_gate))
+    st = load_library().moe_forward_ep(ctypes.byref(layer.struct()), _ptr(logits), _ptr(x), T, k,
+                                       MOE_ROUTE_RENORM if renorm else 0, flags, ctypes.byref(routing.struct()),
+                                       _ptr(y_pair), _ptr(y_shared), _ptr(shared_scale), ctypes.byref(ep), _ptr(out),
+                                       _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "moe_forward_ep")
 
 
 def moe_check_device_errors(stream=None):
@@ -283,21 +324,29 @@ class LayerBuffers:
         self.xq = torch.empty((T, H), dtype=torch.int8, device=device)
         self.xd = torch.empty((T, H // 256), dtype=torch.float32, device=device)
         self.out = torch.empty((T, H), dtype=torch.float32, device=device)
+        self.gate_s = torch.empty(T, dtype=torch.float32, device=device)
         fwd = moe_forward_workspace_bytes(layer, T, k, flags)
         self.fwd_ws = torch.empty(max(fwd, 256), dtype=torch.uint8, device=device)
 
 
 def forward(layer: Layer, logits, x, k: int, bufs: LayerBuffers | None = None, flags: int = MOE_FFN_AUTO,
-            renorm: bool = True, shared_scale=None, stream=None, fused: bool = True) -> LayerBuffers:
+            renorm: bool = True, shared_scale=None, stream=None, fused: bool = True, residual=None,
+            shared_gate=None) -> LayerBuffers:
     """The whole layer on one stream.  fused=True: one moe_forward call (two kernels
-    for decode batches); fused=False: the separate calls route -> (quantize) ->
-    expert FFN -> combine."""
+    for decode batches), moe_forward_ep when an epilogue (residual, shared-expert
+    gate vector) is given; fused=False: the separate calls route -> (quantize) ->
+    expert FFN -> (shared gate) -> combine."""
     T = x.shape[0]
     if bufs is None:
         bufs = LayerBuffers(layer, T, k, flags, device=x.device)
+    epilogue = residual is not None or shared_gate is not None
     if fused:
-        moe_forward(layer, logits, x, k, bufs.routing, bufs.y_pair, bufs.out, bufs.y_shared, shared_scale, renorm,
-                    flags, bufs.fwd_ws, stream)
+        if epilogue:
+            moe_forward_ep(layer, logits, x, k, bufs.routing, bufs.y_pair, bufs.out, bufs.y_shared, shared_scale,
+                           residual, shared_gate, renorm, flags, bufs.fwd_ws, stream)
+        else:
+            moe_forward(layer, logits, x, k, bufs.routing, bufs.y_pair, bufs.out, bufs.y_shared, shared_scale,
+                        renorm, flags, bufs.fwd_ws, stream)
         return bufs
     path = flags if flags != MOE_FFN_AUTO else (MOE_FFN_DECODE if T <= AUTO_DECODE_MAX_T else MOE_FFN_INT8)
     moe_route_topk(logits, k, bufs.routing, renorm, bufs.route_ws, stream)
@@ -306,5 +355,12 @@ def forward(layer: Layer, logits, x, k: int, bufs: LayerBuffers | None = None, f
     moe_expert_ffn_q(layer, bufs.routing, T, k, bufs.y_pair, x=x if path == MOE_FFN_DECODE else None,
                      xq=bufs.xq if path == MOE_FFN_INT8 else None, xd=bufs.xd if path == MOE_FFN_INT8 else None,
                      flags=path, y_shared=bufs.y_shared, workspace=bufs.ffn_ws, stream=stream)
-    moe_combine(bufs.y_pair, bufs.routing.w, bufs.out, bufs.y_shared, shared_scale, stream)
+    if epilogue:
+        sg = None
+        if shared_gate is not None:
+            sg = bufs.gate_s
+            moe_shared_gate(x, shared_gate, sg, stream)
+        moe_combine_ep(bufs.y_pair, bufs.routing.w, bufs.out, bufs.y_shared, shared_scale, sg, residual, stream)
+    else:
+        moe_combine(bufs.y_pair, bufs.routing.w, bufs.out, bufs.y_shared, shared_scale, stream)
     return bufs

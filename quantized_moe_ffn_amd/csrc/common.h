@@ -131,4 +131,24 @@ __device__ __forceinline__ float ubyte_f32(uint32_t v) {
 // g the reciprocal of +inf is 0 and the result is -0.
 __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// Sigmoid gate of the shared expert for one token, by one wave:
+// 1 / (1 + e^-z), z = g . x.  Lane l takes the float4 columns 4l, 4l + 256, ...
+// in order and the wave adds the lanes with the fixed DPP tree, so every
+// caller (the decode layer's routing workgroup, the separate gate kernel) gets
+// the same bits.  g and x 16-byte aligned, H a multiple of 4.
+__device__ __forceinline__ float shared_gate_wave(const float* __restrict__ g, const float* __restrict__ x, int H) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float acc = 0.f;
+    for (int c = 4 * lane; c < H; c += 4 * kWave) {
+        const float4 gv = *reinterpret_cast<const float4*>(g + c);
+        const float4 xv = *reinterpret_cast<const float4*>(x + c);
+        acc = fmaf(gv.x, xv.x, acc);
+        acc = fmaf(gv.y, xv.y, acc);
+        acc = fmaf(gv.z, xv.z, acc);
+        acc = fmaf(gv.w, xv.w, acc);
+    }
+    const float z = wave_sum(acc);
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 }  // namespace moe

@@ -60,6 +60,7 @@ struct Gcd<A, 0> {
 struct DecRoute {
     int sel[kDecMaxPairs];
     float w[kDecMaxPairs];
+    float sg[kDecMaxT];   // sigmoid gate of the shared expert per token (when the layer has one)
 };
 
 static_assert(sizeof(DecRoute) <= kDecRouteTabBytes, "routing table size");
@@ -590,6 +591,14 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
         if (blockIdx.x != 0) return;
         dec_route<V>(a.logits, a.T, a.E, a.k, a.renorm, R);
         dec_publish(R, a.T, a.E, a.k, a.r);
+        if (a.sgate_w) {   // one wave per token, as the separate gate kernel
+            const int wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
+            for (int t = wave; t < a.T; t += nwaves) {
+                const float v = shared_gate_wave(a.sgate_w, a.x + (int64_t)t * a.H, a.H);
+                if ((threadIdx.x & (kWave - 1)) == 0) R.sg[t] = v;
+            }
+            __syncthreads();
+        }
         const int* src = reinterpret_cast<const int*>(&R);
         for (int i = threadIdx.x; i < (int)(sizeof(DecRoute) / 4); i += blockDim.x) a.route_tab[i] = src[i];
         return;
@@ -819,9 +828,11 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
         }
         if (a.has_shared) {
             const float ys = s_y[(P + t) * RO + r];
-            acc = fmaf(a.shared_scale ? a.shared_scale[t] : 1.0f, ys, acc);
+            const float sc = (a.shared_scale ? a.shared_scale[t] : 1.0f) * (a.sgate_w ? R.sg[t] : 1.0f);
+            acc = fmaf(sc, ys, acc);
             if (a.y_shared) a.y_shared[(int64_t)t * a.H + o] = ys;
         }
+        if (a.residual) acc += a.residual[(int64_t)t * a.H + o];   // may be out itself: read, then written
         a.out[(int64_t)t * a.H + o] = acc;
     }
 }

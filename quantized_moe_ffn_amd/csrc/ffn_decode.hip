@@ -348,20 +348,24 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Combine and the dequantization test hook.
 // ---------------------------------------------------------------------------
+// out may be the residual array itself (each element is read, then written, by
+// one thread), so neither carries __restrict__.
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y_pair,
                                                       const float* __restrict__ w,
                                                       const float* __restrict__ y_shared,
-                                                      const float* __restrict__ shared_scale, int T,
-                                                      int k, int H, float* __restrict__ out) {
+                                                      const float* __restrict__ shared_scale,
+                                                      const float* __restrict__ sgate, const float* residual,
+                                                      int T, int k, int H, float* out) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)T * H) return;
     const int t = (int)(idx / H), o = (int)(idx - (int64_t)t * H);
     float acc = 0.f;
     for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], y_pair[((int64_t)t * k + j) * H + o], acc);
     if (y_shared) {
-        const float sc = shared_scale ? shared_scale[t] : 1.0f;
+        const float sc = (shared_scale ? shared_scale[t] : 1.0f) * (sgate ? sgate[t] : 1.0f);
         acc = fmaf(sc, y_shared[(int64_t)t * H + o], acc);
     }
+    if (residual) acc += residual[idx];
     out[idx] = acc;
 }
 
@@ -370,8 +374,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 __global__ void __launch_bounds__(256) combine4_kernel(const float4* __restrict__ y_pair,
                                                        const float* __restrict__ w,
                                                        const float4* __restrict__ y_shared,
-                                                       const float* __restrict__ shared_scale, int T, int k,
-                                                       int H4, float4* __restrict__ out) {
+                                                       const float* __restrict__ shared_scale,
+                                                       const float* __restrict__ sgate, const float4* residual,
+                                                       int T, int k, int H4, float4* out) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)T * H4) return;
     const int t = (int)(idx / H4), o = (int)(idx - (int64_t)t * H4);
@@ -385,28 +390,52 @@ __global__ void __launch_bounds__(256) combine4_kernel(const float4* __restrict_
         acc.w = fmaf(wj, y.w, acc.w);
     }
     if (y_shared) {
-        const float sc = shared_scale ? shared_scale[t] : 1.0f;
+        const float sc = (shared_scale ? shared_scale[t] : 1.0f) * (sgate ? sgate[t] : 1.0f);
         const float4 ys = y_shared[(int64_t)t * H4 + o];
         acc.x = fmaf(sc, ys.x, acc.x);
         acc.y = fmaf(sc, ys.y, acc.y);
         acc.z = fmaf(sc, ys.z, acc.z);
         acc.w = fmaf(sc, ys.w, acc.w);
     }
+    if (residual) {
+        const float4 r = residual[idx];
+        acc.x += r.x;
+        acc.y += r.y;
+        acc.z += r.z;
+        acc.w += r.w;
+    }
     out[idx] = acc;
 }
 
-hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared,
-                          const float* shared_scale, int T, int k, int H, float* out, hipStream_t s) {
+hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
+                          const float* sgate, const float* residual, int T, int k, int H, float* out,
+                          hipStream_t s) {
     const auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
-    if (H % 4 == 0 && a16(y_pair) && a16(out) && (!y_shared || a16(y_shared))) {
+    if (H % 4 == 0 && a16(y_pair) && a16(out) && (!y_shared || a16(y_shared)) && (!residual || a16(residual))) {
         const int64_t n = (int64_t)T * (H / 4);
         combine4_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
             reinterpret_cast<const float4*>(y_pair), w, reinterpret_cast<const float4*>(y_shared), shared_scale,
-            T, k, H / 4, reinterpret_cast<float4*>(out));
+            sgate, reinterpret_cast<const float4*>(residual), T, k, H / 4, reinterpret_cast<float4*>(out));
         return hipGetLastError();
     }
     const int64_t n = (int64_t)T * H;
-    combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(y_pair, w, y_shared, shared_scale, T, k, H, out);
+    combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(y_pair, w, y_shared, shared_scale, sgate, residual,
+                                                               T, k, H, out);
+    return hipGetLastError();
+}
+
+// One wave per token: s[t] = sigmoid(g . x_t) (shared_gate_wave).
+__global__ void __launch_bounds__(256) shared_gate_kernel(const float* __restrict__ x, int T, int H,
+                                                          const float* __restrict__ g, float* __restrict__ s) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int t = blockIdx.x * (blockDim.x / kWave) + wave;
+    if (t >= T) return;
+    const float v = shared_gate_wave(g, x + (int64_t)t * H, H);
+    if (lane == 0) s[t] = v;
+}
+
+hipError_t launch_shared_gate(const float* x, int T, int H, const float* g, float* s, hipStream_t st) {
+    shared_gate_kernel<<<(unsigned)((T + 3) / 4), 4 * kWave, 0, st>>>(x, T, H, g, s);
     return hipGetLastError();
 }
 

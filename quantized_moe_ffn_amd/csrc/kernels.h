@@ -93,6 +93,8 @@ struct DecArgs {
     float* y_pair;        // [T*k][H] or null
     float* y_shared;      // [T][H] or null
     const float* shared_scale;
+    const float* sgate_w; // [H] or null: sigmoid gate of the shared expert
+    const float* residual;// [T][H] or null: added to out last
     float* out;           // [T][H]
     int* route_tab;       // workspace: the routing table K1 hands to K2 (kDecRouteTabBytes)
 };
@@ -116,8 +118,13 @@ constexpr int kRouterMaxH = 8192;     // router: largest hidden size
 hipError_t launch_router(const float* x, int T, int H, const float* w, int E, float* logits, hipStream_t s);
 
 hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s);
-hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared,
-                          const float* shared_scale, int T, int k, int H, float* out, hipStream_t s);
+// out = sum_j w_j y_pair_j (slot order) + (shared_scale * sgate) * y_shared + residual;
+// null arrays drop their term (a null scale or gate is 1).
+hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
+                          const float* sgate, const float* residual, int T, int k, int H, float* out,
+                          hipStream_t s);
+// s[t] = 1 / (1 + exp(-(g . x_t))), one wave per token
+hipError_t launch_shared_gate(const float* x, int T, int H, const float* g, float* s, hipStream_t st);
 hipError_t launch_dequant(const void* blocks, int qtype, int64_t n_weights, float* out, hipStream_t s);
 
 }  // namespace moe

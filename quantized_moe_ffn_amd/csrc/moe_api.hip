@@ -124,7 +124,7 @@ void set_ffn_ws(moe::FfnArgs& a, char* base, const FfnWorkspace& w) {
 }
 
 struct ForwardWorkspace {
-    size_t route, ffn, xq, xd, tab, total;
+    size_t route, ffn, xq, xd, tab, sg, total;
 };
 
 ForwardWorkspace forward_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
@@ -140,6 +140,8 @@ ForwardWorkspace forward_ws_layout(const moe_layer* L, int T, int k, uint32_t pa
     off += align_up((size_t)T * (L->hidden / 256) * sizeof(float), 256);
     w.tab = off;
     off += moe::kDecRouteTabBytes;
+    w.sg = off;   // shared-expert gate values of the separate stages
+    off += align_up((size_t)T * sizeof(float), 256);
     w.total = off;
     return w;
 }
@@ -324,8 +326,24 @@ moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, 
                        uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
                        float* y_shared, const float* shared_scale, float* out, void* workspace, size_t ws_bytes,
                        hipStream_t stream) {
+    return moe_forward_ep(L, logits, x, T, k, route_flags, ffn_flags, r, y_pair, y_shared, shared_scale, nullptr,
+                          out, workspace, ws_bytes, stream);
+}
+
+moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
+                          uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
+                          float* y_shared, const float* shared_scale, const moe_epilogue* ep, float* out,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
     moe_status st = validate_layer(L, T, k, y_shared);
     if (st != MOE_OK) return st;
+    const float* sgate_w = ep ? ep->shared_gate : nullptr;
+    const float* residual = ep ? ep->residual : nullptr;
+    if (sgate_w && !L->has_shared)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue shared_gate given for a layer without a shared expert");
+    if ((sgate_w && !aligned(sgate_w, 16)) || (residual && !aligned(residual, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: shared_gate must be 16-byte aligned, residual 4-byte aligned");
+    if (residual && (residual == y_pair || residual == y_shared))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: residual must not alias y_pair or y_shared");
     if (!logits || !x || !out || !y_pair) return fail(MOE_ERR_INVALID_ARGUMENT, "logits, x, y_pair or out is NULL");
     if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(out, 4) || !aligned(y_pair, 4) ||
         (y_shared && !aligned(y_shared, 4)) || (shared_scale && !aligned(shared_scale, 4)))
@@ -370,6 +388,8 @@ moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, 
         d.y_pair = y_pair;
         d.y_shared = y_shared;
         d.shared_scale = shared_scale;
+        d.sgate_w = sgate_w;
+        d.residual = residual;
         d.out = out;
         d.route_tab = (int*)(ws + wl.tab);
         return from_hip(moe::launch_dec_fused(d, stream), "moe_forward (decode) launch");
@@ -398,9 +418,25 @@ moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, 
         e = moe::launch_ffn_decode(a, stream);
     }
     if (e != hipSuccess) return from_hip(e, "moe_forward: expert FFN launch");
-    return from_hip(moe::launch_combine(y_pair, r->w, L->has_shared ? y_shared : nullptr, shared_scale, T, k,
-                                        L->hidden, out, stream),
+    float* sg = nullptr;
+    if (sgate_w) {
+        sg = (float*)(ws + wl.sg);
+        e = moe::launch_shared_gate(x, T, L->hidden, sgate_w, sg, stream);
+        if (e != hipSuccess) return from_hip(e, "moe_forward: shared-expert gate launch");
+    }
+    return from_hip(moe::launch_combine(y_pair, r->w, L->has_shared ? y_shared : nullptr, shared_scale, sg, residual,
+                                        T, k, L->hidden, out, stream),
                     "moe_forward: combine launch");
+}
+
+moe_status moe_shared_gate(const float* x, int32_t T, int32_t H, const float* gate_w, float* s,
+                           hipStream_t stream) {
+    if (!x || !gate_w || !s) return fail(MOE_ERR_INVALID_ARGUMENT, "x, gate_w or s is NULL");
+    if (T < 1 || H < 4 || H % 4)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d, H = %d: need T >= 1 and H a positive multiple of 4", T, H);
+    if (!aligned(x, 16) || !aligned(gate_w, 16) || !aligned(s, 4))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "x and gate_w must be 16-byte aligned, s 4-byte aligned");
+    return from_hip(moe::launch_shared_gate(x, T, H, gate_w, s, stream), "moe_shared_gate launch");
 }
 
 moe_status moe_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
@@ -411,8 +447,24 @@ moe_status moe_combine(const float* y_pair, const float* w, const float* y_share
                     kMaxTopK);
     if (shared_scale && !y_shared)
         return fail(MOE_ERR_INVALID_ARGUMENT, "shared_scale given without y_shared");
-    return from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, T, k, H, out, stream),
+    return from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, nullptr, nullptr, T, k, H, out, stream),
                     "moe_combine launch");
+}
+
+moe_status moe_combine_ep(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
+                          const float* shared_gate_s, const float* residual, int32_t T, int32_t k, int32_t H,
+                          float* out, hipStream_t stream) {
+    if (!y_pair || !w || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "y_pair, w or out is NULL");
+    if (T < 1 || k < 1 || k > kMaxTopK || H < 1)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d, k = %d, H = %d: need T >= 1, 1 <= k <= %d, H >= 1", T, k, H,
+                    kMaxTopK);
+    if ((shared_scale || shared_gate_s) && !y_shared)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "shared_scale or shared_gate_s given without y_shared");
+    if (residual && (residual == y_pair || residual == y_shared))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "residual must not alias y_pair or y_shared");
+    return from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, shared_gate_s, residual, T, k, H, out,
+                                        stream),
+                    "moe_combine_ep launch");
 }
 
 moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, float* out, hipStream_t stream) {

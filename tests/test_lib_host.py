@@ -216,3 +216,50 @@ def test_router_rejects_null_and_misaligned():
     assert st == 1 and "NULL" in qm.moe_last_error()
     st = lib.moe_router_logits(ctypes.c_void_p(264), 1, 256, ctypes.c_void_p(4096), 8, ctypes.c_void_p(8192), None)
     assert st == 1 and "16-byte aligned" in qm.moe_last_error()
+
+
+def _forward_ep_args(L, r, ep, **kw):
+    a = list(_forward_args(L, r, **kw))
+    # moe_forward_ep takes the epilogue between shared_scale and out
+    return tuple(a[:11] + [ctypes.byref(ep)] + a[11:])
+
+
+def test_forward_ep_validation():
+    lib = qm.load_library()
+    r = _routing_null()
+    L = _layer()
+    ep = qm.moe_epilogue(None, 4096)            # a gate vector, but the layer has no shared expert
+    st = lib.moe_forward_ep(*_forward_ep_args(L, r, ep, ws_bytes=1 << 30))
+    assert st == 1 and "without a shared expert" in qm.moe_last_error()
+    L.has_shared = 1
+    L.sh_gate, L.sh_up, L.sh_down = _qm(12, 256, 512, 1), _qm(12, 256, 512, 1), _qm(12, 512, 256, 1)
+    ep = qm.moe_epilogue(None, 4100)            # misaligned gate vector
+    st = lib.moe_forward_ep(*_forward_ep_args(L, r, ep, ws_bytes=1 << 30, y_shared=ctypes.c_void_p(12288)))
+    assert st == 1 and "16-byte aligned" in qm.moe_last_error()
+    ep = qm.moe_epilogue(8192, None)            # residual aliasing y_pair
+    st = lib.moe_forward_ep(*_forward_ep_args(L, r, ep, ws_bytes=1 << 30, y_shared=ctypes.c_void_p(12288)))
+    assert st == 1 and "alias" in qm.moe_last_error()
+
+
+def test_forward_workspace_holds_the_gate_values():
+    lib = qm.load_library()
+    L = _layer()
+    for T in (1, 9, 300):
+        a = lib.moe_forward_workspace_bytes(ctypes.byref(L), T, 2, 2)
+        assert a >= T * 4 + 4096
+
+
+def test_shared_gate_and_combine_ep_validation():
+    lib = qm.load_library()
+    P = ctypes.c_void_p
+    assert lib.moe_shared_gate(P(256), 2, 258, P(4096), P(512), None) == 1
+    assert "multiple of 4" in qm.moe_last_error()
+    assert lib.moe_shared_gate(P(256), 0, 256, P(4096), P(512), None) == 1
+    assert lib.moe_shared_gate(P(260), 2, 256, P(4096), P(512), None) == 1
+    assert "16-byte aligned" in qm.moe_last_error()
+    assert lib.moe_shared_gate(None, 2, 256, P(4096), P(512), None) == 1
+    # combine_ep: a gate without a shared output, a residual aliasing y_pair
+    assert lib.moe_combine_ep(P(256), P(512), None, None, P(1024), None, 2, 2, 64, P(2048), None) == 1
+    assert "without y_shared" in qm.moe_last_error()
+    assert lib.moe_combine_ep(P(256), P(512), None, None, None, P(256), 2, 2, 64, P(2048), None) == 1
+    assert "alias" in qm.moe_last_error()
