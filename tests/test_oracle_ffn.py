@@ -69,20 +69,23 @@ def test_unit_vector_picks_columns():
         assert np.allclose(y[0], Wd @ h, rtol=1e-12, atol=1e-12 * np.abs(Wd @ h).max())
 
 
-@pytest.mark.parametrize("qd", [Q4K, Q80])
-def test_brute_force_tiny(qd):
-    """Oracle vs a dense numpy evaluation of the same definition on a tiny layer."""
+@pytest.mark.parametrize("qg,qd", [(Q4K, Q4K), (Q4K, Q80), (oracle.Q5_K, oracle.Q5_1), (oracle.Q5_1, oracle.Q5_K),
+                                   (Q80, oracle.Q5_1)])
+def test_brute_force_tiny(qg, qd):
+    """Oracle vs a dense numpy evaluation of the same definition on a tiny layer, in each
+    expert format (the rows are decoded through the pinned dequantizers, the products and
+    the SiLU are numpy's)."""
     H, I, T = 256, 256, 3
-    g = synth.rng(22, qd)
-    gate = synth.bank_np(g, Q4K, 2, I, H)
-    up = synth.bank_np(g, Q4K, 2, I, H)
+    g = synth.rng(22, qg, qd)
+    gate = synth.bank_np(g, qg, 2, I, H)
+    up = synth.bank_np(g, qg, 2, I, H)
     down = synth.bank_np(g, qd, 2, H, I)
     x = synth.activations_np(g, T, H)
     pe, pt = [1, 0, 1], [0, 1, 2]
-    y = oracle.expert_ffn(gate, up, down, (Q4K, Q4K, qd), H, I, pe, pt, x)
+    y = oracle.expert_ffn(gate, up, down, (qg, qg, qd), H, I, pe, pt, x)
     for p in range(3):
         e, t = pe[p], pt[p]
-        Wg, Wu, Wd = _dense(gate[e], Q4K, H), _dense(up[e], Q4K, H), _dense(down[e], qd, I)
+        Wg, Wu, Wd = _dense(gate[e], qg, H), _dense(up[e], qg, H), _dense(down[e], qd, I)
         xv = x[t].astype(np.float64)
         gg = Wg @ xv
         ref = Wd @ (gg * expit(gg) * (Wu @ xv))
