@@ -68,6 +68,9 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the tokens per layer call (a decode batch or verify window of the "
                          "same layer shape)")
+    ap.add_argument("--experts", type=int, default=None,
+                    help="override the routed experts per layer (e.g. one GPU's share under expert parallelism)")
+    ap.add_argument("--top-k", type=int, default=None, help="override the routed experts per token")
     ap.add_argument("--path", choices=["auto", "decode", "int8"], default=None,
                     help="FFN path (default: the workload's own; auto takes the decode path up to 8 tokens)")
     args = ap.parse_args()
@@ -96,6 +99,13 @@ def main() -> int:
             return 2
         if args.tokens != w.tokens:
             w = dataclasses.replace(w, name="%s_t%d" % (w.name, args.tokens), tokens=args.tokens)
+    if args.experts is not None or args.top_k is not None:
+        E2 = args.experts if args.experts is not None else w.n_experts
+        k2 = args.top_k if args.top_k is not None else w.top_k
+        if not (1 <= k2 <= min(E2, 16)):
+            print("need 1 <= top-k <= min(experts, 16)", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, name="%s_e%d_k%d" % (w.name, E2, k2), n_experts=E2, top_k=k2)
     L = args.layers or w.layers
     R = max(1, args.replays)
     T, H, E, k, I = w.tokens, w.hidden, w.n_experts, w.top_k, w.inter
