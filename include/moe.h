@@ -71,8 +71,8 @@ typedef enum moe_status {
  * Q4_K and Q5_K banks must be 16-byte aligned, Q5_1 banks 8-byte aligned,
  * Q8_0 banks 2-byte aligned.  The two-kernel decode layer takes gate/up in
  * any of the four formats (one format for both) with down in any of them;
- * the int8 MFMA GEMMs take Q4_K throughout; other mixes run on the general
- * kernels of the chosen path. */
+ * the int8 MFMA GEMMs take Q4_K or Q5_K gate/up with Q4_K or Q5_K down; other
+ * mixes run on the general kernels of the chosen path. */
 enum { MOE_Q5_1 = 7, MOE_Q8_0 = 8, MOE_Q4_K = 12, MOE_Q5_K = 13 };
 
 /* moe_route_topk flags */
@@ -83,7 +83,7 @@ enum {
     MOE_FFN_AUTO = 0u,   /* decode path up to 8 tokens, int8 path above               */
     MOE_FFN_DECODE = 1u, /* fp32 activations, weights dequantized in registers        */
     MOE_FFN_INT8 = 2u    /* int8 activations (moe_quantize_act); grouped int8 MFMA GEMMs
-                            when gate, up and down (and the shared expert) are all Q4_K */
+                            when gate, up and down are Q4_K or Q5_K */
 };
 
 /* One projection of an expert bank: n_experts matrices of rows x cols weights,
@@ -180,11 +180,13 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_
  * Weights are dequantized inside the dot products.  Decode path: x fp32 [T][H].
  * Int8 path: xq/xd from moe_quantize_act (xq 16-byte aligned); h is
  * re-quantized per (pair, 256-wide block of I) with moe_quantize_act's rule for
- * the int8 down projection.  With every matrix Q4_K (and (T*k + T)*max(H, I) <
- * 2^31) both projections run as grouped int8 MFMA GEMMs over the tokens of each
- * expert; there the Q4_K min term is carried in fp16, so every block's dmin must
- * be below 1039 in magnitude (dmin*63 < 65504).  Other format mixes use the
- * decode path's kernels on the dequantized int8 activations.  y_pair fp32
+ * the int8 down projection.  With gate/up Q4_K or Q5_K and down Q4_K or Q5_K
+ * (and (T*k + T)*max(H, I) < 2^31) both projections run as grouped int8 MFMA
+ * GEMMs over the tokens of each expert; there the min term is carried in fp16,
+ * so every block's dmin*m (Q4_K), or 16*d*sc - dmin*m (Q5_K, whose quants
+ * enter as q - 16), must stay below 65504 in magnitude (dmin below 1039; for
+ * Q5_K also d below 64).  Other format mixes use the decode path's kernels on
+ * the dequantized int8 activations.  y_pair fp32
  * [T*k][H]; y_shared fp32 [T][H] (required iff has_shared).  r must hold the
  * result of moe_route_topk for the same T, k and E (read on the device: no host
  * synchronisation).

@@ -7,17 +7,17 @@
 // re-quantized per (pair, 256-wide block of I) with the same rule before the
 // down projection.
 //
-// Q4_K gate/up/down run as grouped int8 MFMA GEMMs (ffn_mfma.hip).  Other
-// format mixes evaluate both projections with the decode path's in-register
-// dequantization on x = xd*xq and h = hd*hq.
+// Q4_K or Q5_K gate/up with Q4_K or Q5_K down run as grouped int8 MFMA GEMMs
+// (ffn_mfma.hip).  Other format mixes evaluate both projections with the
+// decode path's in-register dequantization on x = xd*xq and h = hd*hq.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s) {
-    if (a.tiles && mfma_path_supported(a.H, a.I, a.gate.qtype, a.up.qtype, a.down.qtype) &&
-        (!a.has_shared || (a.sgate.qtype == kQ4_K && a.sup.qtype == kQ4_K && a.sdown.qtype == kQ4_K))) {
+    // (the shared expert's formats equal the routed ones: checked by the API layer)
+    if (a.tiles && mfma_path_supported(a.H, a.I, a.gate.qtype, a.up.qtype, a.down.qtype)) {
         MfmaArgs m{};
         m.gate = a.gate;
         m.up = a.up;

@@ -1,5 +1,5 @@
 // ffn_mfma.hip — grouped int8 MFMA GEMMs of the prompt-chunk expert FFN over
-// Q4_K experts (tokens grouped per expert; "Strata - the details", faster
+// Q4_K and Q5_K experts (tokens grouped per expert; "Strata - the details", faster
 // prompts: quantized expert kernels instead of FP16 expansion; one activation
 // quantization per token, the "Strata-Sage-A1.5-GGUF" card's round-2 table).
 //
@@ -110,21 +110,46 @@ __device__ __forceinline__ uint32_t byte_pair(uint32_t v, int j) {
 }
 
 // One 256-block of a weight row, as a lane needs it: the 16-byte header and
-// its four 16-byte quant slices (lane half h: bytes 32c + 16h .. + 15).
+// its four 16-byte quant slices (lane half h: bytes 32c + 16h .. + 15 of the
+// quants); for Q5_K also the 16 fifth-bit bytes of those weights (qh bytes
+// 16h .. 16h + 15: byte l holds the fifth bit of the low-nibble weight of
+// chunk c in bit 2c and of the high-nibble weight in bit 2c + 1).
+template <int QT>
+struct MQuant;
+template <>
+struct MQuant<kQ4_K> {
+    static constexpr int kBytes = 144, kQs = 16;
+};
+template <>
+struct MQuant<kQ5_K> {
+    static constexpr int kBytes = 176, kQs = 48;
+};
+
 struct BlockRegs {
     uint4 hdr;
     uint4 q[4];
+    uint4 qh;
 };
 
+template <int QT>
 __device__ __forceinline__ void load_block(const uint8_t* blk, int h, BlockRegs& r) {
     r.hdr = *reinterpret_cast<const uint4*>(blk);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint4*>(blk + 16 + 32 * c + 16 * h);
+    for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint4*>(blk + MQuant<QT>::kQs + 32 * c + 16 * h);
+    if constexpr (QT == kQ5_K) r.qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * h);
 }
 
 // out[mt] += (this 256-block's contribution) for the lane's weight row and the
 // tile's 32*MTILES rows, block index b of the row.
-template <int MTILES>
+//
+// Q5_K: the quants reach 31, and 7*31 does not fit an int8 byte, so the
+// weights enter as sc*(q - 16) (limbs in -112..105).  A limb byte s*q (<= 217,
+// from the same packed multiply) becomes s*(q - 16) by adding 128 - 16s to
+// every byte, which cannot carry since the sum is s*(q - 16) + 128 in 16..233,
+// and flipping bit 7 of every byte (the two's complement of the sum minus
+// 128).  The 16*sc*X_j it takes away comes back through the min-term MFMA,
+// whose weight side becomes 16*d*sc_j - dmin*m_j.
+template <int MTILES, int QT>
 __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const TileLds& T, v16f (&out)[MTILES]) {
     constexpr int MT = 32 * MTILES;
     const int lane = threadIdx.x & (kWave - 1);
@@ -141,6 +166,8 @@ __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const Tile
     const uint32_t sh4[2] = {(sc_lo >> 3) & 0x07070707u, (sc_hi >> 3) & 0x07070707u};
 
     v16i accl[MTILES], acch[MTILES];
+    constexpr bool kFifth = QT == kQ5_K;
+    const uint32_t hb4[4] = {br.qh.x, br.qh.y, br.qh.z, br.qh.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const uint32_t w4[4] = {br.q[c].x, br.q[c].y, br.q[c].z, br.q[c].w};
@@ -148,12 +175,21 @@ __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const Tile
         for (int hi = 0; hi < 2; ++hi) {
             const int j = 2 * c + hi;
             const uint32_t sl = byte_pair(sl4[j >> 2], j & 3), sh = byte_pair(sh4[j >> 2], j & 3);
+            // Q5_K: 128 - 16*s in every byte (s in both 16-bit halves of sl / sh)
+            const uint32_t bias_l = kFifth ? 0x80808080u - ((sl | (sl << 8)) << 4) : 0u;
+            const uint32_t bias_h = kFifth ? 0x80808080u - ((sh | (sh << 8)) << 4) : 0u;
             v4i Bl, Bh;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t q = (hi ? (w4[i] >> 4) : w4[i]) & 0x0F0F0F0Fu;
-                Bl[i] = (int)pk_mul_u16(q, sl);
-                Bh[i] = (int)pk_mul_u16(q, sh);
+                uint32_t q = (hi ? (w4[i] >> 4) : w4[i]) & 0x0F0F0F0Fu;
+                if constexpr (kFifth) {
+                    q |= ((hb4[i] >> j) & 0x01010101u) << 4;
+                    Bl[i] = (int)((pk_mul_u16(q, sl) + bias_l) ^ 0x80808080u);
+                    Bh[i] = (int)((pk_mul_u16(q, sh) + bias_h) ^ 0x80808080u);
+                } else {
+                    Bl[i] = (int)pk_mul_u16(q, sl);
+                    Bh[i] = (int)pk_mul_u16(q, sh);
+                }
             }
 #pragma unroll
             for (int mt = 0; mt < MTILES; ++mt) {
@@ -171,14 +207,20 @@ __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const Tile
     }
 
     // min term: out += sum_j (-dmin m_j) (X_j xd / s), hi/lo fp16 pairs; lane
-    // half 0 carries the hi parts of X_j xd / s, half 1 the lo parts
+    // half 0 carries the hi parts of X_j xd / s, half 1 the lo parts (Q5_K:
+    // 16 d sc_j - dmin m_j, each product exact, their sum rounded once)
     {
         const float dmin = q4k_dmin(hd);
+        const float d16 = 16.0f * q4k_d(hd);
         v8h Bmh, Bml;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t mb = j < 4 ? mn_lo : mn_hi;
-            const float bv = -(dmin * (float)((mb >> (8 * (j & 3))) & 0xFFu));  // exact: 11 x 6 bits
+            float bv = -(dmin * (float)((mb >> (8 * (j & 3))) & 0xFFu));  // exact: 11 x 6 bits
+            if constexpr (kFifth) {
+                const uint32_t sb = j < 4 ? sc_lo : sc_hi;
+                bv = fmaf(d16, (float)((sb >> (8 * (j & 3))) & 0xFFu), bv);
+            }
             const _Float16 bh = (_Float16)bv;
             Bmh[j] = bh;
             Bml[j] = (_Float16)(bv - (float)bh);
@@ -348,7 +390,7 @@ __device__ __forceinline__ TileLds carve(unsigned char* lds, int K, const float*
     return TileLds{a, xd, xs, s_sc, lda, xs_ld, K / 32};
 }
 
-template <int MTILES>
+template <int MTILES, int QG>
 __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -387,11 +429,11 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     // blocks s = 0 .. 2*nsb-1 (gate row, then up row), loaded two ahead of use
     auto blk_ptr = [&](int sx) {
         const int r = sx >= nsb ? 1 : 0;
-        return rows[r] + (int64_t)(sx - r * nsb) * 144;
+        return rows[r] + (int64_t)(sx - r * nsb) * MQuant<QG>::kBytes;
     };
     const int steps = 2 * nsb;
     auto step = [&](const BlockRegs& br, int sx) {
-        block_mma<MTILES>(br, sx >= nsb ? sx - nsb : sx, T, acc);
+        block_mma<MTILES, QG>(br, sx >= nsb ? sx - nsb : sx, T, acc);
         if (sx == nsb - 1) {
             apply_row_scale<MTILES>(T, acc);
 #pragma unroll
@@ -406,11 +448,11 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     // registers that loads in flight still write); steps is even, so the body
     // has no conditional steps and the compiler can interleave them
     BlockRegs b0, b1;
-    load_block(blk_ptr(0), h, b0);
+    load_block<QG>(blk_ptr(0), h, b0);
     for (int s = 0; s < steps; s += 2) {
-        load_block(blk_ptr(s + 1), h, b1);
+        load_block<QG>(blk_ptr(s + 1), h, b1);
         step(b0, s);
-        load_block(blk_ptr(min(s + 2, steps - 1)), h, b0);
+        load_block<QG>(blk_ptr(min(s + 2, steps - 1)), h, b0);
         step(b1, s + 1);
     }
 
@@ -484,7 +526,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
 
 constexpr int kDownRoundsMax = 4;  // 256-row rounds per down workgroup (large batches)
 
-template <int MTILES>
+template <int MTILES, int QD>
 __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -525,12 +567,12 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
         for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
     auto blk_ptr = [&](int sx) {
         const int r = sx / nsb;
-        return base + r * round_stride + (int64_t)(sx - r * nsb) * 144;
+        return base + r * round_stride + (int64_t)(sx - r * nsb) * MQuant<QD>::kBytes;
     };
     const int steps = nr * nsb;
     auto step = [&](const BlockRegs& br, int sx) {
         const int r = sx / nsb, b = sx - r * nsb;
-        block_mma<MTILES>(br, b, T, acc);
+        block_mma<MTILES, QD>(br, b, T, acc);
         if (b == nsb - 1) {
             apply_row_scale<MTILES>(T, acc);
             const int o = (r0 + r) * 256 + wave * 32 + n;
@@ -551,12 +593,12 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
         }
     };
     BlockRegs b0, b1;
-    load_block(blk_ptr(0), h, b0);
+    load_block<QD>(blk_ptr(0), h, b0);
     int s = 0;
     for (; s + 1 < steps; s += 2) {
-        load_block(blk_ptr(s + 1), h, b1);
+        load_block<QD>(blk_ptr(s + 1), h, b1);
         step(b0, s);
-        load_block(blk_ptr(min(s + 2, steps - 1)), h, b0);
+        load_block<QD>(blk_ptr(min(s + 2, steps - 1)), h, b0);
         step(b1, s + 1);
     }
     if (s < steps) step(b0, s);
@@ -622,7 +664,7 @@ int max_tiles(int T, int k, int E, int has_shared, int mt) {
 
 unsigned grid_for(int works) { return (unsigned)((works + kXcds - 1) / kXcds * kXcds); }
 
-template <int MTILES>
+template <int MTILES, int QG, int QD>
 hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     constexpr int MT = 32 * MTILES;
     const int maxt = max_tiles(a.T, a.k, a.E, a.has_shared, MT);
@@ -634,7 +676,7 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, n_sums, a.H, a.xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds_gu = std::max(tile_lds_bytes<MTILES>(a.H), (size_t)MT * kHStride * sizeof(float));
-    gateup_mfma_kernel<MTILES><<<grid_for(maxt * (a.I / 256)), kMThreads, lds_gu, s>>>(a);
+    gateup_mfma_kernel<MTILES, QG><<<grid_for(maxt * (a.I / 256)), kMThreads, lds_gu, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // rounds of 256 output rows per down workgroup: four amortise the tile's LDS
     // load over 1,024 rows when there are work items to spare; small batches (a
@@ -643,14 +685,27 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     MfmaArgs d = a;
     d.down_rounds = (int64_t)maxt * ((a.H / 256 + kDownRoundsMax - 1) / kDownRoundsMax) >= 1024 ? kDownRoundsMax : 1;
     const int nb_down = (a.H / 256 + d.down_rounds - 1) / d.down_rounds;
-    down_mfma_kernel<MTILES><<<grid_for(maxt * nb_down), kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(d);
+    down_mfma_kernel<MTILES, QD><<<grid_for(maxt * nb_down), kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(d);
     return hipGetLastError();
+}
+
+template <int MTILES, int QG>
+hipError_t launch_mfma_qd(const MfmaArgs& a, hipStream_t s) {
+    return a.down.qtype == kQ5_K ? launch_mfma_path<MTILES, QG, kQ5_K>(a, s) : launch_mfma_path<MTILES, QG, kQ4_K>(a, s);
+}
+
+template <int MTILES>
+hipError_t launch_mfma_q(const MfmaArgs& a, hipStream_t s) {
+    return a.gate.qtype == kQ5_K ? launch_mfma_qd<MTILES, kQ5_K>(a, s) : launch_mfma_qd<MTILES, kQ4_K>(a, s);
 }
 
 }  // namespace
 
+// Gate and up in one of Q4_K and Q5_K (the same for both), down in either.
 bool mfma_path_supported(int H, int I, int qg, int qu, int qd) {
-    return qg == kQ4_K && qu == kQ4_K && qd == kQ4_K && H <= kMfmaMaxDim && I <= kMfmaMaxDim;
+    const bool kq_g = (qg == kQ4_K || qg == kQ5_K) && qu == qg;
+    const bool kq_d = qd == kQ4_K || qd == kQ5_K;
+    return kq_g && kq_d && H <= kMfmaMaxDim && I <= kMfmaMaxDim;
 }
 
 // The kernels index h and y rows with 32-bit element offsets.
@@ -672,8 +727,8 @@ size_t mfma_tiles_bytes(int T, int k, int E, int has_shared, int H, int I) {
 }
 
 hipError_t launch_ffn_mfma(const MfmaArgs& a, hipStream_t s) {
-    if (mfma_tile_rows(a.T, a.k, a.E, a.H, a.I) == 64) return launch_mfma_path<2>(a, s);
-    return launch_mfma_path<1>(a, s);
+    if (mfma_tile_rows(a.T, a.k, a.E, a.H, a.I) == 64) return launch_mfma_q<2>(a, s);
+    return launch_mfma_q<1>(a, s);
 }
 
 }  // namespace moe

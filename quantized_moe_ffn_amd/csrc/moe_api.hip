@@ -80,11 +80,11 @@ struct FfnWorkspace {
     bool mfma;
 };
 
-// The int8 path runs as grouped int8 MFMA GEMMs when every expert matrix is Q4_K.
+// The int8 path runs as grouped int8 MFMA GEMMs for k-quant experts (Q4_K or
+// Q5_K gate/up, Q4_K or Q5_K down); the shared expert's formats equal the
+// routed ones (validate_layer).
 bool int8_uses_mfma(const moe_layer* L) {
-    const bool sh_ok = !L->has_shared || (L->sh_gate.qtype == MOE_Q4_K && L->sh_up.qtype == MOE_Q4_K &&
-                                          L->sh_down.qtype == MOE_Q4_K);
-    return sh_ok && moe::mfma_path_supported(L->hidden, L->inter, L->gate.qtype, L->up.qtype, L->down.qtype);
+    return moe::mfma_path_supported(L->hidden, L->inter, L->gate.qtype, L->up.qtype, L->down.qtype);
 }
 
 FfnWorkspace ffn_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {

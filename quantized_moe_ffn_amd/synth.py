@@ -186,6 +186,9 @@ WORKLOADS = {
     # "Strata v0.1.31" release notes run natively; the Sage-like layer stands in
     "sage_decode_q5k": Workload("sage_decode_q5k", 2048, 256, 8, 512, 1, qt_gate=Q5_K, qt_up=Q5_K, qt_down=Q5_K,
                                 layers=40, notes="the sage_decode layer with Q5_K gate/up/down"),
+    "prefill_chunk_q5k": Workload("prefill_chunk_q5k", 2048, 256, 8, 512, 4096, qt_gate=Q5_K, qt_up=Q5_K,
+                                  qt_down=Q5_K, zipf_s=1.1, layers=4, int8_path=True,
+                                  notes="the prompt chunk with Q5_K gate/up/down"),
     # Q5_1 experts, another format of those files (32-weight blocks, scale and offset)
     "sage_decode_q51": Workload("sage_decode_q51", 2048, 256, 8, 512, 1, qt_gate=Q5_1, qt_up=Q5_1, qt_down=Q5_1,
                                 layers=40, notes="the sage_decode layer with Q5_1 gate/up/down"),

@@ -252,10 +252,11 @@ def test_int8_path_tiny_full(fused):
     _check_layer(m, dl, w, logits, x, bufs, 1, TOL_INT8)
 
 
-def test_int8_prefill_chunk_sampled():
+@pytest.mark.parametrize("name", ["prefill_chunk", "prefill_chunk_q5k"])
+def test_int8_prefill_chunk_sampled(name):
     m = qm()
-    _say("int8 prefill chunk T=4096 (sampled tokens)")
-    dl, w = _layer("prefill_chunk")
+    _say("int8 prompt chunk T=4096 (sampled tokens)", name)
+    dl, w = _layer(name)
     from quantized_moe_ffn_amd import layers
     logits, x = layers.inputs_np(w, seed=0)
     bufs = _run_layer(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8)
@@ -270,7 +271,12 @@ def test_int8_prefill_chunk_sampled():
     dict(hidden=2560, inter=512, n_experts=16, top_k=2, tokens=40),                # 32-token tiles (hidden > 2048)
     dict(hidden=512, inter=256, n_experts=8, top_k=2, tokens=20, qt_down=oracle.Q8_0),  # Q8_0 down: in-register path
     dict(hidden=512, inter=256, n_experts=8, top_k=2, tokens=20, qt_gate=oracle.Q5_K, qt_up=oracle.Q5_K,
-         qt_down=oracle.Q5_K, shared=True),                                          # Q5_K experts: in-register path
+         qt_down=oracle.Q5_K, shared=True),                                          # Q5_K experts: MFMA GEMMs
+    dict(hidden=768, inter=512, n_experts=24, top_k=4, tokens=70, qt_gate=oracle.Q5_K, qt_up=oracle.Q5_K,
+         shared=True),                                                               # Q5_K gate/up, Q4_K down
+    dict(hidden=512, inter=768, n_experts=6, top_k=2, tokens=130, qt_down=oracle.Q5_K),  # Q4_K gate/up, Q5_K down
+    dict(hidden=2560, inter=512, n_experts=16, top_k=2, tokens=40, qt_gate=oracle.Q5_K, qt_up=oracle.Q5_K,
+         qt_down=oracle.Q5_K),                                                       # Q5_K, 32-token tiles
     dict(hidden=768, inter=512, n_experts=10, top_k=3, tokens=24, qt_gate=oracle.Q5_1, qt_up=oracle.Q5_1,
          qt_down=oracle.Q5_1, shared=True),                                          # Q5_1 experts: in-register path
 ])
