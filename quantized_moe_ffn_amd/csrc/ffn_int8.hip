@@ -42,6 +42,7 @@ hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s) {
         m.hs = a.hs;
         m.y_pair = a.y_pair;
         m.y_shared = a.y_shared;
+        m.xs_ready = a.xs_ready;
         const size_t half = (mfma_tiles_bytes(a.T, a.k, a.E, a.has_shared, a.H, a.I) - 256) / 2;
         m.tile_e = a.tiles;
         m.tile_m0 = a.tiles + half / sizeof(int32_t);

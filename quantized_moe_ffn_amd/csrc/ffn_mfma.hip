@@ -672,9 +672,11 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
                                          a.tile_m0, a.n_tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n_sums = (int64_t)a.T * (a.H / 32);
-    act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, n_sums, a.H, a.xs);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!a.xs_ready) {
+        const int64_t n_sums = (int64_t)a.T * (a.H / 32);
+        act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, n_sums, a.H, a.xs);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const size_t lds_gu = std::max(tile_lds_bytes<MTILES>(a.H), (size_t)MT * kHStride * sizeof(float));
     gateup_mfma_kernel<MTILES, QG><<<grid_for(maxt * (a.I / 256)), kMThreads, lds_gu, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

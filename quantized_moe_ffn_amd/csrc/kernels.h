@@ -50,6 +50,7 @@ struct FfnArgs {
     int16_t* xs;                   // workspace [T][H/32]: per-32 sums of xq (int8 MFMA path)
     int16_t* hs;                   // workspace [T*k + T][I/32]: per-32 sums of hq (int8 MFMA path)
     int32_t* tiles;                // workspace: MFMA tile list (mfma_tiles_bytes)
+    int xs_ready;                  // xs already holds the per-32 sums of xq
 };
 
 // The grouped int8 MFMA GEMMs of the int8 path (Q4_K gate/up/down).
@@ -73,6 +74,7 @@ struct MfmaArgs {
     int32_t* tile_m0;
     int32_t* n_tiles;
     int down_rounds;               // 256-row rounds per down workgroup (set by the launcher)
+    int xs_ready;                  // xs already holds the per-32 sums of xq (written with the codes)
 };
 
 bool mfma_path_supported(int H, int I, int qg, int qu, int qd);
@@ -117,7 +119,9 @@ constexpr int kRouterGemvMaxT = 16;   // router: tokens up to which the matrix-v
 constexpr int kRouterMaxH = 8192;     // router: largest hidden size
 hipError_t launch_router(const float* x, int T, int H, const float* w, int E, float* logits, hipStream_t s);
 
-hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s);
+// xs non-null: also the int16 sums of every 32 codes (xs [T][H/32])
+hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s,
+                               int16_t* xs = nullptr);
 // out = sum_j w_j y_pair_j (slot order) + (shared_scale * sgate) * y_shared + residual;
 // null arrays drop their term (a null scale or gate is 1).
 hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,

@@ -411,7 +411,9 @@ moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* 
     a.y_pair = y_pair;
     a.y_shared = y_shared;
     if (path == MOE_FFN_INT8) {
-        e = moe::launch_quantize_act(x, T, L->hidden, (int8_t*)a.xq, (float*)a.xd, stream);
+        // the MFMA GEMMs' per-32 code sums come out of the same pass (a.xs is null otherwise)
+        e = moe::launch_quantize_act(x, T, L->hidden, (int8_t*)a.xq, (float*)a.xd, stream, a.xs);
+        a.xs_ready = a.xs ? 1 : 0;
         if (e != hipSuccess) return from_hip(e, "moe_forward: quantisation launch");
         e = moe::launch_ffn_int8(a, stream);
     } else {

@@ -12,38 +12,59 @@
 
 namespace moe {
 
-// One wave per (row, 256-block): lane l holds elements 4l..4l+3.
+constexpr int kQBlocksPerWave = 2;   // blocks of one wave, loaded together
+
+// One wave per kQBlocksPerWave consecutive (row, 256-block)s: lane l holds
+// elements 4l..4l+3 of each.  With xs non-null it also writes the exact sums
+// of every 32 codes (int16, |sum| <= 4064), which the int8 MFMA GEMMs use.
 __global__ void __launch_bounds__(256) quantize_act_kernel(const float* __restrict__ x, int64_t n_blocks,
-                                                           int8_t* __restrict__ xq, float* __restrict__ xd) {
-    const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+                                                           int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                           int16_t* __restrict__ xs) {
+    const int64_t blk0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kQBlocksPerWave;
     const int lane = threadIdx.x & (kWave - 1);
-    if (blk >= n_blocks) return;
-    const float4 v = reinterpret_cast<const float4*>(x + blk * 256)[lane];
-    const bool fin = isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w);
-    const bool all_fin = !__any(!fin);
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = wave_max(amax);
-    char4 q = make_char4(0, 0, 0, 0);
-    float d = 0.0f;
-    if (!all_fin) {
-        if (lane == 0) raise_error(kErrActNonFinite);
-    } else if (amax > 0.0f) {
-        const float id = __fdiv_rn(127.0f, amax);
-        auto qz = [&](float a) -> signed char {
-            float r = rintf(__fmul_rn(a, id));
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            return (signed char)(int)r;
-        };
-        q = make_char4(qz(v.x), qz(v.y), qz(v.z), qz(v.w));
-        d = __fdiv_rn(amax, 127.0f);
+    if (blk0 >= n_blocks) return;
+    float4 v[kQBlocksPerWave];
+#pragma unroll
+    for (int b = 0; b < kQBlocksPerWave; ++b) {   // a block past the end reloads the last one, never stored
+        const int64_t blk = blk0 + b < n_blocks ? blk0 + b : n_blocks - 1;
+        v[b] = reinterpret_cast<const float4*>(x + blk * 256)[lane];
     }
-    reinterpret_cast<char4*>(xq + blk * 256)[lane] = q;
-    if (lane == 0) xd[blk] = d;
+#pragma unroll
+    for (int b = 0; b < kQBlocksPerWave; ++b) {
+        const int64_t blk = blk0 + b;
+        if (blk >= n_blocks) break;
+        const bool fin = isfinite(v[b].x) && isfinite(v[b].y) && isfinite(v[b].z) && isfinite(v[b].w);
+        const bool all_fin = !__any(!fin);
+        float amax = fmaxf(fmaxf(fabsf(v[b].x), fabsf(v[b].y)), fmaxf(fabsf(v[b].z), fabsf(v[b].w)));
+        amax = wave_max(amax);
+        char4 q = make_char4(0, 0, 0, 0);
+        float d = 0.0f;
+        if (!all_fin) {
+            if (lane == 0) raise_error(kErrActNonFinite);
+        } else if (amax > 0.0f) {
+            const float id = __fdiv_rn(127.0f, amax);
+            auto qz = [&](float a) -> signed char {
+                float r = rintf(__fmul_rn(a, id));
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                return (signed char)(int)r;
+            };
+            q = make_char4(qz(v[b].x), qz(v[b].y), qz(v[b].z), qz(v[b].w));
+            d = __fdiv_rn(amax, 127.0f);
+        }
+        reinterpret_cast<char4*>(xq + blk * 256)[lane] = q;
+        if (lane == 0) xd[blk] = d;
+        if (xs) {   // lanes 8c .. 8c + 7 hold codes 32c .. 32c + 31 (sums exact in fp32)
+            const float s32 = segment_sum<8>((float)((int)q.x + (int)q.y + (int)q.z + (int)q.w));
+            if ((lane & 7) == 7) xs[blk * 8 + (lane >> 3)] = (int16_t)(int)s32;
+        }
+    }
 }
 
-hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s) {
+hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s,
+                               int16_t* xs) {
     const int64_t n_blocks = (int64_t)T * (H / 256);
-    quantize_act_kernel<<<(unsigned)((n_blocks + 3) / 4), 256, 0, s>>>(x, n_blocks, xq, xd);
+    const int64_t waves = (n_blocks + kQBlocksPerWave - 1) / kQBlocksPerWave;
+    quantize_act_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(x, n_blocks, xq, xd, xs);
     return hipGetLastError();
 }
 

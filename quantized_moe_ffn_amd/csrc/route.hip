@@ -306,36 +306,68 @@ __global__ void __launch_bounds__(kTilePairs) bucket_tile_kernel(const int32_t* 
 }
 
 // One workgroup: per-expert totals, offsets, tile bases and the active list.
+// G = blockDim/E threads share an expert (thread t: expert t % E, chunk t / E
+// of the tiles): each sums its chunk, the chunk sums meet in LDS, and each
+// then writes its chunk's exclusive prefixes from the sum of the chunks
+// before it; a chunk's values stay in registers between the two passes when
+// it holds at most kB tiles (one round trip each way instead of one per 16
+// tiles).
 __global__ void __launch_bounds__(1024) bucket_scan_kernel(int n_tiles, int E, int P,
                                                            int32_t* tile_hist, RoutingPtrs r) {
     __shared__ int s_wave[kWave + 1];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < E) {
-        // per-expert exclusive prefix over tiles, 16 loads in flight at a time
-        constexpr int kB = 16;
-        for (int t0 = 0; t0 < n_tiles; t0 += kB) {
-            int hv[kB];
+    __shared__ int s_part[1024];
+    constexpr int kB = 32;
+    const int t = threadIdx.x;
+    const int G = max(1, (int)blockDim.x / E);
+    const int q = t / E, e = t - q * E;
+    const bool act = q < G;
+    const int chunk = (n_tiles + G - 1) / G;
+    const int lo = q * chunk, hi = min(n_tiles, lo + chunk);
+    int hv[kB];
+    int sum = 0;
+    if (act) {
+        for (int t0 = lo; t0 < hi; t0 += kB) {
 #pragma unroll
-            for (int i = 0; i < kB; ++i) hv[i] = tile_hist[(int64_t)min(t0 + i, n_tiles - 1) * E + e];
+            for (int i = 0; i < kB; ++i) hv[i] = t0 + i < hi ? tile_hist[(int64_t)(t0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kB; ++i) sum += hv[i];
+        }
+    }
+    s_part[t] = act ? sum : 0;
+    __syncthreads();
+    int base = 0, run = 0;
+    if (act) {
+        for (int qq = 0; qq < G; ++qq) {
+            const int v = s_part[qq * E + e];
+            base += qq < q ? v : 0;
+            run += v;
+        }
+        int c = base;
+        for (int t0 = lo; t0 < hi; t0 += kB) {
+            if (hi - lo > kB) {   // more than one batch: the registers hold the last one only
+#pragma unroll
+                for (int i = 0; i < kB; ++i) hv[i] = t0 + i < hi ? tile_hist[(int64_t)(t0 + i) * E + e] : 0;
+            }
 #pragma unroll
             for (int i = 0; i < kB; ++i) {
-                if (t0 + i < n_tiles) {
-                    tile_hist[(int64_t)(t0 + i) * E + e] = run;
-                    run += hv[i];
+                if (t0 + i < hi) {
+                    tile_hist[(int64_t)(t0 + i) * E + e] = c;
+                    c += hv[i];
                 }
             }
         }
     }
+    // threads t < E (chunk 0) hold their expert's total in run
     int total, n_act;
-    const int off = block_exclusive_scan(e < E ? run : 0, s_wave, total);
-    const int apos = block_exclusive_scan((e < E && run > 0) ? 1 : 0, s_wave, n_act);
-    if (e < E) {
-        r.count[e] = run;
-        r.offset[e] = off;
-        if (run > 0) r.active[apos] = e;
+    const int mine = t < E ? run : 0;
+    const int off = block_exclusive_scan(mine, s_wave, total);
+    const int apos = block_exclusive_scan((t < E && run > 0) ? 1 : 0, s_wave, n_act);
+    if (t < E) {
+        r.count[t] = run;
+        r.offset[t] = off;
+        if (run > 0) r.active[apos] = t;
     }
-    if (e == 0) {
+    if (t == 0) {
         r.offset[E] = total;
         *r.n_active = n_act;
     }
