@@ -12,7 +12,7 @@
 
 namespace moe {
 
-constexpr int kQBlocksPerWave = 2;   // blocks of one wave, loaded together
+constexpr int kQBlocksPerWave = 4;   // blocks of one wave, loaded together
 
 // One wave per kQBlocksPerWave consecutive (row, 256-block)s: lane l holds
 // elements 4l..4l+3 of each.  With xs non-null it also writes the exact sums
@@ -36,7 +36,8 @@ __global__ void __launch_bounds__(256) quantize_act_kernel(const float* __restri
         const bool fin = isfinite(v[b].x) && isfinite(v[b].y) && isfinite(v[b].z) && isfinite(v[b].w);
         const bool all_fin = !__any(!fin);
         float amax = fmaxf(fmaxf(fabsf(v[b].x), fabsf(v[b].y)), fmaxf(fabsf(v[b].z), fabsf(v[b].w)));
-        amax = wave_max(amax);
+        // |x| >= 0 orders as its bit pattern: the DPP maximum of unsigned values
+        amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));
         char4 q = make_char4(0, 0, 0, 0);
         float d = 0.0f;
         if (!all_fin) {
