@@ -264,7 +264,9 @@ typedef struct moe_epilogue {
  * moe_shared_gate does.  On the two-kernel decode layer both are fused: the
  * routing workgroup of the gate/up kernel computes the gate, the down kernel
  * adds the residual while it forms the combine; elsewhere a gate kernel and
- * the combine kernel do it.  Same bits on both.  Extra checks: shared_gate
+ * the combine kernel do it.  The gate values are the same bits on both, and
+ * the epilogue equals moe_forward with those values as shared_scale followed
+ * by one fp32 add of the residual, bit for bit.  Extra checks: shared_gate
  * needs has_shared; residual must not alias y_pair or y_shared. */
 moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
                           uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
