@@ -201,12 +201,20 @@ def main() -> int:
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record(stream)
+    step_ev = []
     for s in range(args.steps):
         step(args.warmup + s)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        step_ev.append(e)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = ev0.elapsed_time(ev1)
+    # per-step spread of the layer call (each step is L calls)
+    step_us = np.array([(ev0 if s == 0 else step_ev[s - 1]).elapsed_time(step_ev[s]) * 1e3 / L
+                        for s in range(args.steps)])
+    pct = {q: round(float(np.percentile(step_us, q)), 3) for q in (10, 50, 90)}
     qm.moe_check_device_errors()
     ms_per_step = ms_total / args.steps
     tokens = T * L * args.steps
@@ -262,6 +270,8 @@ def main() -> int:
                    "parallelism": "single GPU", "graphs": args.graph,
                    "router": "fp32 [E][H], moe_router_logits in the timed step" if routers is not None else None},
         "hbm_GBps_end_to_end": round(dom_bytes / (ms_total / 1e3) / 1e9, 1),
+        "layer_call_us_p10_p50_p90": [pct[10], pct[50], pct[90]],
+        "hbm_copy_GBps_measured": copy_bandwidth(torch, dev),
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity_max_normwise_err": parity,
@@ -269,6 +279,27 @@ def main() -> int:
     }
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def copy_bandwidth(torch, dev) -> float:
+    """Measured device-to-device copy rate of 1 GiB (bytes read + written per second, GB/s):
+    the practical streaming ceiling the decode roofline is read against."""
+    n = 1 << 28
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = 2.0 * 4 * n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return round(rate, 1)
 
 
 def fmt(qt):
