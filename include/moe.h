@@ -201,7 +201,7 @@ moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T,
  *   out[t] = sum_{j<k} w[t][j] * y_pair[t*k+j]  (+ s_t * y_shared[t])
  * summed in slot order, then the shared expert; s_t = shared_scale[t], or 1
  * when shared_scale is NULL; y_shared may be NULL (no shared expert).
- * All fp32; out [T][H].  No residual, norm or bias. */
+ * All fp32 and 4-byte aligned; out [T][H].  No residual, norm or bias. */
 moe_status moe_combine(const float* y_pair, const float* w, const float* y_shared,
                        const float* shared_scale, int32_t T, int32_t k, int32_t H, float* out,
                        hipStream_t stream);
@@ -213,7 +213,8 @@ moe_status moe_combine(const float* y_pair, const float* w, const float* y_share
  * y_shared).  shared_gate_s [T] holds the gate values moe_shared_gate writes.
  * residual [T][H] or NULL; out may be the residual array itself (an in-place
  * update of the residual stream) but must not alias y_pair or y_shared.  With
- * shared_gate_s and residual NULL this is moe_combine, bit for bit. */
+ * shared_gate_s and residual NULL this is moe_combine, bit for bit.  All
+ * arrays fp32 and 4-byte aligned. */
 moe_status moe_combine_ep(const float* y_pair, const float* w, const float* y_shared,
                           const float* shared_scale, const float* shared_gate_s, const float* residual,
                           int32_t T, int32_t k, int32_t H, float* out, hipStream_t stream);
@@ -244,7 +245,8 @@ size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uin
  * contract as the three calls (bitwise
  * deterministic; combine in slot order).  y_pair [T*k][H] is always written;
  * y_shared [T][H] is required iff the layer has a shared expert;
- * shared_scale [T] or NULL.  x must be 16-byte aligned.  Checks: those of
+ * shared_scale [T] or NULL (non-NULL needs a shared expert).  x must be
+ * 16-byte aligned.  Checks: those of
  * moe_route_topk and moe_expert_ffn_q; ws_bytes >= moe_forward_workspace_bytes. */
 moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
                        uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,

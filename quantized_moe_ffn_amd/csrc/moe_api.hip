@@ -340,6 +340,8 @@ moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* 
     const float* residual = ep ? ep->residual : nullptr;
     if (sgate_w && !L->has_shared)
         return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue shared_gate given for a layer without a shared expert");
+    if (shared_scale && !L->has_shared)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "shared_scale given for a layer without a shared expert");
     if ((sgate_w && !aligned(sgate_w, 16)) || (residual && !aligned(residual, 4)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: shared_gate must be 16-byte aligned, residual 4-byte aligned");
     if (residual && (residual == y_pair || residual == y_shared))
@@ -449,6 +451,9 @@ moe_status moe_combine(const float* y_pair, const float* w, const float* y_share
                     kMaxTopK);
     if (shared_scale && !y_shared)
         return fail(MOE_ERR_INVALID_ARGUMENT, "shared_scale given without y_shared");
+    if (!aligned(y_pair, 4) || !aligned(w, 4) || !aligned(out, 4) || (y_shared && !aligned(y_shared, 4)) ||
+        (shared_scale && !aligned(shared_scale, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "fp32 arrays must be 4-byte aligned");
     return from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, nullptr, nullptr, T, k, H, out, stream),
                     "moe_combine launch");
 }
@@ -464,6 +469,10 @@ moe_status moe_combine_ep(const float* y_pair, const float* w, const float* y_sh
         return fail(MOE_ERR_INVALID_ARGUMENT, "shared_scale or shared_gate_s given without y_shared");
     if (residual && (residual == y_pair || residual == y_shared))
         return fail(MOE_ERR_INVALID_ARGUMENT, "residual must not alias y_pair or y_shared");
+    if (!aligned(y_pair, 4) || !aligned(w, 4) || !aligned(out, 4) || (y_shared && !aligned(y_shared, 4)) ||
+        (shared_scale && !aligned(shared_scale, 4)) || (shared_gate_s && !aligned(shared_gate_s, 4)) ||
+        (residual && !aligned(residual, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "fp32 arrays must be 4-byte aligned");
     return from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, shared_gate_s, residual, T, k, H, out,
                                         stream),
                     "moe_combine_ep launch");

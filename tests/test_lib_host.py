@@ -241,6 +241,25 @@ def test_forward_ep_validation():
     assert st == 1 and "alias" in qm.moe_last_error()
 
 
+def test_forward_rejects_a_shared_scale_without_a_shared_expert():
+    lib = qm.load_library()
+    a = list(_forward_args(_layer(), _routing_null(), ws_bytes=1 << 30))
+    a[10] = ctypes.c_void_p(20480)               # shared_scale, on a layer with no shared expert
+    assert lib.moe_forward(*a) == 1 and "without a shared expert" in qm.moe_last_error()
+    ep = qm.moe_epilogue(None, None)
+    assert lib.moe_forward_ep(*tuple(a[:11] + [ctypes.byref(ep)] + a[11:])) == 1
+    assert "without a shared expert" in qm.moe_last_error()
+
+
+def test_combine_rejects_misaligned_arrays():
+    lib = qm.load_library()
+    P = ctypes.c_void_p
+    assert lib.moe_combine(P(258), P(512), None, None, 2, 2, 64, P(2048), None) == 1
+    assert "4-byte aligned" in qm.moe_last_error()
+    assert lib.moe_combine_ep(P(256), P(512), P(4096), None, None, P(8194), 2, 2, 64, P(2048), None) == 1
+    assert "4-byte aligned" in qm.moe_last_error()
+
+
 def test_forward_workspace_holds_the_gate_values():
     lib = qm.load_library()
     L = _layer()
