@@ -49,7 +49,7 @@ extern "C" {
 typedef enum moe_status {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARGUMENT = 1, /* a shape, pointer, alignment or flag check failed */
-    MOE_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement      */
+    MOE_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement     */
     MOE_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required       */
     MOE_ERR_DEVICE = 4            /* a HIP call failed, or a kernel set the error word */
 } moe_status;

@@ -158,7 +158,7 @@ moe_status validate_layer(const moe_layer* L, int32_t T, int32_t k, const float*
     if (H < 256 || H % 256 || I < 256 || I % 256)
         return fail(MOE_ERR_INVALID_ARGUMENT, "hidden = %d, inter = %d: both must be positive multiples of 256", H, I);
     if (H > kMaxDim || I > kMaxDim)
-        return fail(MOE_ERR_UNSUPPORTED, "hidden = %d, inter = %d: this build supports up to %d", H, I, kMaxDim);
+        return fail(MOE_ERR_UNSUPPORTED, "hidden = %d, inter = %d: the library supports up to %d", H, I, kMaxDim);
     if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d: need at least one token", T);
     if (k < 1 || k > E || k > kMaxTopK)
         return fail(MOE_ERR_INVALID_ARGUMENT, "k = %d: need 1 <= k <= min(E = %d, %d)", k, E, kMaxTopK);
