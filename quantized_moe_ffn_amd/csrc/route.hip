@@ -27,16 +27,44 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 // Extraction engine: one wave, the E (<= 64*V) logits of one token, lane l
 // owning experts l, l+64, ...  Each lane caches the largest key it still holds
 // (best) and the lowest v holding it (bv), so a round is one DPP wave maximum
-// of best, a ballot, and a readlane of the winner's bv; only the winning lane
-// then rescans its V keys.  Ties: equal keys resolve to the lower expert index
-// (lower v first, since e = lane + 64*v, then the lower lane).  Key 0 marks
-// taken or absent experts; real keys are >= 1.  Rounds return the slots in
-// descending-logit order.  No LDS traffic.
+// of best, a ballot, and a readlane of the winner's bv.  Ties: equal keys
+// resolve to the lower expert index (lower v first, since e = lane + 64*v, then
+// the lower lane).  Key 0 marks taken or absent experts; real keys are >= 1.
+// Rounds return the slots in descending-logit order.  No LDS traffic.
+// Up to kSortedV keys per lane, each lane sorts its keys once (descending,
+// equal keys by ascending v), so the winner of a round only shifts its list
+// by one and its next best is already at the front; with more keys per lane
+// the winner clears the taken key and rescans.
+constexpr int kSortedV = 8;
+
 template <int V>
 struct WaveExtract {
     uint32_t key[V];
+    int vi[V];   // sorted lists: the v of key[i]
     uint32_t best;
     int bv;
+    // Stable descending sort of the lane's keys: odd-even transposition, whose
+    // compare-exchanges touch neighbours only and swap on a strictly larger key,
+    // so equal keys keep their ascending-v order.
+    __device__ __forceinline__ void sort_keys() {
+#pragma unroll
+        for (int v = 0; v < V; ++v) vi[v] = v;
+#pragma unroll
+        for (int ph = 0; ph < V; ++ph) {
+#pragma unroll
+            for (int i = ph & 1; i + 1 < V; i += 2) {
+                const bool sw = key[i + 1] > key[i];
+                const uint32_t ka = key[i], kb = key[i + 1];
+                const int ia = vi[i], ib = vi[i + 1];
+                key[i] = sw ? kb : ka;
+                key[i + 1] = sw ? ka : kb;
+                vi[i] = sw ? ib : ia;
+                vi[i + 1] = sw ? ia : ib;
+            }
+        }
+        best = key[0];
+        bv = vi[0];
+    }
     __device__ __forceinline__ void refresh() {
         best = key[0];
 #pragma unroll
@@ -74,7 +102,11 @@ struct WaveExtract {
             bad |= in & !isfinite(xv[v]);
             key[v] = in ? kk : 0u;
         }
-        refresh();
+        if constexpr (V <= kSortedV) {
+            sort_keys();
+        } else {
+            refresh();
+        }
         return bad;
     }
     // The expert of the next slot; M receives its key.  Branch-free except for
@@ -94,9 +126,22 @@ struct WaveExtract {
             wv = (int)(c / kWave);
         }
         const bool mine = lane == wl;
+        if constexpr (V <= kSortedV) {
+            // the winning lane's taken key is its front one (wv is its bv):
+            // shift its list by one
 #pragma unroll
-        for (int v = 0; v < V; ++v) key[v] = (mine && v == wv) ? 0u : key[v];
-        refresh();
+            for (int v = 0; v + 1 < V; ++v) {
+                key[v] = mine ? key[v + 1] : key[v];
+                vi[v] = mine ? vi[v + 1] : vi[v];
+            }
+            key[V - 1] = mine ? 0u : key[V - 1];
+            best = key[0];
+            bv = vi[0];
+        } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v) key[v] = (mine && v == wv) ? 0u : key[v];
+            refresh();
+        }
         return wl + kWave * wv;
     }
     __device__ __forceinline__ int next() {
