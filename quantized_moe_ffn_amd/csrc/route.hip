@@ -114,18 +114,22 @@ struct WaveExtract {
     __device__ __forceinline__ int next(uint32_t& M) {
         const int lane = threadIdx.x & (kWave - 1);
         M = wave_max_u32(best);
-        const uint64_t lanes = __ballot(best == M);
+        const bool hold = best == M;
+        const uint64_t lanes = __ballot(hold);
         int wl = (int)__builtin_ctzll(lanes);
         int wv = __builtin_amdgcn_readlane(bv, wl);
+        // one holder (the usual case): it is the winner, known without the
+        // scalar lane search, so the next round's maximum need not wait for it
+        bool mine = hold;
         if (__popcll(lanes) != 1) {
             // the lowest (v, lane) among the lanes holding M: a wave minimum of
             // 64*v + lane over those lanes
-            const uint32_t cand = best == M ? (uint32_t)(kWave * bv + lane) : 0xFFFFFFFFu;
+            const uint32_t cand = hold ? (uint32_t)(kWave * bv + lane) : 0xFFFFFFFFu;
             const uint32_t c = ~wave_max_u32(~cand);
             wl = (int)(c & (kWave - 1));
             wv = (int)(c / kWave);
+            mine = lane == wl;
         }
-        const bool mine = lane == wl;
         if constexpr (V <= kSortedV) {
             // the winning lane's taken key is its front one (wv is its bv):
             // shift its list by one
