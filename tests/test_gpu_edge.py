@@ -4,7 +4,8 @@ Covered here: a single expert (E = 1, k = 1); every expert selected (k = E);
 every token routed to the same experts (one bucket spanning several MFMA
 tiles); all-zero activations (the quantiser's amax = 0 rule, outputs exactly 0);
 the largest hidden and intermediate sizes the library takes (3,584); the
-boundary of the AUTO path choice (T = 8 decode, T = 9 int8); and graph replay
+boundary of the AUTO path choice (T = 8 decode, T = 9 int8); logits tied
+within one lane of the extracting wave (E = 256, 512, 1024); and graph replay
 of the int8 path.  References come from the CPU oracle on the same seeded
 inputs; tolerances as in the other parity tests.
 """
@@ -103,6 +104,22 @@ def test_every_token_on_the_same_experts(path, fused):
     bufs = _check(m, dl, w, logits, x, _flags(m, path), fused, TOL_INT8 if path == "int8" else TOL_DECODE)
     counts = bufs.routing.count.cpu().numpy()
     assert sorted(counts[counts > 0].tolist()) == [x.shape[0]] * 3
+
+
+@pytest.mark.parametrize("path,fused", PATHS)
+@pytest.mark.parametrize("E,k", [(256, 8), (512, 10), (1024, 8)])
+def test_tied_logits_held_by_one_lane(E, k, path, fused):
+    """Logits drawn from three values, so every lane of the extracting wave holds
+    equal keys (experts e, e + 64, ...): 4, 8 or 16 keys per lane, the first two on
+    the sorted per-lane lists, the last on the rescan.  The selection must still
+    take equal logits in ascending expert order, on the routing outputs and inside
+    the decode layer's gate/up kernel, whose waves pick their slots themselves."""
+    m = qm()
+    dl, w = _layer(n_experts=E, top_k=k, tokens=3)
+    from quantized_moe_ffn_amd import layers
+    _, x = layers.inputs_np(w, seed=17)
+    logits = np.random.default_rng(E + k).integers(-1, 2, size=(3, E)).astype(np.float32)
+    _check(m, dl, w, logits, x, _flags(m, path), fused, TOL_INT8 if path == "int8" else TOL_DECODE)
 
 
 @pytest.mark.parametrize("path,fused", PATHS)

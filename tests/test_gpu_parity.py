@@ -124,6 +124,18 @@ def test_route_ties_signed_zeros_and_plain_softmax():
     _check_routing(_route(m, lg2, 6, renorm=False), lg2, 6, renorm=False)
 
 
+@pytest.mark.parametrize("E", [128, 256, 512, 1024])
+def test_route_ties_held_by_one_lane(E):
+    """Ties between experts of one lane (e and e + 64, ...): 2 to 16 keys per lane,
+    sorted once per lane up to 8, rescanned above; equal logits in ascending
+    expert order either way."""
+    m = qm()
+    lg = np.random.default_rng(203 + E).integers(-1, 2, size=(24, E)).astype(np.float32)
+    for k in (1, 5, 8, 16):
+        _say("route ties in a lane", E, k)
+        _check_routing(_route(m, lg, k), lg, k)
+
+
 # --------------------------------------------------------------------------- activation quantisation
 
 def test_quantize_act_bit_exact():
