@@ -30,6 +30,11 @@
  *    memory out of bounds.  moe_check_device_errors reports and clears it.
  *  - Results are bitwise deterministic run to run, and a token's result does
  *    not depend on which other tokens share its experts.
+ *  - With MOE_SYNC_DEBUG=1 in the environment (read at every call), each call
+ *    that enqueues work synchronises its stream and checks the device error
+ *    word before returning, so it reports its own asynchronous faults and
+ *    kernel-detected errors (MOE_ERR_DEVICE).  Not done while the stream is
+ *    being captured into a graph.
  *  - All sizes are element counts unless named *_bytes.
  */
 #ifndef MOE_H
@@ -276,9 +281,12 @@ moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* 
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Test hook: dequantize n_weights weights of contiguous blocks to fp32 with the
- * same device unpacking helpers the FFN kernels use.  Each value is the exact
+ * unpacking helpers of the general (unfused) kernels.  Each value is the exact
  * d*sc*q - dmin*m (Q4_K, Q5_K), d*q (Q8_0) or d*q + m (Q5_1) rounded once to
- * fp32.  n_weights must be a multiple of the block size. */
+ * fp32.  The two-kernel decode layer and the int8 MFMA GEMMs unpack the same
+ * blocks with code of their own (per-lane slices; 3-bit scale limbs); those
+ * are pinned by layers whose every result is exact.  n_weights must be a
+ * multiple of the block size. */
 moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, float* out,
                          hipStream_t stream);
 

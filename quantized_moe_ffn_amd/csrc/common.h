@@ -28,7 +28,6 @@ constexpr unsigned kErrExpertRange = 1u;   // an expert id outside [0, E)
 constexpr unsigned kErrPairRange = 2u;     // bucket offsets / pair ids outside their range
 constexpr unsigned kErrLogitNonFinite = 4u;
 constexpr unsigned kErrActNonFinite = 8u;
-constexpr unsigned kErrBarrierTimeout = 16u;
 
 extern __device__ unsigned int g_moe_err;
 

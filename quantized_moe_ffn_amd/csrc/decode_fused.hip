@@ -737,7 +737,6 @@ __global__ void __launch_bounds__((K1Shape<NB, 1>::THREADS)) dec_gateup_pipe_ker
 // ---------------------------------------------------------------------------
 constexpr int kK2MinPasses = 2;   // passes per workgroup: enough to cover H with
 constexpr int kK2MaxPasses = 3;   // about one workgroup per CU
-constexpr int kDecCUs = 256;      // compute units of an MI355X
 constexpr int kK2MaxThreads = 1024;
 
 template <int QD, int NS, int PS>
@@ -796,7 +795,12 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
                 hh4[v] = ph[v];
             }
         }
-        if (!live) continue;
+        if (!live) {   // the combine still reads the slot's rows: zeros, so out stays deterministic
+#pragma unroll
+            for (int pp = 0; pp < PS; ++pp)
+                if (sl == NS - 1) s_y[u * RO + pp * RP + rr] = 0.f;
+            continue;
+        }
         float hl[1][16], hh[1][16], shl[1], shh[1];
         unpack_f4<1>(hl4, hl[0]);
         unpack_f4<1>(hh4, hh[0]);
@@ -845,6 +849,20 @@ namespace {
 // Workgroups of a K1 instance that the current device holds at once (per-CU
 // occupancy times CUs), looked up once per instance and device; 0 if unknown.
 constexpr int kDecMaxDevices = 64;
+
+// Compute units of the current device, looked up once per device (256 on an
+// MI355X; that value if the query fails).
+int device_cus() {
+    static std::atomic<int> cus[kDecMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDecMaxDevices) return 256;
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cus[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
 
 template <int NB, int V, int TT, int SM, int QG>
 int k1_capacity() {
@@ -936,7 +954,8 @@ template <int QD, int NS>
 hipError_t launch_k2(const DecArgs& a, hipStream_t s) {
     constexpr int RP = kWave / NS;
     const int groups = (a.H + RP - 1) / RP;
-    int ps = (groups + kDecCUs - 1) / kDecCUs;
+    const int cus = device_cus();
+    int ps = (groups + cus - 1) / cus;
     ps = ps < kK2MinPasses ? kK2MinPasses : (ps > kK2MaxPasses ? kK2MaxPasses : ps);
     return ps == 2 ? launch_k2p<QD, NS, 2>(a, s) : launch_k2p<QD, NS, 3>(a, s);
 }

@@ -2,6 +2,7 @@
 // validation, workspace layout and dispatch to the kernels.  Nothing here
 // allocates, frees or synchronises (except moe_check_device_errors).
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -31,7 +32,45 @@ moe_status from_hip(hipError_t e, const char* what) {
     return fail(MOE_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
+// Reads and clears the current device's error word (the stream already synchronised).
+// Returns MOE_ERR_DEVICE, with a message that starts with `what`, if it was set.
+moe_status take_error_word(const char* what) {
+    unsigned int word = 0, zero = 0;
+    hipError_t e = hipMemcpyFromSymbol(&word, HIP_SYMBOL(moe::g_moe_err), sizeof(word), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return from_hip(e, "read the device error word");
+    if (word == 0) return ok();
+    e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_moe_err), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return from_hip(e, "clear the device error word");
+    return fail(MOE_ERR_DEVICE, "%sdevice error word 0x%x:%s%s%s%s", what, word,
+                (word & moe::kErrExpertRange) ? " expert id out of range;" : "",
+                (word & moe::kErrPairRange) ? " bucket offsets or pair ids out of range;" : "",
+                (word & moe::kErrLogitNonFinite) ? " non-finite router logit;" : "",
+                (word & moe::kErrActNonFinite) ? " non-finite activation;" : "");
+}
+
+// MOE_SYNC_DEBUG=1 in the environment (read at every call): each call that
+// enqueued work synchronises its stream and checks the device error word
+// before it returns, so an asynchronous fault or a kernel-detected error is
+// reported by the call that caused it.  Skipped while the stream is being
+// captured into a graph (a synchronisation would end the capture).
+moe_status finish(moe_status st, hipStream_t stream, const char* what) {
+    if (st != MOE_OK) return st;
+    const char* v = getenv("MOE_SYNC_DEBUG");
+    if (!v || strcmp(v, "1") != 0) return st;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return from_hip(e, "MOE_SYNC_DEBUG: query stream capture");
+    if (cs != hipStreamCaptureStatusNone) return st;
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s (MOE_SYNC_DEBUG): stream synchronize: HIP error %d (%s)", what,
+                                     (int)e, hipGetErrorString(e));
+    char prefix[160];
+    snprintf(prefix, sizeof(prefix), "%s (MOE_SYNC_DEBUG): ", what);
+    return take_error_word(prefix);
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
 
 bool known_qtype(int qt) { return qt == MOE_Q4_K || qt == MOE_Q5_K || qt == MOE_Q8_0 || qt == MOE_Q5_1; }
 int blk_weights(int qt) { return (qt == MOE_Q8_0 || qt == MOE_Q5_1) ? 32 : 256; }
@@ -245,8 +284,10 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
         return fail(MOE_ERR_WORKSPACE, "routing workspace: %zu bytes given, %zu needed", ws_bytes, need);
     if (need && !aligned(workspace, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 4-byte aligned");
     moe::RoutingPtrs rp{r->idx, r->w, r->count, r->offset, r->pair, r->active, r->n_active};
-    return from_hip(moe::launch_route(logits, T, E, k, (flags & MOE_ROUTE_RENORM) ? 1 : 0, rp, workspace, stream),
-                    "moe_route_topk launch");
+    return finish(from_hip(moe::launch_route(logits, T, E, k, (flags & MOE_ROUTE_RENORM) ? 1 : 0, rp, workspace,
+                                             stream),
+                           "moe_route_topk launch"),
+                  stream, "moe_route_topk");
 }
 
 moe_status moe_quantize_act(const float* x, int32_t T, int32_t H, int8_t* xq, float* xd, hipStream_t stream) {
@@ -255,7 +296,8 @@ moe_status moe_quantize_act(const float* x, int32_t T, int32_t H, int8_t* xq, fl
     if (H < 256 || H % 256 != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "H = %d: must be a positive multiple of 256", H);
     if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xd, 4))
         return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned, xq and xd 4-byte aligned");
-    return from_hip(moe::launch_quantize_act(x, T, H, xq, xd, stream), "moe_quantize_act launch");
+    return finish(from_hip(moe::launch_quantize_act(x, T, H, xq, xd, stream), "moe_quantize_act launch"), stream,
+                  "moe_quantize_act");
 }
 
 moe_status moe_router_logits(const float* x, int32_t T, int32_t H, const float* w_router, int32_t E,
@@ -268,7 +310,8 @@ moe_status moe_router_logits(const float* x, int32_t T, int32_t H, const float* 
                     moe::kRouterMaxH);
     if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(logits, 4))
         return fail(MOE_ERR_INVALID_ARGUMENT, "x and w_router must be 16-byte aligned, logits 4-byte aligned");
-    return from_hip(moe::launch_router(x, T, H, w_router, E, logits, stream), "moe_router_logits launch");
+    return finish(from_hip(moe::launch_router(x, T, H, w_router, E, logits, stream), "moe_router_logits launch"),
+                  stream, "moe_router_logits");
 }
 
 size_t moe_ffn_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t flags) {
@@ -313,8 +356,11 @@ moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T,
     set_ffn_ws(a, (char*)workspace, wl);
     a.y_pair = y_pair;
     a.y_shared = y_shared;
-    if (path == MOE_FFN_DECODE) return from_hip(moe::launch_ffn_decode(a, stream), "moe_expert_ffn_q (decode) launch");
-    return from_hip(moe::launch_ffn_int8(a, stream), "moe_expert_ffn_q (int8) launch");
+    if (path == MOE_FFN_DECODE)
+        return finish(from_hip(moe::launch_ffn_decode(a, stream), "moe_expert_ffn_q (decode) launch"), stream,
+                      "moe_expert_ffn_q");
+    return finish(from_hip(moe::launch_ffn_int8(a, stream), "moe_expert_ffn_q (int8) launch"), stream,
+                  "moe_expert_ffn_q");
 }
 
 size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t ffn_flags) {
@@ -394,7 +440,8 @@ moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* 
         d.residual = residual;
         d.out = out;
         d.route_tab = (int*)(ws + wl.tab);
-        return from_hip(moe::launch_dec_fused(d, stream), "moe_forward (decode) launch");
+        return finish(from_hip(moe::launch_dec_fused(d, stream), "moe_forward (decode) launch"), stream,
+                      "moe_forward");
     }
 
     hipError_t e = moe::launch_route(logits, T, L->n_experts, k, renorm, rp, ws + wl.route, stream);
@@ -428,9 +475,10 @@ moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* 
         e = moe::launch_shared_gate(x, T, L->hidden, sgate_w, sg, stream);
         if (e != hipSuccess) return from_hip(e, "moe_forward: shared-expert gate launch");
     }
-    return from_hip(moe::launch_combine(y_pair, r->w, L->has_shared ? y_shared : nullptr, shared_scale, sg, residual,
-                                        T, k, L->hidden, out, stream),
-                    "moe_forward: combine launch");
+    return finish(from_hip(moe::launch_combine(y_pair, r->w, L->has_shared ? y_shared : nullptr, shared_scale, sg,
+                                               residual, T, k, L->hidden, out, stream),
+                           "moe_forward: combine launch"),
+                  stream, "moe_forward");
 }
 
 moe_status moe_shared_gate(const float* x, int32_t T, int32_t H, const float* gate_w, float* s,
@@ -440,7 +488,8 @@ moe_status moe_shared_gate(const float* x, int32_t T, int32_t H, const float* ga
         return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d, H = %d: need T >= 1 and H a positive multiple of 4", T, H);
     if (!aligned(x, 16) || !aligned(gate_w, 16) || !aligned(s, 4))
         return fail(MOE_ERR_INVALID_ARGUMENT, "x and gate_w must be 16-byte aligned, s 4-byte aligned");
-    return from_hip(moe::launch_shared_gate(x, T, H, gate_w, s, stream), "moe_shared_gate launch");
+    return finish(from_hip(moe::launch_shared_gate(x, T, H, gate_w, s, stream), "moe_shared_gate launch"), stream,
+                  "moe_shared_gate");
 }
 
 moe_status moe_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
@@ -454,8 +503,10 @@ moe_status moe_combine(const float* y_pair, const float* w, const float* y_share
     if (!aligned(y_pair, 4) || !aligned(w, 4) || !aligned(out, 4) || (y_shared && !aligned(y_shared, 4)) ||
         (shared_scale && !aligned(shared_scale, 4)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "fp32 arrays must be 4-byte aligned");
-    return from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, nullptr, nullptr, T, k, H, out, stream),
-                    "moe_combine launch");
+    return finish(from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, nullptr, nullptr, T, k, H, out,
+                                               stream),
+                           "moe_combine launch"),
+                  stream, "moe_combine");
 }
 
 moe_status moe_combine_ep(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
@@ -473,9 +524,10 @@ moe_status moe_combine_ep(const float* y_pair, const float* w, const float* y_sh
         (shared_scale && !aligned(shared_scale, 4)) || (shared_gate_s && !aligned(shared_gate_s, 4)) ||
         (residual && !aligned(residual, 4)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "fp32 arrays must be 4-byte aligned");
-    return from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, shared_gate_s, residual, T, k, H, out,
-                                        stream),
-                    "moe_combine_ep launch");
+    return finish(from_hip(moe::launch_combine(y_pair, w, y_shared, shared_scale, shared_gate_s, residual, T, k, H,
+                                               out, stream),
+                           "moe_combine_ep launch"),
+                  stream, "moe_combine_ep");
 }
 
 moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, float* out, hipStream_t stream) {
@@ -489,24 +541,14 @@ moe_status moe_dequant_q(const void* blocks, int32_t qtype, int64_t n_weights, f
     if (!aligned(blocks, blk_align(qtype)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "blocks must be %d-byte aligned", (int)blk_align(qtype));
     if (n_weights == 0) return ok();
-    return from_hip(moe::launch_dequant(blocks, qtype, n_weights, out, stream), "moe_dequant_q launch");
+    return finish(from_hip(moe::launch_dequant(blocks, qtype, n_weights, out, stream), "moe_dequant_q launch"), stream,
+                  "moe_dequant_q");
 }
 
 moe_status moe_check_device_errors(hipStream_t stream) {
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return from_hip(e, "moe_check_device_errors: stream synchronize");
-    unsigned int word = 0, zero = 0;
-    e = hipMemcpyFromSymbol(&word, HIP_SYMBOL(moe::g_moe_err), sizeof(word), 0, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return from_hip(e, "moe_check_device_errors: read error word");
-    if (word == 0) return ok();
-    e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_moe_err), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
-    if (e != hipSuccess) return from_hip(e, "moe_check_device_errors: clear error word");
-    return fail(MOE_ERR_DEVICE, "device error word 0x%x:%s%s%s%s%s", word,
-                (word & moe::kErrExpertRange) ? " expert id out of range;" : "",
-                (word & moe::kErrPairRange) ? " bucket offsets or pair ids out of range;" : "",
-                (word & moe::kErrLogitNonFinite) ? " non-finite router logit;" : "",
-                (word & moe::kErrActNonFinite) ? " non-finite activation;" : "",
-                (word & moe::kErrBarrierTimeout) ? " grid barrier timed out;" : "");
+    return take_error_word("");
 }
 
 }  // extern "C"
