@@ -280,6 +280,24 @@ moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* 
                           float* y_shared, const float* shared_scale, const moe_epilogue* ep, float* out,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward
+ * with its workspace taken from a static device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU, held by each GPU the library runs on until
+ * the process ends.  Same arguments, checks, results and contract as
+ * moe_forward, without workspace/ws_bytes.  Rejects (MOE_ERR_WORKSPACE, nothing
+ * enqueued) a call whose moe_forward_workspace_bytes exceeds the array: every
+ * decode batch fits, and int8-path batches up to about a thousand tokens of a
+ * hidden-2048 / top-8 / intermediate-512 layer.  Calls no allocating routine.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and give wrong results;
+ * serialise them.  The array needs no clearing: each call writes every byte of
+ * it that it reads. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+moe_status moe_forward_noalloc(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
+                               uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
+                               float* y_shared, const float* shared_scale, float* out, hipStream_t stream);
+
 /* Test hook: dequantize n_weights weights of contiguous blocks to fp32 with the
  * unpacking helpers of the general (unfused) kernels.  Each value is the exact
  * d*sc*q - dmin*m (Q4_K, Q5_K), d*q (Q8_0) or d*q + m (Q5_1) rounded once to

@@ -6,9 +6,18 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "common.h"
 #include "kernels.h"
+
+// Workspace of moe_forward_noalloc: a device array of the library, one copy per
+// GPU, held until the process ends.  Host code never passes its name to a
+// kernel or a copy (on the host the name is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -71,6 +80,38 @@ moe_status finish(moe_status st, hipStream_t stream, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Device address of `scratch` on the device of `stream`, looked up once per
+// device with that device current, and kept.
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+std::mutex g_scratch_mu;
+
+moe_status scratch_address(hipStream_t stream, void** out) {
+    int dev = 0, cur = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return from_hip(e, "moe_forward_noalloc: device of the stream");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_forward_noalloc: device %d (supported: 0..%d)", dev, kScratchDevices - 1);
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_acquire);
+        if (!p) {
+            if ((e = hipGetDevice(&cur)) != hipSuccess) return from_hip(e, "moe_forward_noalloc: current device");
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+                return from_hip(e, "moe_forward_noalloc: make the stream's device current");
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+            if (e != hipSuccess) return from_hip(e, "moe_forward_noalloc: hipGetSymbolAddress(scratch)");
+            if (e2 != hipSuccess) return from_hip(e2, "moe_forward_noalloc: restore the current device");
+            if (!p || ((uintptr_t)p % 256) != 0)
+                return fail(MOE_ERR_DEVICE, "moe_forward_noalloc: scratch address %p is not 256-byte aligned", p);
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return ok();
+}
 
 bool known_qtype(int qt) { return qt == MOE_Q4_K || qt == MOE_Q5_K || qt == MOE_Q8_0 || qt == MOE_Q5_1; }
 int blk_weights(int qt) { return (qt == MOE_Q8_0 || qt == MOE_Q5_1) ? 32 : 256; }
@@ -549,6 +590,26 @@ moe_status moe_check_device_errors(hipStream_t stream) {
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return from_hip(e, "moe_check_device_errors: stream synchronize");
     return take_error_word("");
+}
+
+moe_status moe_forward_noalloc(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
+                               uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
+                               float* y_shared, const float* shared_scale, float* out, hipStream_t stream) {
+    moe_status st = validate_layer(L, T, k, y_shared);
+    if (st != MOE_OK) return st;
+    if (ffn_flags != MOE_FFN_AUTO && ffn_flags != MOE_FFN_DECODE && ffn_flags != MOE_FFN_INT8)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "ffn_flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8",
+                    ffn_flags);
+    const size_t need = forward_ws_layout(L, T, k, resolve_path(ffn_flags, T)).total;
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_WORKSPACE,
+                    "moe_forward_noalloc: T = %d, k = %d needs %zu bytes of workspace; its static scratch holds %zu "
+                    "(use moe_forward with a caller-owned workspace)",
+                    T, k, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((st = scratch_address(stream, &ws)) != MOE_OK) return st;
+    return moe_forward(L, logits, x, T, k, route_flags, ffn_flags, r, y_pair, y_shared, shared_scale, out, ws,
+                       (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

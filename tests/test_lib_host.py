@@ -282,3 +282,23 @@ def test_shared_gate_and_combine_ep_validation():
     assert "without y_shared" in qm.moe_last_error()
     assert lib.moe_combine_ep(P(256), P(512), None, None, None, P(256), 2, 2, 64, P(2048), None) == 1
     assert "alias" in qm.moe_last_error()
+
+
+def test_noalloc_rejects_a_request_beyond_its_scratch_before_any_device_call():
+    """moe_forward_noalloc checks the workspace its call needs against the static scratch
+    (MOE_NOALLOC_SCRATCH_BYTES) before it touches a device: a 4,096-token int8 batch does
+    not fit, and the call fails with the numbers and enqueues nothing."""
+    lib = qm.load_library()
+    r = _routing_null()
+    L = _layer(H=2048, I=512, E=256)
+    T, k = 4096, 8
+    need = lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, 2)
+    assert need > qm.MOE_NOALLOC_SCRATCH_BYTES
+    st = lib.moe_forward_noalloc(ctypes.byref(L), ctypes.c_void_p(4096), ctypes.c_void_p(4096), T, k, 1, 2,
+                                 ctypes.byref(r), ctypes.c_void_p(8192), None, None, ctypes.c_void_p(16384), None)
+    assert st == 3
+    msg = qm.moe_last_error()
+    assert "static scratch" in msg and str(need) in msg
+    # every decode batch fits
+    for T in (1, 3, 8):
+        assert lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, 1) <= qm.MOE_NOALLOC_SCRATCH_BYTES
