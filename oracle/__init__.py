@@ -55,6 +55,7 @@ def _load():
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.orc_threads.restype = ctypes.c_int
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_fp16_to_f64.argtypes = [ctypes.c_uint16]
     lib.orc_fp16_to_f64.restype = ctypes.c_double
     lib.orc_q4k_unpack.argtypes = [P, P, P, P, P, P]
@@ -90,6 +91,12 @@ def _ptr(a: np.ndarray) -> int:
 def threads() -> int:
     """Number of OpenMP threads the oracle's parallel loops use."""
     return int(_load().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (a single-thread baseline
+    runs the same code with n = 1)."""
+    _load().orc_set_threads(int(n))
 
 
 def fp16_to_f64(bits) -> np.ndarray:
@@ -372,3 +379,70 @@ def moe_layer(logits, x, gate, up, down, qtypes, k: int, renorm: bool = True, mo
     res = {"idx": idx, "w": w, "y_pair": y_pair, "y_shared": y_sh, "out": out, "shared_gate": sgv}
     res.update(b)
     return res
+
+
+# ----------------------------------------------------------------------------- int8-path decisions
+
+# Error model of an fp32 evaluation of the int8 path's h (reading R-quant with the
+# int8 path's quantisation points): g and u exact in int32 per 256-block, scaled and
+# summed over the blocks in fp32, so their error is bounded by G_EPS * sum |w x|;
+# silu and the product add a few ulps of h.  An h code is a float-rounding decision
+# when its scaled value h*127/amax lies within that error of a rounding tie.
+G_EPS = 2.0 ** -20
+H_REL = 2.0 ** -20
+
+
+def int8_pair_candidates(Wg, Wu, Wd, x_row):
+    """One pair on the int8 path from dense fp64 matrices (Wg, Wu [I][H], Wd [H][I],
+    rows decoded by ``dequant``): y as defined (x quantized per 256-block in fp32, h in
+    fp64 requantized per 256-block), plus the change of y for each h position whose code
+    is a float-rounding decision (its scaled value within the fp32 error bound of h of a
+    tie): the other neighbouring code there.  Every result in {y + any subset of the
+    deltas} is a correct int8-path output; outside these positions the codes are unique."""
+    xq, xd = quantize_act(np.asarray(x_row, np.float32)[None])
+    xh = np.repeat(xd[0].astype(np.float64), 256) * xq[0].astype(np.float64)
+    g = Wg @ xh
+    u = Wu @ xh
+    with np.errstate(over="ignore"):
+        sg = g / (1.0 + np.exp(-g))
+    h = sg * u
+    dg = G_EPS * (np.abs(Wg) @ np.abs(xh))
+    du = G_EPS * (np.abs(Wu) @ np.abs(xh))
+    dh = 1.1 * dg * np.abs(u) + np.abs(sg) * du + H_REL * np.abs(h)
+    hh = np.zeros_like(h)
+    deltas = []
+    for b in range(len(h) // 256):
+        sl = slice(256 * b, 256 * (b + 1))
+        seg = h[sl]
+        amax = np.abs(seg).max()
+        if amax == 0.0:
+            continue
+        r = seg * (127.0 / amax)
+        c = np.clip(np.rint(r), -127, 127)
+        d = amax / 127.0
+        hh[sl] = d * c
+        rel_amax = dh[sl][np.argmax(np.abs(seg))] / amax
+        band = dh[sl] * (127.0 / amax) + np.abs(r) * (rel_amax + 2.0 ** -22)
+        fl = np.floor(r)
+        near = np.abs((r - fl) - 0.5) <= band
+        for i in np.nonzero(near)[0]:
+            other = fl[i] if c[i] == fl[i] + 1 else fl[i] + 1
+            if abs(other) <= 127:
+                deltas.append(Wd[:, 256 * b + i] * (d * (other - c[i])))
+    return Wd @ hh, deltas
+
+
+def best_candidate_err(got, y, deltas, max_flips=12) -> float:
+    """Smallest normwise error (max |got - ref| / max |ref|) of ``got`` over the candidate
+    set {y + any subset of deltas} of ``int8_pair_candidates``."""
+    import itertools
+    got = np.asarray(got, np.float64)
+    if len(deltas) > max_flips:
+        raise ValueError("%d ambiguous h codes in one pair" % len(deltas))
+    best = np.inf
+    for n in range(len(deltas) + 1):
+        for sub in itertools.combinations(range(len(deltas)), n):
+            ref = y + sum((deltas[i] for i in sub), np.zeros_like(y))
+            den = np.abs(ref).max()
+            best = min(best, float(np.abs(got - ref).max() / (den if den > 0 else 1.0)))
+    return best

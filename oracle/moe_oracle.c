@@ -80,6 +80,16 @@ int orc_threads(void) {
 #endif
 }
 
+/* Threads of the parallel loops from now on (n >= 1); for a single-thread
+ * baseline of the same code. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------- */
 /* IEEE binary16 -> fp64, exact for every bit pattern (incl. subnormals).     */
 /* Q4_K's d/dmin and Q8_0's d are stored as binary16 (R-layout).             */

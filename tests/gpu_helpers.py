@@ -54,63 +54,7 @@ def oracle_shared(dl, hb, tokens, x, mode):
                              np.zeros(len(tokens), np.int32), np.asarray(tokens, np.int32), x, mode)
 
 
-# Error model of the int8 path's h on the GPU, for deciding which h codes are float-rounding
-# decisions.  g and u are int32-exact per 256-block, scaled and summed over the blocks in
-# fp32 (plus the fp16 hi/lo min term at about 2^-22): their error is bounded by
-# G_EPS * sum |w x|.  silu and the product add a few ulps of h.  A code is a rounding
-# decision when its scaled value h*127/amax lies within that error of a tie.
-G_EPS = 2.0 ** -20
-H_REL = 2.0 ** -20
-
-
-def int8_pair_candidates(Wg, Wu, Wd, x_row):
-    """One pair on the int8 path, evaluated as the oracle defines it (x quantized per
-    256-block in fp32, h in fp64 requantized per 256-block), plus the change of y for each
-    h position whose code is a float-rounding decision (its scaled value within the fp32
-    error bound of h of a tie): the other neighbouring code there.  Returns
-    (y, [delta_y, ...]); every result in {y + sum of any subset of the deltas} is a correct
-    int8-path output, and outside these positions the codes are unique."""
-    xq, xd = oracle.quantize_act(np.asarray(x_row, np.float32)[None])
-    xh = np.repeat(xd[0].astype(np.float64), 256) * xq[0].astype(np.float64)
-    g = Wg @ xh
-    u = Wu @ xh
-    with np.errstate(over="ignore"):
-        sg = g / (1.0 + np.exp(-g))
-    h = sg * u
-    dg = G_EPS * (np.abs(Wg) @ np.abs(xh))
-    du = G_EPS * (np.abs(Wu) @ np.abs(xh))
-    dh = 1.1 * dg * np.abs(u) + np.abs(sg) * du + H_REL * np.abs(h)
-    hh = np.zeros_like(h)
-    deltas = []
-    for b in range(len(h) // 256):
-        sl = slice(256 * b, 256 * (b + 1))
-        seg = h[sl]
-        amax = np.abs(seg).max()
-        if amax == 0.0:
-            continue
-        r = seg * (127.0 / amax)
-        c = np.clip(np.rint(r), -127, 127)
-        d = amax / 127.0
-        hh[sl] = d * c
-        rel_amax = dh[sl][np.argmax(np.abs(seg))] / amax
-        band = dh[sl] * (127.0 / amax) + np.abs(r) * (rel_amax + 2.0 ** -22)
-        fl = np.floor(r)
-        near = np.abs((r - fl) - 0.5) <= band
-        for i in np.nonzero(near)[0]:
-            other = fl[i] if c[i] == fl[i] + 1 else fl[i] + 1
-            if abs(other) <= 127:
-                deltas.append(Wd[:, 256 * b + i] * (d * (other - c[i])))
-    return Wd @ hh, deltas
-
-
-def best_candidate_err(got, y, deltas, max_flips=12):
-    """Smallest normwise error of `got` against the candidate set of int8_pair_candidates."""
-    import itertools
-    if len(deltas) > max_flips:
-        raise AssertionError("%d ambiguous h codes in one pair" % len(deltas))
-    best = np.inf
-    for n in range(len(deltas) + 1):
-        for sub in itertools.combinations(range(len(deltas)), n):
-            ref = y + sum((deltas[i] for i in sub), np.zeros_like(y))
-            best = min(best, float(normwise_err(got[None], ref[None])[0]))
-    return best
+# The int8 path's float-rounding code decisions: the oracle's candidate set
+# (oracle.int8_pair_candidates) and the best match against it.
+int8_pair_candidates = oracle.int8_pair_candidates
+best_candidate_err = oracle.best_candidate_err
