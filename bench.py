@@ -137,9 +137,11 @@ def run_workload(args, w, flags, torch, qm, dev, full_layer_oracle=False, single
         for l in range(L):
             lg, x = row[l]
             if routers is not None:
-                qm.moe_router_logits(x, routers[l], lgbuf, stream)
-                lg = lgbuf
-            qm.forward(stack[l].layer, lg, x, k, bufs, flags=flags, stream=stream)
+                # the layer from x and the router matrix: router kernel, then the layer
+                qm.moe_forward_router(stack[l].layer, x, routers[l], lgbuf, k, bufs.routing, bufs.y_pair, bufs.out,
+                                      bufs.fwd_ws, bufs.y_shared, flags=flags, stream=stream)
+            else:
+                qm.forward(stack[l].layer, lg, x, k, bufs, flags=flags, stream=stream)
 
     # unique experts per (replay, layer): algorithmic bytes of each layer call
     stream = torch.cuda.current_stream()
@@ -218,18 +220,20 @@ def run_workload(args, w, flags, torch, qm, dev, full_layer_oracle=False, single
         ops = 2.0 * T * k * 3 * H * I + (2.0 * T * 3 * H * I if w.shared else 0.0)
         achieved = ops / (avg_us / 1e6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profiles(w.name),
-                "kernel": ("moe_router_logits + " if routers is not None else "") +
-                          "moe_forward (int8 path: route, quantize, gate/up, requantize, down, combine)",
+                "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                "traffic": traffic_from_profiles(w.name) if routers is None else None,
+                "kernel": ("moe_forward_router (router kernel, then " if routers is not None else "moe_forward (") +
+                          "int8 path: route, quantize, gate/up, requantize, down, combine)",
                 "ops_per_launch": ops, "avg_launch_us": round(avg_us, 3)}
         if routers is None:
             roof.update(gemm_time(w, stack, inputs, bufs, flags, k, ops, args.steps, L, R, torch, qm))
     else:
         achieved = dom_bytes / (ms_total / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(w.name),
-                "kernel": ("moe_router_logits + " if routers is not None else "") +
-                          "moe_forward (decode: route+gate/up+SiLU kernel, down+combine kernel)",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_from_profiles(w.name) if routers is None else None,
+                "kernel": ("moe_forward_router (router kernel, then " if routers is not None else "moe_forward (") +
+                          "decode: route+gate/up+SiLU kernel, down+combine kernel)",
                 "bytes_per_launch": round(dom_bytes / n_launch), "avg_launch_us": round(avg_us, 3)}
     log("[bench] %s: layer call %.2f us, %s %s" % (w.name, avg_us, roof["achieved"], roof["unit"]))
 
@@ -258,7 +262,7 @@ def run_workload(args, w, flags, torch, qm, dev, full_layer_oracle=False, single
                    "shared_expert": w.shared, "layers": L, "replays": R,
                    "formats": {"gate": fmt(w.qt_gate), "up": fmt(w.qt_up), "down": fmt(w.qt_down)},
                    "parallelism": "single GPU", "graphs": args.graph,
-                   "router": "fp32 [E][H], moe_router_logits in the timed step" if routers is not None else None},
+                   "router": "fp32 [E][H], moe_forward_router in the timed step" if routers is not None else None},
         "hbm_GBps_end_to_end": round(dom_bytes / (ms_total / 1e3) / 1e9, 1),
         "layer_call_us_p10_p50_p90": [pct[10], pct[50], pct[90]],
         "roofline": roof,
@@ -315,8 +319,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", choices=["on", "off"], default="on", help="replay each step as a HIP graph")
     ap.add_argument("--router", action="store_true",
-                    help="compute each layer's logits on the GPU from x and a seeded fp32 [E][H] router "
-                         "matrix (moe_router_logits) inside the timed step")
+                    help="run each layer from x and a seeded fp32 [E][H] router matrix (moe_forward_router: the "
+                         "router projection on the GPU inside the timed step)")
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the tokens per layer call (a decode batch or verify window of the "
                          "same layer shape)")

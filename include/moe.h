@@ -280,6 +280,18 @@ moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* 
                           float* y_shared, const float* shared_scale, const moe_epilogue* ep, float* out,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* The layer from the activations and the router matrix, in one call: the
+ * router projection of moe_router_logits (its kernel, so the same bits, written
+ * to logits fp32 [T][E]), then moe_forward on those logits with moe_forward's
+ * arguments, workspace (moe_forward_workspace_bytes), checks and results
+ * contract.  Router matrices are a GPU stage in front of the top-k ("Strata -
+ * the details", "How it works").  w_router fp32 [E][H], 16-byte aligned;
+ * H <= 8192.  No epilogue (see moe_forward_ep). */
+moe_status moe_forward_router(const moe_layer* L, const float* x, const float* w_router, float* logits, int32_t T,
+                              int32_t k, uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r,
+                              float* y_pair, float* y_shared, const float* shared_scale, float* out, void* workspace,
+                              size_t ws_bytes, hipStream_t stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward
  * with its workspace taken from a static device array of the library,

@@ -8,7 +8,7 @@ loaded, the first call raises.
 
 Entry points keep the C names: ``moe_route_topk``, ``moe_quantize_act``,
 ``moe_router_logits``, ``moe_expert_ffn_q``, ``moe_combine``, ``moe_combine_ep``, ``moe_shared_gate``,
-``moe_forward``, ``moe_forward_ep``, ``moe_forward_noalloc``, ``moe_dequant_q``,
+``moe_forward``, ``moe_forward_ep``, ``moe_forward_noalloc``, ``moe_forward_router``, ``moe_dequant_q``,
 ``moe_check_device_errors``, ``moe_last_error``, ``moe_abi_version``,
 ``moe_route_workspace_bytes``, ``moe_ffn_workspace_bytes``,
 ``moe_forward_workspace_bytes``.
@@ -40,6 +40,7 @@ EXPORTS = (
     "moe_quantize_act", "moe_ffn_workspace_bytes", "moe_expert_ffn_q", "moe_combine",
     "moe_dequant_q", "moe_check_device_errors", "moe_forward_workspace_bytes", "moe_forward",
     "moe_router_logits", "moe_combine_ep", "moe_shared_gate", "moe_forward_ep", "moe_forward_noalloc",
+    "moe_forward_router",
 )
 
 MOE_NOALLOC_SCRATCH_BYTES = 8 << 20   # the static workspace of moe_forward_noalloc, per GPU
@@ -116,6 +117,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(moe_layer), P, P, i32, i32, u32, u32,
                                         ctypes.POINTER(moe_routing), P, P, P, P, P]
     lib.moe_forward_noalloc.restype = st
+    lib.moe_forward_router.argtypes = [ctypes.POINTER(moe_layer), P, P, P, i32, i32, u32, u32,
+                                       ctypes.POINTER(moe_routing), P, P, P, P, P, sz, P]
+    lib.moe_forward_router.restype = st
     lib.moe_combine_ep.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P]
     lib.moe_combine_ep.restype = st
     lib.moe_shared_gate.argtypes = [P, i32, i32, P, P, P]
@@ -315,6 +319,18 @@ def moe_forward_noalloc(layer: Layer, logits, x, k: int, routing: Routing, y_pai
                                             _ptr(y_pair), _ptr(y_shared), _ptr(shared_scale), _ptr(out),
                                             _stream(stream))
     _check(st, "moe_forward_noalloc")
+
+
+def moe_forward_router(layer: Layer, x, w_router, logits, k: int, routing: Routing, y_pair, out, workspace,
+                       y_shared=None, shared_scale=None, renorm: bool = True, flags: int = MOE_FFN_AUTO, stream=None):
+    """The layer from x and the router matrix (logits written); moe_forward's workspace."""
+    T = x.shape[0]
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().moe_forward_router(ctypes.byref(layer.struct()), _ptr(x), _ptr(w_router), _ptr(logits), T, k,
+                                           MOE_ROUTE_RENORM if renorm else 0, flags, ctypes.byref(routing.struct()),
+                                           _ptr(y_pair), _ptr(y_shared), _ptr(shared_scale), _ptr(out),
+                                           _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "moe_forward_router")
 
 
 def moe_check_device_errors(stream=None):

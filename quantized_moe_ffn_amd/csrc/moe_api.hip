@@ -292,6 +292,122 @@ bool use_fused_decode(const moe_layer* L, int T, int k, const float* x, uint32_t
     return true;
 }
 
+// The router stage of moe_forward_router: the router matrix.
+struct RouterStage {
+    const float* w;
+};
+
+// moe_forward_ep, and with rt the layer from x and the router matrix (logits
+// are then written by moe_router_logits' kernel ahead of the layer).
+moe_status forward_impl(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
+                        uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
+                        float* y_shared, const float* shared_scale, const moe_epilogue* ep, float* out,
+                        void* workspace, size_t ws_bytes, hipStream_t stream, const RouterStage* rt) {
+    moe_status st = validate_layer(L, T, k, y_shared);
+    if (st != MOE_OK) return st;
+    const float* sgate_w = ep ? ep->shared_gate : nullptr;
+    const float* residual = ep ? ep->residual : nullptr;
+    if (sgate_w && !L->has_shared)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue shared_gate given for a layer without a shared expert");
+    if (shared_scale && !L->has_shared)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "shared_scale given for a layer without a shared expert");
+    if ((sgate_w && !aligned(sgate_w, 16)) || (residual && !aligned(residual, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: shared_gate must be 16-byte aligned, residual 4-byte aligned");
+    if (residual && (residual == y_pair || residual == y_shared))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: residual must not alias y_pair or y_shared");
+    if (!logits || !x || !out || !y_pair) return fail(MOE_ERR_INVALID_ARGUMENT, "logits, x, y_pair or out is NULL");
+    if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(out, 4) || !aligned(y_pair, 4) ||
+        (y_shared && !aligned(y_shared, 4)) || (shared_scale && !aligned(shared_scale, 4)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned, the other fp32 arrays 4-byte aligned");
+    if (route_flags & ~(uint32_t)MOE_ROUTE_RENORM)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "route_flags = 0x%x: only MOE_ROUTE_RENORM is defined", route_flags);
+    if (ffn_flags != MOE_FFN_AUTO && ffn_flags != MOE_FFN_DECODE && ffn_flags != MOE_FFN_INT8)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "ffn_flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8",
+                    ffn_flags);
+    if (!r || !r->idx || !r->w || !r->count || !r->offset || !r->pair || !r->active || !r->n_active)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_routing or one of its arrays is NULL");
+    const uint32_t path = resolve_path(ffn_flags, T);
+    const ForwardWorkspace wl = forward_ws_layout(L, T, k, path);
+    if (!workspace || ws_bytes < wl.total)
+        return fail(MOE_ERR_WORKSPACE, "forward workspace: %zu bytes given, %zu needed", ws_bytes, wl.total);
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    char* ws = (char*)workspace;
+    moe::RoutingPtrs rp{r->idx, r->w, r->count, r->offset, r->pair, r->active, r->n_active};
+    const int renorm = (route_flags & MOE_ROUTE_RENORM) ? 1 : 0;
+    if (rt) {
+        const hipError_t e0 = moe::launch_router(x, T, L->hidden, rt->w, L->n_experts, (float*)logits, stream);
+        if (e0 != hipSuccess) return from_hip(e0, "moe_forward_router: router launch");
+    }
+
+    if (use_fused_decode(L, T, k, x, path)) {
+        moe::DecArgs d{};
+        d.logits = logits;
+        d.x = x;
+        d.gate = to_qmat(L->gate);
+        d.up = to_qmat(L->up);
+        d.down = to_qmat(L->down);
+        d.has_shared = L->has_shared ? 1 : 0;
+        if (d.has_shared) {
+            d.sgate = to_qmat(L->sh_gate);
+            d.sup = to_qmat(L->sh_up);
+            d.sdown = to_qmat(L->sh_down);
+        }
+        d.T = T;
+        d.E = L->n_experts;
+        d.k = k;
+        d.H = L->hidden;
+        d.I = L->inter;
+        d.renorm = renorm;
+        d.r = rp;
+        d.h = (float*)(ws + wl.ffn);
+        d.y_pair = y_pair;
+        d.y_shared = y_shared;
+        d.shared_scale = shared_scale;
+        d.sgate_w = sgate_w;
+        d.residual = residual;
+        d.out = out;
+        d.route_tab = (int*)(ws + wl.tab);
+        return finish(from_hip(moe::launch_dec_fused(d, stream), "moe_forward (decode) launch"), stream,
+                      rt ? "moe_forward_router" : "moe_forward");
+    }
+
+    hipError_t e = moe::launch_route(logits, T, L->n_experts, k, renorm, rp, ws + wl.route, stream);
+    if (e != hipSuccess) return from_hip(e, "moe_forward: routing launch");
+    moe::FfnArgs a{};
+    fill_ffn_args(a, L, T, k);
+    a.count = r->count;
+    a.offset = r->offset;
+    a.pair = r->pair;
+    a.active = r->active;
+    a.n_active = r->n_active;
+    a.x = x;
+    a.xq = (int8_t*)(ws + wl.xq);
+    a.xd = (float*)(ws + wl.xd);
+    set_ffn_ws(a, ws + wl.ffn, ffn_ws_layout(L, T, k, path));
+    a.y_pair = y_pair;
+    a.y_shared = y_shared;
+    if (path == MOE_FFN_INT8) {
+        // the MFMA GEMMs' per-32 code sums come out of the same pass (a.xs is null otherwise)
+        e = moe::launch_quantize_act(x, T, L->hidden, (int8_t*)a.xq, (float*)a.xd, stream, a.xs);
+        a.xs_ready = a.xs ? 1 : 0;
+        if (e != hipSuccess) return from_hip(e, "moe_forward: quantisation launch");
+        e = moe::launch_ffn_int8(a, stream);
+    } else {
+        e = moe::launch_ffn_decode(a, stream);
+    }
+    if (e != hipSuccess) return from_hip(e, "moe_forward: expert FFN launch");
+    float* sg = nullptr;
+    if (sgate_w) {
+        sg = (float*)(ws + wl.sg);
+        e = moe::launch_shared_gate(x, T, L->hidden, sgate_w, sg, stream);
+        if (e != hipSuccess) return from_hip(e, "moe_forward: shared-expert gate launch");
+    }
+    return finish(from_hip(moe::launch_combine(y_pair, r->w, L->has_shared ? y_shared : nullptr, shared_scale, sg,
+                                               residual, T, k, L->hidden, out, stream),
+                           "moe_forward: combine launch"),
+                  stream, "moe_forward");
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,105 +537,22 @@ moe_status moe_forward_ep(const moe_layer* L, const float* logits, const float* 
                           uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r, float* y_pair,
                           float* y_shared, const float* shared_scale, const moe_epilogue* ep, float* out,
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
-    moe_status st = validate_layer(L, T, k, y_shared);
-    if (st != MOE_OK) return st;
-    const float* sgate_w = ep ? ep->shared_gate : nullptr;
-    const float* residual = ep ? ep->residual : nullptr;
-    if (sgate_w && !L->has_shared)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue shared_gate given for a layer without a shared expert");
-    if (shared_scale && !L->has_shared)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "shared_scale given for a layer without a shared expert");
-    if ((sgate_w && !aligned(sgate_w, 16)) || (residual && !aligned(residual, 4)))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: shared_gate must be 16-byte aligned, residual 4-byte aligned");
-    if (residual && (residual == y_pair || residual == y_shared))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: residual must not alias y_pair or y_shared");
-    if (!logits || !x || !out || !y_pair) return fail(MOE_ERR_INVALID_ARGUMENT, "logits, x, y_pair or out is NULL");
-    if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(out, 4) || !aligned(y_pair, 4) ||
-        (y_shared && !aligned(y_shared, 4)) || (shared_scale && !aligned(shared_scale, 4)))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned, the other fp32 arrays 4-byte aligned");
-    if (route_flags & ~(uint32_t)MOE_ROUTE_RENORM)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "route_flags = 0x%x: only MOE_ROUTE_RENORM is defined", route_flags);
-    if (ffn_flags != MOE_FFN_AUTO && ffn_flags != MOE_FFN_DECODE && ffn_flags != MOE_FFN_INT8)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "ffn_flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8",
-                    ffn_flags);
-    if (!r || !r->idx || !r->w || !r->count || !r->offset || !r->pair || !r->active || !r->n_active)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_routing or one of its arrays is NULL");
-    const uint32_t path = resolve_path(ffn_flags, T);
-    const ForwardWorkspace wl = forward_ws_layout(L, T, k, path);
-    if (!workspace || ws_bytes < wl.total)
-        return fail(MOE_ERR_WORKSPACE, "forward workspace: %zu bytes given, %zu needed", ws_bytes, wl.total);
-    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    char* ws = (char*)workspace;
-    moe::RoutingPtrs rp{r->idx, r->w, r->count, r->offset, r->pair, r->active, r->n_active};
-    const int renorm = (route_flags & MOE_ROUTE_RENORM) ? 1 : 0;
+    return forward_impl(L, logits, x, T, k, route_flags, ffn_flags, r, y_pair, y_shared, shared_scale, ep, out,
+                        workspace, ws_bytes, stream, nullptr);
+}
 
-    if (use_fused_decode(L, T, k, x, path)) {
-        moe::DecArgs d{};
-        d.logits = logits;
-        d.x = x;
-        d.gate = to_qmat(L->gate);
-        d.up = to_qmat(L->up);
-        d.down = to_qmat(L->down);
-        d.has_shared = L->has_shared ? 1 : 0;
-        if (d.has_shared) {
-            d.sgate = to_qmat(L->sh_gate);
-            d.sup = to_qmat(L->sh_up);
-            d.sdown = to_qmat(L->sh_down);
-        }
-        d.T = T;
-        d.E = L->n_experts;
-        d.k = k;
-        d.H = L->hidden;
-        d.I = L->inter;
-        d.renorm = renorm;
-        d.r = rp;
-        d.h = (float*)(ws + wl.ffn);
-        d.y_pair = y_pair;
-        d.y_shared = y_shared;
-        d.shared_scale = shared_scale;
-        d.sgate_w = sgate_w;
-        d.residual = residual;
-        d.out = out;
-        d.route_tab = (int*)(ws + wl.tab);
-        return finish(from_hip(moe::launch_dec_fused(d, stream), "moe_forward (decode) launch"), stream,
-                      "moe_forward");
-    }
-
-    hipError_t e = moe::launch_route(logits, T, L->n_experts, k, renorm, rp, ws + wl.route, stream);
-    if (e != hipSuccess) return from_hip(e, "moe_forward: routing launch");
-    moe::FfnArgs a{};
-    fill_ffn_args(a, L, T, k);
-    a.count = r->count;
-    a.offset = r->offset;
-    a.pair = r->pair;
-    a.active = r->active;
-    a.n_active = r->n_active;
-    a.x = x;
-    a.xq = (int8_t*)(ws + wl.xq);
-    a.xd = (float*)(ws + wl.xd);
-    set_ffn_ws(a, ws + wl.ffn, ffn_ws_layout(L, T, k, path));
-    a.y_pair = y_pair;
-    a.y_shared = y_shared;
-    if (path == MOE_FFN_INT8) {
-        // the MFMA GEMMs' per-32 code sums come out of the same pass (a.xs is null otherwise)
-        e = moe::launch_quantize_act(x, T, L->hidden, (int8_t*)a.xq, (float*)a.xd, stream, a.xs);
-        a.xs_ready = a.xs ? 1 : 0;
-        if (e != hipSuccess) return from_hip(e, "moe_forward: quantisation launch");
-        e = moe::launch_ffn_int8(a, stream);
-    } else {
-        e = moe::launch_ffn_decode(a, stream);
-    }
-    if (e != hipSuccess) return from_hip(e, "moe_forward: expert FFN launch");
-    float* sg = nullptr;
-    if (sgate_w) {
-        sg = (float*)(ws + wl.sg);
-        e = moe::launch_shared_gate(x, T, L->hidden, sgate_w, sg, stream);
-        if (e != hipSuccess) return from_hip(e, "moe_forward: shared-expert gate launch");
-    }
-    return finish(from_hip(moe::launch_combine(y_pair, r->w, L->has_shared ? y_shared : nullptr, shared_scale, sg,
-                                               residual, T, k, L->hidden, out, stream),
-                           "moe_forward: combine launch"),
-                  stream, "moe_forward");
+moe_status moe_forward_router(const moe_layer* L, const float* x, const float* w_router, float* logits, int32_t T,
+                              int32_t k, uint32_t route_flags, uint32_t ffn_flags, const moe_routing* r,
+                              float* y_pair, float* y_shared, const float* shared_scale, float* out, void* workspace,
+                              size_t ws_bytes, hipStream_t stream) {
+    if (!L) return fail(MOE_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
+    if (!w_router || !aligned(w_router, 16))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "w_router is NULL or not 16-byte aligned");
+    if (L->hidden > moe::kRouterMaxH)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden = %d: the router supports up to %d", L->hidden, moe::kRouterMaxH);
+    const RouterStage rt{w_router};
+    return forward_impl(L, logits, x, T, k, route_flags, ffn_flags, r, y_pair, y_shared, shared_scale, nullptr, out,
+                        workspace, ws_bytes, stream, &rt);
 }
 
 moe_status moe_shared_gate(const float* x, int32_t T, int32_t H, const float* gate_w, float* s,

@@ -302,3 +302,23 @@ def test_noalloc_rejects_a_request_beyond_its_scratch_before_any_device_call():
     # every decode batch fits
     for T in (1, 3, 8):
         assert lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, 1) <= qm.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_forward_router_checks_its_arguments_before_any_device_call():
+    """moe_forward_router takes moe_forward's workspace: a short or missing one, or a
+    missing or misaligned router matrix, fails with a message and enqueues nothing."""
+    lib = qm.load_library()
+    r = _routing_null()
+    L = _layer(H=2048, I=512, E=256)
+    T, k = 1, 8
+    fwd = lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, 1)
+    P = ctypes.c_void_p
+    args = (T, k, 1, 1, ctypes.byref(r), P(8192), None, None, P(16384))
+    assert lib.moe_forward_router(ctypes.byref(L), P(4096), P(4096), P(4096), *args, None, 0, None) == 3
+    assert "forward workspace" in qm.moe_last_error()
+    assert lib.moe_forward_router(ctypes.byref(L), P(4096), None, P(4096), *args, P(1 << 20), 1 << 20, None) == 1
+    assert "w_router" in qm.moe_last_error()
+    assert lib.moe_forward_router(ctypes.byref(L), P(4096), P(4100), P(4096), *args, P(1 << 20), 1 << 20, None) == 1
+    assert "w_router" in qm.moe_last_error()
+    assert lib.moe_forward_router(ctypes.byref(L), P(4096), P(4096), P(4096), *args, P(1 << 20), fwd - 1, None) == 3
+    assert "forward workspace" in qm.moe_last_error()
