@@ -370,39 +370,62 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 }
 
 // Four consecutive outputs per thread with 16-byte loads and stores (the same
-// per-element summation order as combine_kernel, so the same bits).
+// per-element summation order as combine_kernel, so the same bits). The pair
+// rows of a token are loaded kRows at a time before any of them is summed, so a
+// thread waits on one memory round trip per kRows rows, not one per row.
 __global__ void __launch_bounds__(256) combine4_kernel(const float4* __restrict__ y_pair,
                                                        const float* __restrict__ w,
                                                        const float4* __restrict__ y_shared,
                                                        const float* __restrict__ shared_scale,
                                                        const float* __restrict__ sgate, const float4* residual,
                                                        int T, int k, int H4, float4* out) {
+    constexpr int kRows = 8;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)T * H4) return;
     const int t = (int)(idx / H4), o = (int)(idx - (int64_t)t * H4);
+    const float4* yp = y_pair + (int64_t)t * k * H4 + o;
+    const float* wt = w + (int64_t)t * k;
+    float4 ys = make_float4(0.f, 0.f, 0.f, 0.f), rs = ys;
+    float ss = 1.0f, sg = 1.0f;
+    if (y_shared) {
+        ys = y_shared[(int64_t)t * H4 + o];
+        if (shared_scale) ss = shared_scale[t];
+        if (sgate) sg = sgate[t];
+    }
+    if (residual) rs = residual[idx];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const float wj = w[t * k + j];
-        const float4 y = y_pair[((int64_t)t * k + j) * H4 + o];
-        acc.x = fmaf(wj, y.x, acc.x);
-        acc.y = fmaf(wj, y.y, acc.y);
-        acc.z = fmaf(wj, y.z, acc.z);
-        acc.w = fmaf(wj, y.w, acc.w);
+    for (int j0 = 0; j0 < k; j0 += kRows) {
+        float4 y[kRows];
+        float wj[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            if (j0 + i < k) {
+                y[i] = yp[(int64_t)(j0 + i) * H4];
+                wj[i] = wt[j0 + i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            if (j0 + i < k) {
+                acc.x = fmaf(wj[i], y[i].x, acc.x);
+                acc.y = fmaf(wj[i], y[i].y, acc.y);
+                acc.z = fmaf(wj[i], y[i].z, acc.z);
+                acc.w = fmaf(wj[i], y[i].w, acc.w);
+            }
+        }
     }
     if (y_shared) {
-        const float sc = (shared_scale ? shared_scale[t] : 1.0f) * (sgate ? sgate[t] : 1.0f);
-        const float4 ys = y_shared[(int64_t)t * H4 + o];
+        const float sc = ss * sg;
         acc.x = fmaf(sc, ys.x, acc.x);
         acc.y = fmaf(sc, ys.y, acc.y);
         acc.z = fmaf(sc, ys.z, acc.z);
         acc.w = fmaf(sc, ys.w, acc.w);
     }
     if (residual) {
-        const float4 r = residual[idx];
-        acc.x += r.x;
-        acc.y += r.y;
-        acc.z += r.z;
-        acc.w += r.w;
+        acc.x += rs.x;
+        acc.y += rs.y;
+        acc.z += rs.z;
+        acc.w += rs.w;
     }
     out[idx] = acc;
 }

@@ -15,9 +15,24 @@
 
 namespace moe {
 
-hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s) {
+TileList int8_tile_list(const FfnArgs& a) {
+    TileList t{};
     // (the shared expert's formats equal the routed ones: checked by the API layer)
-    if (a.tiles && mfma_path_supported(a.H, a.I, a.gate.qtype, a.up.qtype, a.down.qtype)) {
+    if (!a.tiles || !mfma_path_supported(a.H, a.I, a.gate.qtype, a.up.qtype, a.down.qtype)) return t;
+    const size_t half = (mfma_tiles_bytes(a.T, a.k, a.E, a.has_shared, a.H, a.I) - 256) / 2;
+    t.tile_e = a.tiles;
+    t.tile_m0 = a.tiles + half / sizeof(int32_t);
+    t.n_tiles = a.tiles + 2 * (half / sizeof(int32_t));
+    t.mt = mfma_tile_rows(a.T, a.k, a.E, a.H, a.I);
+    t.max_t = max_tiles(a.T, a.k, a.E, a.has_shared, t.mt);
+    t.T = a.T;
+    t.has_shared = a.has_shared;
+    return t;
+}
+
+hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s) {
+    const TileList tl = int8_tile_list(a);
+    if (tl.mt > 0) {
         MfmaArgs m{};
         m.gate = a.gate;
         m.up = a.up;
@@ -43,10 +58,10 @@ hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s) {
         m.y_pair = a.y_pair;
         m.y_shared = a.y_shared;
         m.xs_ready = a.xs_ready;
-        const size_t half = (mfma_tiles_bytes(a.T, a.k, a.E, a.has_shared, a.H, a.I) - 256) / 2;
-        m.tile_e = a.tiles;
-        m.tile_m0 = a.tiles + half / sizeof(int32_t);
-        m.n_tiles = a.tiles + 2 * (half / sizeof(int32_t));
+        m.tile_e = tl.tile_e;
+        m.tile_m0 = tl.tile_m0;
+        m.n_tiles = tl.n_tiles;
+        m.tiles_ready = a.tiles_ready;
         return launch_ffn_mfma(m, s);
     }
     hipError_t e = launch_gateup(a, 1, s);

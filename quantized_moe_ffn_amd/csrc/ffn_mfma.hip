@@ -623,37 +623,14 @@ __global__ void __launch_bounds__(256) act_sums_kernel(const int8_t* __restrict_
     xs[idx] = (int16_t)s;
 }
 
-// Tile list: tiles of 'mt' bucket entries per expert with count > 0, in
-// ascending expert order, then the shared expert's tiles (e == E).
-__global__ void __launch_bounds__(1024) mfma_tiles_kernel(const int32_t* __restrict__ count, int E, int T,
-                                                          int npairs, int has_shared, int mt, int max_t,
-                                                          int32_t* __restrict__ tile_e,
-                                                          int32_t* __restrict__ tile_m0,
-                                                          int32_t* __restrict__ n_tiles) {
+// Tile list of a caller's routing (write_tile_list: 'mt' bucket entries per
+// tile, experts in ascending order, then the shared expert's tiles, e == E).
+__global__ void __launch_bounds__(1024) mfma_tiles_kernel(const int32_t* __restrict__ count, int E, int npairs,
+                                                          TileList tl) {
     __shared__ int s_wave[kWave + 1];
+    __shared__ int s_start[1024];
     const int tid = threadIdx.x;
-    int c = tid < E ? count[tid] : 0;
-    if (c < 0 || c > npairs) {
-        raise_error(kErrPairRange);
-        c = 0;
-    }
-    const int nt = (c + mt - 1) / mt;
-    int total = 0;
-    const int start = block_exclusive_scan(nt, s_wave, total);
-    // counts that sum past T*k cannot come from a routing call; never write past the list
-    for (int i = 0; i < nt && start + i < max_t; ++i) {
-        tile_e[start + i] = tid;
-        tile_m0[start + i] = i * mt;
-    }
-    const int ns = has_shared ? (T + mt - 1) / mt : 0;
-    for (int i = tid; i < ns && total + i < max_t; i += blockDim.x) {
-        tile_e[total + i] = E;
-        tile_m0[total + i] = i * mt;
-    }
-    if (tid == 0) {
-        if (total + ns > max_t) raise_error(kErrPairRange);
-        *n_tiles = min(total + ns, max_t);
-    }
+    write_tile_list(tid < E ? count[tid] : 0, npairs, E, tl, s_wave, s_start);
 }
 
 
@@ -668,10 +645,12 @@ template <int MTILES, int QG, int QD>
 hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     constexpr int MT = 32 * MTILES;
     const int maxt = max_tiles(a.T, a.k, a.E, a.has_shared, MT);
-    mfma_tiles_kernel<<<1, 1024, 0, s>>>(a.count, a.E, a.T, a.T * a.k, a.has_shared, MT, maxt, a.tile_e,
-                                         a.tile_m0, a.n_tiles);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (!a.tiles_ready) {
+        const TileList tl{a.tile_e, a.tile_m0, a.n_tiles, MT, maxt, a.T, a.has_shared};
+        mfma_tiles_kernel<<<1, 1024, 0, s>>>(a.count, a.E, a.T * a.k, tl);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (!a.xs_ready) {
         const int64_t n_sums = (int64_t)a.T * (a.H / 32);
         act_sums_kernel<<<(unsigned)((n_sums + 255) / 256), 256, 0, s>>>(a.xq, n_sums, a.H, a.xs);

@@ -51,6 +51,19 @@ struct FfnArgs {
     int16_t* hs;                   // workspace [T*k + T][I/32]: per-32 sums of hq (int8 MFMA path)
     int32_t* tiles;                // workspace: MFMA tile list (mfma_tiles_bytes)
     int xs_ready;                  // xs already holds the per-32 sums of xq
+    int tiles_ready;               // the tile list in tiles is already written (by the routing launches)
+};
+
+// The MFMA GEMMs' work list: tile i of expert e covers rows mt*i .. mt*i + mt - 1
+// of e's bucket; the shared expert's tiles (expert index E) cover all T tokens.
+struct TileList {
+    int32_t* tile_e;
+    int32_t* tile_m0;
+    int32_t* n_tiles;
+    int mt;                        // tokens per tile; 0: no tile list
+    int max_t;                     // capacity of tile_e / tile_m0
+    int T;
+    int has_shared;
 };
 
 // The grouped int8 MFMA GEMMs of the int8 path (Q4_K gate/up/down).
@@ -75,6 +88,7 @@ struct MfmaArgs {
     int32_t* n_tiles;
     int down_rounds;               // 256-row rounds per down workgroup (set by the launcher)
     int xs_ready;                  // xs already holds the per-32 sums of xq (written with the codes)
+    int tiles_ready;               // tile_e / tile_m0 / n_tiles already hold the tile list
 };
 
 bool mfma_path_supported(int H, int I, int qg, int qu, int qd);
@@ -106,14 +120,29 @@ constexpr int kDecRouteTabBytes = 4096;
 bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd);
 hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s);
 
+// The int8 path's other two prologue stages, carried by the routing launches of
+// a layer call: quantisation of x (launch_quantize_act's rule and outputs) and,
+// with tiles.mt > 0, the MFMA tile list (written from the bucket counts).
+struct RouteExtras {
+    const float* x;                // [T][H], 16-byte aligned
+    int H;
+    int8_t* xq;
+    float* xd;
+    int16_t* xs;                   // may be null (no per-32 sums)
+    TileList tiles;
+    bool tiles_written;            // set by launch_route
+};
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, const RoutingPtrs& r,
-                        void* ws, hipStream_t s);
+                        void* ws, hipStream_t s, RouteExtras* ex = nullptr);
 size_t route_workspace_bytes(int T, int E, int k);
 
 hipError_t launch_gateup(const FfnArgs& a, int xmode, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, int hmode, hipStream_t s);
 hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s);
+// The tile list launch_ffn_int8's MFMA GEMMs would use (mt = 0 when it takes another path).
+TileList int8_tile_list(const FfnArgs& a);
 
 constexpr int kRouterGemvMaxT = 16;   // router: tokens up to which the matrix-vector kernel runs
 constexpr int kRouterMaxH = 8192;     // router: largest hidden size

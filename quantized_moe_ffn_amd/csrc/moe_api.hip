@@ -371,8 +371,6 @@ moe_status forward_impl(const moe_layer* L, const float* logits, const float* x,
                       rt ? "moe_forward_router" : "moe_forward");
     }
 
-    hipError_t e = moe::launch_route(logits, T, L->n_experts, k, renorm, rp, ws + wl.route, stream);
-    if (e != hipSuccess) return from_hip(e, "moe_forward: routing launch");
     moe::FfnArgs a{};
     fill_ffn_args(a, L, T, k);
     a.count = r->count;
@@ -386,13 +384,25 @@ moe_status forward_impl(const moe_layer* L, const float* logits, const float* x,
     set_ffn_ws(a, ws + wl.ffn, ffn_ws_layout(L, T, k, path));
     a.y_pair = y_pair;
     a.y_shared = y_shared;
+    hipError_t e;
     if (path == MOE_FFN_INT8) {
-        // the MFMA GEMMs' per-32 code sums come out of the same pass (a.xs is null otherwise)
-        e = moe::launch_quantize_act(x, T, L->hidden, (int8_t*)a.xq, (float*)a.xd, stream, a.xs);
+        // The routing launches also quantise x (with the MFMA GEMMs' per-32 code
+        // sums when a.xs is set) and, on large batches, write the tile list.
+        moe::RouteExtras ex{};
+        ex.x = x;
+        ex.H = L->hidden;
+        ex.xq = (int8_t*)a.xq;
+        ex.xd = (float*)a.xd;
+        ex.xs = a.xs;
+        ex.tiles = moe::int8_tile_list(a);
+        e = moe::launch_route(logits, T, L->n_experts, k, renorm, rp, ws + wl.route, stream, &ex);
+        if (e != hipSuccess) return from_hip(e, "moe_forward: routing and quantisation launch");
         a.xs_ready = a.xs ? 1 : 0;
-        if (e != hipSuccess) return from_hip(e, "moe_forward: quantisation launch");
+        a.tiles_ready = ex.tiles_written ? 1 : 0;
         e = moe::launch_ffn_int8(a, stream);
     } else {
+        e = moe::launch_route(logits, T, L->n_experts, k, renorm, rp, ws + wl.route, stream);
+        if (e != hipSuccess) return from_hip(e, "moe_forward: routing launch");
         e = moe::launch_ffn_decode(a, stream);
     }
     if (e != hipSuccess) return from_hip(e, "moe_forward: expert FFN launch");

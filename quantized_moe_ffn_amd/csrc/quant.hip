@@ -14,13 +14,12 @@ namespace moe {
 
 constexpr int kQBlocksPerWave = 4;   // blocks of one wave, loaded together
 
-// One wave per kQBlocksPerWave consecutive (row, 256-block)s: lane l holds
-// elements 4l..4l+3 of each.  With xs non-null it also writes the exact sums
-// of every 32 codes (int16, |sum| <= 4064), which the int8 MFMA GEMMs use.
-__global__ void __launch_bounds__(256) quantize_act_kernel(const float* __restrict__ x, int64_t n_blocks,
-                                                           int8_t* __restrict__ xq, float* __restrict__ xd,
-                                                           int16_t* __restrict__ xs) {
-    const int64_t blk0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kQBlocksPerWave;
+// Wave number wv quantises kQBlocksPerWave consecutive (row, 256-block)s: lane
+// l holds elements 4l..4l+3 of each.  With xs non-null it also writes the exact
+// sums of every 32 codes (int16, |sum| <= 4064), which the int8 MFMA GEMMs use.
+__device__ void quantize_act_wave(int64_t wv, const float* __restrict__ x, int64_t n_blocks,
+                                  int8_t* __restrict__ xq, float* __restrict__ xd, int16_t* __restrict__ xs) {
+    const int64_t blk0 = wv * kQBlocksPerWave;
     const int lane = threadIdx.x & (kWave - 1);
     if (blk0 >= n_blocks) return;
     float4 v[kQBlocksPerWave];
@@ -61,10 +60,22 @@ __global__ void __launch_bounds__(256) quantize_act_kernel(const float* __restri
     }
 }
 
+__global__ void __launch_bounds__(256) quantize_act_kernel(const float* __restrict__ x, int64_t n_blocks,
+                                                           int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                           int16_t* __restrict__ xs) {
+    quantize_act_wave((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, x, n_blocks, xq, xd, xs);
+}
+
+// Waves of quantize_act_wave that cover T rows of H (H a multiple of 256).
+int64_t quantize_act_waves(int T, int H) {
+    const int64_t n_blocks = (int64_t)T * (H / 256);
+    return (n_blocks + kQBlocksPerWave - 1) / kQBlocksPerWave;
+}
+
 hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* xd, hipStream_t s,
                                int16_t* xs) {
     const int64_t n_blocks = (int64_t)T * (H / 256);
-    const int64_t waves = (n_blocks + kQBlocksPerWave - 1) / kQBlocksPerWave;
+    const int64_t waves = quantize_act_waves(T, H);
     quantize_act_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(x, n_blocks, xq, xd, xs);
     return hipGetLastError();
 }

@@ -260,6 +260,51 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int& total) {
     return res;
 }
 
+// The MFMA GEMMs' tile list from the bucket counts: expert e's ceil(count/mt)
+// tiles in expert order, then the shared expert's tiles over all T tokens.
+// Every thread of the workgroup calls it (blockDim.x >= E); thread e < E passes
+// count[e], the others 0.  s_start holds E ints of LDS.  Each thread writes
+// list entries j = tid, tid + blockDim.x, ..., finding the expert of entry j
+// as the last e whose first entry is <= j (experts without tiles share the
+// next expert's first entry, so the last such e is the one with tiles).
+// Counts past npairs cannot come from a routing pass: they raise
+// kErrPairRange, and the list never grows past max_t.
+__device__ void write_tile_list(int c, int npairs, int E, const TileList& tl, int* s_wave, int* s_start) {
+    const int tid = threadIdx.x;
+    if (c < 0 || c > npairs) {
+        raise_error(kErrPairRange);
+        c = 0;
+    }
+    const int nt = (c + tl.mt - 1) / tl.mt;
+    int total = 0;
+    const int start = block_exclusive_scan(nt, s_wave, total);
+    if (tid < E) s_start[tid] = start;
+    __syncthreads();
+    const int ns = tl.has_shared ? (tl.T + tl.mt - 1) / tl.mt : 0;
+    const int n = min(total + ns, tl.max_t);
+    for (int j = tid; j < n; j += blockDim.x) {
+        int e = E, m0 = (j - total) * tl.mt;
+        if (j < total) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_start[mid] <= j)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            e = lo;
+            m0 = (j - s_start[lo]) * tl.mt;
+        }
+        tl.tile_e[j] = e;
+        tl.tile_m0[j] = m0;
+    }
+    if (tid == 0) {
+        if (total + ns > tl.max_t) raise_error(kErrPairRange);
+        *tl.n_tiles = n;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Small batches (T*k <= kSmallPairs): top-k and bucketing in one workgroup.
 // ---------------------------------------------------------------------------
@@ -318,12 +363,9 @@ __global__ void __launch_bounds__(1024) route_small_kernel(const float* __restri
 // Large batches: one wave per token, then a tiled stable counting sort.
 // ---------------------------------------------------------------------------
 template <int V>
-__global__ void __launch_bounds__(256) route_tokens_kernel(const float* __restrict__ logits, int T,
-                                                           int E, int k, int renorm, int32_t* idx,
-                                                           float* w) {
-    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+__device__ void route_token_wave(int t, const float* __restrict__ logits, int E, int k, int renorm, int32_t* idx,
+                                 float* w) {
     const int lane = threadIdx.x & (kWave - 1);
-    if (t >= T) return;
     int e;
     float wt;
     wave_topk<V>(logits + (int64_t)t * E, E, k, renorm != 0, e, wt);
@@ -331,6 +373,33 @@ __global__ void __launch_bounds__(256) route_tokens_kernel(const float* __restri
         idx[(int64_t)t * k + lane] = e;
         w[(int64_t)t * k + lane] = wt;
     }
+}
+
+template <int V>
+__global__ void __launch_bounds__(256) route_tokens_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k, int renorm, int32_t* idx,
+                                                           float* w) {
+    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (t >= T) return;
+    route_token_wave<V>(t, logits, E, k, renorm, idx, w);
+}
+
+// A layer call's prompt chunk: the per-token top-k and the activation
+// quantisation read and write disjoint arrays, so one launch carries both.
+// Workgroups below nr route four tokens each; the rest quantise x.
+template <int V>
+__global__ void __launch_bounds__(256) route_quant_kernel(const float* __restrict__ logits, int T, int E,
+                                                          int k, int renorm, int32_t* idx, float* w, int nr,
+                                                          const float* __restrict__ x, int64_t n_blocks,
+                                                          int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                          int16_t* __restrict__ xs) {
+    const int wave = threadIdx.x / kWave;
+    if ((int)blockIdx.x < nr) {
+        const int t = blockIdx.x * (blockDim.x / kWave) + wave;
+        if (t < T) route_token_wave<V>(t, logits, E, k, renorm, idx, w);
+        return;
+    }
+    quantize_act_wave((int64_t)(blockIdx.x - nr) * (blockDim.x / kWave) + wave, x, n_blocks, xq, xd, xs);
 }
 
 // Per tile of kTilePairs pairs: histogram over experts and each pair's rank
@@ -360,9 +429,9 @@ __global__ void __launch_bounds__(kTilePairs) bucket_tile_kernel(const int32_t* 
 // then writes its chunk's exclusive prefixes from the sum of the chunks
 // before it; a chunk's values stay in registers between the two passes when
 // it holds at most kB tiles (one round trip each way instead of one per 16
-// tiles).
+// tiles).  With tl.mt > 0 the totals also give the MFMA tile list.
 __global__ void __launch_bounds__(1024) bucket_scan_kernel(int n_tiles, int E, int P,
-                                                           int32_t* tile_hist, RoutingPtrs r) {
+                                                           int32_t* tile_hist, RoutingPtrs r, TileList tl) {
     __shared__ int s_wave[kWave + 1];
     __shared__ int s_part[1024];
     constexpr int kB = 32;
@@ -420,7 +489,7 @@ __global__ void __launch_bounds__(1024) bucket_scan_kernel(int n_tiles, int E, i
         r.offset[E] = total;
         *r.n_active = n_act;
     }
-    (void)P;
+    if (tl.mt > 0) write_tile_list(mine, P, E, tl, s_wave, s_part);   // s_part is free again
 }
 
 // pair[offset[e] + (pairs of e in earlier tiles) + rank of p in its tile] = p
@@ -437,9 +506,10 @@ __global__ void __launch_bounds__(256) bucket_scatter_kernel(const int32_t* __re
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, const RoutingPtrs& r,
-                        void* ws, hipStream_t s) {
+                        void* ws, hipStream_t s, RouteExtras* ex) {
     const int P = T * k;
     const int vpl = topk_vpl(E);
+    if (ex) ex->tiles_written = false;
     if (P <= kSmallPairs) {
         if (vpl == 4)
             route_small_kernel<4><<<1, 1024, 0, s>>>(logits, T, E, k, renorm, r);
@@ -447,21 +517,41 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, co
             route_small_kernel<8><<<1, 1024, 0, s>>>(logits, T, E, k, renorm, r);
         else
             route_small_kernel<16><<<1, 1024, 0, s>>>(logits, T, E, k, renorm, r);
-        return hipGetLastError();
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !ex) return e;
+        return launch_quantize_act(ex->x, T, ex->H, ex->xq, ex->xd, s, ex->xs);
     }
     const int n_tiles = (P + kTilePairs - 1) / kTilePairs;
     int32_t* tile_hist = (int32_t*)ws;
     int32_t* rank = tile_hist + (size_t)n_tiles * E;
-    if (vpl == 4)
-        route_tokens_kernel<4><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
-    else if (vpl == 8)
-        route_tokens_kernel<8><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
-    else
-        route_tokens_kernel<16><<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
+    const int nr = (T + 3) / 4;
+    if (ex) {
+        const int64_t n_blocks = (int64_t)T * (ex->H / 256);
+        const unsigned grid = (unsigned)(nr + (quantize_act_waves(T, ex->H) + 3) / 4);
+        if (vpl == 4)
+            route_quant_kernel<4><<<grid, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w, nr, ex->x, n_blocks,
+                                                       ex->xq, ex->xd, ex->xs);
+        else if (vpl == 8)
+            route_quant_kernel<8><<<grid, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w, nr, ex->x, n_blocks,
+                                                       ex->xq, ex->xd, ex->xs);
+        else
+            route_quant_kernel<16><<<grid, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w, nr, ex->x, n_blocks,
+                                                        ex->xq, ex->xd, ex->xs);
+    } else if (vpl == 4) {
+        route_tokens_kernel<4><<<nr, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
+    } else if (vpl == 8) {
+        route_tokens_kernel<8><<<nr, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
+    } else {
+        route_tokens_kernel<16><<<nr, 256, 0, s>>>(logits, T, E, k, renorm, r.idx, r.w);
+    }
     bucket_tile_kernel<<<n_tiles, kTilePairs, 0, s>>>(r.idx, P, E, tile_hist, rank);
-    bucket_scan_kernel<<<1, 1024, 0, s>>>(n_tiles, E, P, tile_hist, r);
+    TileList tl{};
+    if (ex && ex->tiles.mt > 0) tl = ex->tiles;
+    bucket_scan_kernel<<<1, 1024, 0, s>>>(n_tiles, E, P, tile_hist, r, tl);
     bucket_scatter_kernel<<<(P + 255) / 256, 256, 0, s>>>(r.idx, P, E, tile_hist, r.offset, rank, r.pair);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && ex) ex->tiles_written = tl.mt > 0;
+    return e;
 }
 
 size_t route_workspace_bytes(int T, int E, int k) {
