@@ -13,8 +13,11 @@ and for the expert FFN call alone as gemm_tops) and the CPU oracle timed and
 checked on one whole layer; the Sage-like decode layer (1 token, 40 layers) and
 the Flash-Next-like decode layer (1 token, 10 routed + 1 shared, 48 layers) are
 sub-records decode_c1 and decode_c3, each with its own HBM roofline, CPU oracle
-baseline (all host threads and one thread) and parity.  --config runs one
-workload alone.
+baseline (all host threads and one thread) and parity.  The sub-record
+prefill_chunk_pair_bf16 is the prompt chunk again with MOE_FFN_PAIR_BF16 (the
+per-pair outputs handed to the combine as bf16 in the workspace), checked
+against the oracle on one whole layer.  --config runs one workload alone
+(--pair-bf16 sets the flag).
 
 Prints ONE JSON line on stdout.  Progress goes to stderr.
 """
@@ -72,6 +75,12 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def pair_bf16(w, flags, qm):
+    """Workload w run with MOE_FFN_PAIR_BF16 (its records and traffic kept under its own name)."""
+    from quantized_moe_ffn_amd.profiling import PAIR_BF16_SUFFIX
+    return dataclasses.replace(w, name=w.name + PAIR_BF16_SUFFIX), flags | qm.MOE_FFN_PAIR_BF16
 
 
 def resolve_workload(args, synth, qm, name):
@@ -225,7 +234,8 @@ def run_workload(args, w, flags, torch, qm, dev, full_layer_oracle=False, single
                 "kernel": ("moe_forward_router (router kernel, then " if routers is not None else "moe_forward (") +
                           "int8 path: route, quantize, gate/up, requantize, down, combine)",
                 "ops_per_launch": ops, "avg_launch_us": round(avg_us, 3)}
-        if routers is None:
+        if routers is None and not flags & qm.MOE_FFN_PAIR_BF16:
+            # (the separate FFN call has no bf16 hand-off: it times the unflagged GEMMs)
             roof.update(gemm_time(w, stack, inputs, bufs, flags, k, ops, args.steps, L, R, torch, qm))
     else:
         achieved = dom_bytes / (ms_total / 1e3) / 1e9
@@ -262,6 +272,8 @@ def run_workload(args, w, flags, torch, qm, dev, full_layer_oracle=False, single
                    "shared_expert": w.shared, "layers": L, "replays": R,
                    "formats": {"gate": fmt(w.qt_gate), "up": fmt(w.qt_up), "down": fmt(w.qt_down)},
                    "parallelism": "single GPU", "graphs": args.graph,
+                   "pair_outputs": ("workspace, bf16 on the MFMA GEMMs (MOE_FFN_PAIR_BF16)"
+                                    if flags & qm.MOE_FFN_PAIR_BF16 else "fp32 y_pair"),
                    "router": "fp32 [E][H], moe_forward_router in the timed step" if routers is not None else None},
         "hbm_GBps_end_to_end": round(dom_bytes / (ms_total / 1e3) / 1e9, 1),
         "layer_call_us_p10_p50_p90": [pct[10], pct[50], pct[90]],
@@ -292,7 +304,8 @@ def gemm_time(w, stack, inputs, bufs, flags, k, ops, steps, L, R, torch, qm) -> 
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             qm.moe_expert_ffn_q(stack[l].layer, bufs.routing, w.tokens, k, bufs.y_pair, xq=bufs.xq, xd=bufs.xd,
-                                flags=flags, y_shared=bufs.y_shared, workspace=bufs.ffn_ws, stream=stream)
+                                flags=flags & ~qm.MOE_FFN_PAIR_BF16, y_shared=bufs.y_shared,
+                                workspace=bufs.ffn_ws, stream=stream)
             e1.record(stream)
             times.append((e0, e1))
     torch.cuda.synchronize()
@@ -329,6 +342,9 @@ def main() -> int:
     ap.add_argument("--top-k", type=int, default=None, help="override the routed experts per token")
     ap.add_argument("--path", choices=["auto", "decode", "int8"], default=None,
                     help="FFN path (default: the workload's own; auto takes the decode path up to 8 tokens)")
+    ap.add_argument("--pair-bf16", action="store_true",
+                    help="layer calls with MOE_FFN_PAIR_BF16: the per-pair outputs reach the combine through "
+                         "the workspace, as bf16 on the int8 MFMA GEMMs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -337,8 +353,10 @@ def main() -> int:
               % args.gpus, file=sys.stderr)
         return 2
     if args.config is None and (args.tokens is not None or args.experts is not None or args.top_k is not None
-                                or args.path is not None or args.layers is not None or args.router):
-        print("--tokens, --experts, --top-k, --path, --layers and --router need --config", file=sys.stderr)
+                                or args.path is not None or args.layers is not None or args.router
+                                or args.pair_bf16):
+        print("--tokens, --experts, --top-k, --path, --layers, --router and --pair-bf16 need --config",
+              file=sys.stderr)
         return 2
 
     import torch
@@ -357,6 +375,8 @@ def main() -> int:
         print(err, file=sys.stderr)
         return 2
     w, flags = wf
+    if args.pair_bf16:
+        w, flags = pair_bf16(w, flags, qm)
     full = args.config is None
     rec_main = run_workload(args, w, flags, torch, qm, dev, full_layer_oracle=full and w.int8_path,
                             single_thread=not w.int8_path)
@@ -382,6 +402,9 @@ def main() -> int:
             (ws, fs), _ = resolve_workload(args, synth, qm, name)
             sub = run_workload(args, ws, fs, torch, qm, dev, single_thread=True)
             rec[key] = sub
+        # the same prompt chunk with the per-pair outputs handed to the combine as bf16
+        wb, fb = pair_bf16(w, flags, qm)
+        rec["prefill_chunk_pair_bf16"] = run_workload(args, wb, fb, torch, qm, dev, full_layer_oracle=True)
         if not args.no_cpu_baseline:
             rec["cpu_single_thread_tiny"] = cpu_tiny_single_thread(torch, qm, dev)
     print(json.dumps(rec), flush=True)
@@ -501,11 +524,18 @@ def cpu_full_layer(w, stack, inputs, bufs, flags, k):
     import quantized_moe_ffn_amd as qm
     dl = stack[0]
     lg_t, x_t = inputs[0][0]
+    if flags & qm.MOE_FFN_PAIR_BF16:
+        # the flagged call returns no y_pair: the pairs are checked from the same call without
+        # the flag (its fp32 y is what the bf16 hand-off rounds), out from the flagged call
+        qm.forward(dl.layer, lg_t, x_t, k, bufs, flags=flags & ~qm.MOE_FFN_PAIR_BF16)
+        torch.cuda.synchronize()
+        gpu_y = bufs.y_pair.cpu().numpy()
     qm.forward(dl.layer, lg_t, x_t, k, bufs, flags=flags)
     torch.cuda.synchronize()
     qm.moe_check_device_errors()
     gpu_out = bufs.out.cpu().numpy()
-    gpu_y = bufs.y_pair.cpu().numpy()
+    if not flags & qm.MOE_FFN_PAIR_BF16:
+        gpu_y = bufs.y_pair.cpu().numpy()
     idx_gpu = bufs.routing.idx.cpu().numpy()
     lg = lg_t.cpu().numpy()
     x = x_t.cpu().numpy()

@@ -87,8 +87,19 @@ enum { MOE_ROUTE_RENORM = 1u }; /* weights = softmax over the k selected logits 
 enum {
     MOE_FFN_AUTO = 0u,   /* decode path up to 8 tokens, int8 path above               */
     MOE_FFN_DECODE = 1u, /* fp32 activations, weights dequantized in registers        */
-    MOE_FFN_INT8 = 2u    /* int8 activations (moe_quantize_act); grouped int8 MFMA GEMMs
+    MOE_FFN_INT8 = 2u,   /* int8 activations (moe_quantize_act); grouped int8 MFMA GEMMs
                             when gate, up and down are Q4_K or Q5_K */
+    /* The layer calls only (moe_forward and its variants), OR-ed with one of the
+     * above: y_pair is not returned (it may be NULL) and the per-pair outputs
+     * reach the combine through the workspace.  On the int8 MFMA GEMMs they are
+     * kept as bf16 (rounded to nearest even), which halves their write and read
+     * (T*k*H*2 bytes each way instead of *4).  The combine then sums the bf16
+     * values widened to fp32, so out moves by at most 2^-8 * sum_j |w_j*y_j| per
+     * element (bf16's unit roundoff), inside the int8 path's 5e-3 tolerance
+     * ("Strata - the details", "How it works": the per-expert outputs and the
+     * weighted sum stay on the GPU).  The other paths keep the per-pair outputs
+     * in fp32 and give the same out as without the flag. */
+    MOE_FFN_PAIR_BF16 = 16u
 };
 
 /* One projection of an expert bank: n_experts matrices of rows x cols weights,
@@ -235,7 +246,8 @@ moe_status moe_combine_ep(const float* y_pair, const float* w, const float* y_sh
 moe_status moe_shared_gate(const float* x, int32_t T, int32_t H, const float* gate_w, float* s,
                            hipStream_t stream);
 
-/* Bytes of device workspace moe_forward needs (for the path ffn_flags selects). */
+/* Bytes of device workspace moe_forward needs (for the path ffn_flags selects,
+ * with room for the per-pair outputs when it carries MOE_FFN_PAIR_BF16). */
 size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t ffn_flags);
 
 /* The whole layer: routing (as moe_route_topk, results written to r), expert
@@ -248,7 +260,8 @@ size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uin
  * top-k of its token) and the combine fused into the down kernel (formed in
  * slot order in LDS); other shapes run the separate stages.  Same results
  * contract as the three calls (bitwise
- * deterministic; combine in slot order).  y_pair [T*k][H] is always written;
+ * deterministic; combine in slot order).  y_pair [T*k][H] is written unless
+ * ffn_flags carries MOE_FFN_PAIR_BF16 (then it may be NULL and is not touched);
  * y_shared [T][H] is required iff the layer has a shared expert;
  * shared_scale [T] or NULL (non-NULL needs a shared expert).  x must be
  * 16-byte aligned.  Checks: those of

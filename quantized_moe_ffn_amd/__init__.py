@@ -31,6 +31,7 @@ MOE_FFN_AUTO = 0
 AUTO_DECODE_MAX_T = 8   # MOE_FFN_AUTO takes the fp-activation path up to this many tokens
 MOE_FFN_DECODE = 1
 MOE_FFN_INT8 = 2
+MOE_FFN_PAIR_BF16 = 16  # layer calls: per-pair outputs stay in the workspace (bf16 on the MFMA GEMMs)
 
 BLOCK_WEIGHTS = {MOE_Q4_K: 256, MOE_Q5_K: 256, MOE_Q8_0: 32, MOE_Q5_1: 32}
 BLOCK_BYTES = {MOE_Q4_K: 144, MOE_Q5_K: 176, MOE_Q8_0: 34, MOE_Q5_1: 24}
@@ -349,7 +350,7 @@ class LayerBuffers:
         self.routing = Routing(T, E, k, device)
         rw = moe_route_workspace_bytes(T, E, k)
         self.route_ws = torch.empty(max(rw, 1), dtype=torch.uint8, device=device)
-        fw = moe_ffn_workspace_bytes(layer, T, k, flags)
+        fw = moe_ffn_workspace_bytes(layer, T, k, flags & ~MOE_FFN_PAIR_BF16)
         self.ffn_ws = torch.empty(max(fw, 256), dtype=torch.uint8, device=device)
         self.y_pair = torch.empty((T * k, H), dtype=torch.float32, device=device)
         self.y_shared = torch.empty((T, H), dtype=torch.float32, device=device) if layer.shared else None
@@ -380,7 +381,8 @@ def forward(layer: Layer, logits, x, k: int, bufs: LayerBuffers | None = None, f
             moe_forward(layer, logits, x, k, bufs.routing, bufs.y_pair, bufs.out, bufs.y_shared, shared_scale,
                         renorm, flags, bufs.fwd_ws, stream)
         return bufs
-    path = flags if flags != MOE_FFN_AUTO else (MOE_FFN_DECODE if T <= AUTO_DECODE_MAX_T else MOE_FFN_INT8)
+    sel = flags & ~MOE_FFN_PAIR_BF16   # the separate stages hand fp32 y_pair to the combine
+    path = sel if sel != MOE_FFN_AUTO else (MOE_FFN_DECODE if T <= AUTO_DECODE_MAX_T else MOE_FFN_INT8)
     moe_route_topk(logits, k, bufs.routing, renorm, bufs.route_ws, stream)
     if path == MOE_FFN_INT8:
         moe_quantize_act(x, bufs.xq, bufs.xd, stream)

@@ -348,9 +348,20 @@ hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Combine and the dequantization test hook.
 // ---------------------------------------------------------------------------
+// The per-pair rows as the combine reads them: fp32, or bf16 (the layer
+// call's MOE_FFN_PAIR_BF16 hand-off, four values per uint2), widened exactly.
+__device__ __forceinline__ float pair_value(float v) { return v; }
+__device__ __forceinline__ float pair_value(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ float4 pair_values(float4 v) { return v; }
+__device__ __forceinline__ float4 pair_values(uint2 b) {
+    return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u), __uint_as_float(b.y << 16),
+                       __uint_as_float(b.y & 0xFFFF0000u));
+}
+
 // out may be the residual array itself (each element is read, then written, by
 // one thread), so neither carries __restrict__.
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y_pair,
+template <typename YE>
+__global__ void __launch_bounds__(256) combine_kernel(const YE* __restrict__ y_pair,
                                                       const float* __restrict__ w,
                                                       const float* __restrict__ y_shared,
                                                       const float* __restrict__ shared_scale,
@@ -360,7 +371,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     if (idx >= (int64_t)T * H) return;
     const int t = (int)(idx / H), o = (int)(idx - (int64_t)t * H);
     float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], y_pair[((int64_t)t * k + j) * H + o], acc);
+    for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], pair_value(y_pair[((int64_t)t * k + j) * H + o]), acc);
     if (y_shared) {
         const float sc = (shared_scale ? shared_scale[t] : 1.0f) * (sgate ? sgate[t] : 1.0f);
         acc = fmaf(sc, y_shared[(int64_t)t * H + o], acc);
@@ -373,7 +384,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 // per-element summation order as combine_kernel, so the same bits). The pair
 // rows of a token are loaded kRows at a time before any of them is summed, so a
 // thread waits on one memory round trip per kRows rows, not one per row.
-__global__ void __launch_bounds__(256) combine4_kernel(const float4* __restrict__ y_pair,
+template <typename YE4>
+__global__ void __launch_bounds__(256) combine4_kernel(const YE4* __restrict__ y_pair,
                                                        const float* __restrict__ w,
                                                        const float4* __restrict__ y_shared,
                                                        const float* __restrict__ shared_scale,
@@ -383,7 +395,7 @@ __global__ void __launch_bounds__(256) combine4_kernel(const float4* __restrict_
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)T * H4) return;
     const int t = (int)(idx / H4), o = (int)(idx - (int64_t)t * H4);
-    const float4* yp = y_pair + (int64_t)t * k * H4 + o;
+    const YE4* yp = y_pair + (int64_t)t * k * H4 + o;
     const float* wt = w + (int64_t)t * k;
     float4 ys = make_float4(0.f, 0.f, 0.f, 0.f), rs = ys;
     float ss = 1.0f, sg = 1.0f;
@@ -400,7 +412,7 @@ __global__ void __launch_bounds__(256) combine4_kernel(const float4* __restrict_
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
             if (j0 + i < k) {
-                y[i] = yp[(int64_t)(j0 + i) * H4];
+                y[i] = pair_values(yp[(int64_t)(j0 + i) * H4]);
                 wj[i] = wt[j0 + i];
             }
         }
@@ -430,21 +442,36 @@ __global__ void __launch_bounds__(256) combine4_kernel(const float4* __restrict_
     out[idx] = acc;
 }
 
-hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
-                          const float* sgate, const float* residual, int T, int k, int H, float* out,
-                          hipStream_t s) {
-    const auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
-    if (H % 4 == 0 && a16(y_pair) && a16(out) && (!y_shared || a16(y_shared)) && (!residual || a16(residual))) {
+// YE: the element type of y_pair (float or uint16_t bf16); YE4 four of them.
+template <typename YE, typename YE4>
+hipError_t launch_combine_rows(const YE* y_pair, const float* w, const float* y_shared, const float* shared_scale,
+                               const float* sgate, const float* residual, int T, int k, int H, float* out,
+                               hipStream_t s) {
+    const auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+    if (H % 4 == 0 && al(y_pair, sizeof(YE4)) && al(out, 16) && (!y_shared || al(y_shared, 16)) &&
+        (!residual || al(residual, 16))) {
         const int64_t n = (int64_t)T * (H / 4);
-        combine4_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-            reinterpret_cast<const float4*>(y_pair), w, reinterpret_cast<const float4*>(y_shared), shared_scale,
-            sgate, reinterpret_cast<const float4*>(residual), T, k, H / 4, reinterpret_cast<float4*>(out));
+        combine4_kernel<YE4><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+            reinterpret_cast<const YE4*>(y_pair), w, reinterpret_cast<const float4*>(y_shared), shared_scale, sgate,
+            reinterpret_cast<const float4*>(residual), T, k, H / 4, reinterpret_cast<float4*>(out));
         return hipGetLastError();
     }
     const int64_t n = (int64_t)T * H;
-    combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(y_pair, w, y_shared, shared_scale, sgate, residual,
-                                                               T, k, H, out);
+    combine_kernel<YE><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(y_pair, w, y_shared, shared_scale, sgate, residual,
+                                                                   T, k, H, out);
     return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
+                          const float* sgate, const float* residual, int T, int k, int H, float* out,
+                          hipStream_t s) {
+    return launch_combine_rows<float, float4>(y_pair, w, y_shared, shared_scale, sgate, residual, T, k, H, out, s);
+}
+
+hipError_t launch_combine_bf16(const uint16_t* y_pair, const float* w, const float* y_shared,
+                               const float* shared_scale, const float* sgate, const float* residual, int T, int k,
+                               int H, float* out, hipStream_t s) {
+    return launch_combine_rows<uint16_t, uint2>(y_pair, w, y_shared, shared_scale, sgate, residual, T, k, H, out, s);
 }
 
 // One wave per token: s[t] = sigmoid(g . x_t) (shared_gate_wave).

@@ -62,8 +62,10 @@ hipError_t launch_ffn_int8(const FfnArgs& a, hipStream_t s) {
         m.tile_m0 = tl.tile_m0;
         m.n_tiles = tl.n_tiles;
         m.tiles_ready = a.tiles_ready;
+        m.y_pair_bf16 = a.y_pair_bf16;
         return launch_ffn_mfma(m, s);
     }
+    if (a.y_pair_bf16) return hipErrorInvalidValue;   // bf16 pair outputs come from the MFMA GEMMs only
     hipError_t e = launch_gateup(a, 1, s);
     if (e != hipSuccess) return e;
     const int rows = a.T * a.k + (a.has_shared ? a.T : 0);

@@ -526,7 +526,8 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
 
 constexpr int kDownRoundsMax = 4;  // 256-row rounds per down workgroup (large batches)
 
-template <int MTILES, int QD>
+// PAIR16: the per-pair outputs go to y_pair_bf16 as bf16 (nearest even), not to y_pair.
+template <int MTILES, int QD, bool PAIR16>
 __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -582,9 +583,13 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
                 for (int v = 0; v < 16; ++v) {
                     const int orow = s_out[c_row(mt, v, h)];
                     if (orow >= 0) {
-                        if (orow < npairs)
-                            a.y_pair[(uint32_t)(orow * H + o)] = acc[mt][v];
-                        else
+                        if (orow < npairs) {
+                            if constexpr (PAIR16)
+                                a.y_pair_bf16[(uint32_t)(orow * H + o)] =
+                                    __builtin_bit_cast(uint16_t, (__bf16)acc[mt][v]);
+                            else
+                                a.y_pair[(uint32_t)(orow * H + o)] = acc[mt][v];
+                        } else
                             a.y_shared[(uint32_t)((orow - npairs) * H + o)] = acc[mt][v];
                     }
                     acc[mt][v] = 0.0f;
@@ -666,7 +671,11 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     MfmaArgs d = a;
     d.down_rounds = (int64_t)maxt * ((a.H / 256 + kDownRoundsMax - 1) / kDownRoundsMax) >= 1024 ? kDownRoundsMax : 1;
     const int nb_down = (a.H / 256 + d.down_rounds - 1) / d.down_rounds;
-    down_mfma_kernel<MTILES, QD><<<grid_for(maxt * nb_down), kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(d);
+    const dim3 gd(grid_for(maxt * nb_down));
+    if (a.y_pair_bf16)
+        down_mfma_kernel<MTILES, QD, true><<<gd, kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(d);
+    else
+        down_mfma_kernel<MTILES, QD, false><<<gd, kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(d);
     return hipGetLastError();
 }
 

@@ -52,6 +52,8 @@ struct FfnArgs {
     int32_t* tiles;                // workspace: MFMA tile list (mfma_tiles_bytes)
     int xs_ready;                  // xs already holds the per-32 sums of xq
     int tiles_ready;               // the tile list in tiles is already written (by the routing launches)
+    uint16_t* y_pair_bf16;         // non-null: the MFMA GEMMs write the per-pair outputs here as bf16
+                                   // [T*k][H] instead of y_pair
 };
 
 // The MFMA GEMMs' work list: tile i of expert e covers rows mt*i .. mt*i + mt - 1
@@ -89,6 +91,7 @@ struct MfmaArgs {
     int down_rounds;               // 256-row rounds per down workgroup (set by the launcher)
     int xs_ready;                  // xs already holds the per-32 sums of xq (written with the codes)
     int tiles_ready;               // tile_e / tile_m0 / n_tiles already hold the tile list
+    uint16_t* y_pair_bf16;         // non-null: y_pair is written here as bf16 (nearest even) instead
 };
 
 bool mfma_path_supported(int H, int I, int qg, int qu, int qd);
@@ -156,6 +159,10 @@ hipError_t launch_quantize_act(const float* x, int T, int H, int8_t* xq, float* 
 hipError_t launch_combine(const float* y_pair, const float* w, const float* y_shared, const float* shared_scale,
                           const float* sgate, const float* residual, int T, int k, int H, float* out,
                           hipStream_t s);
+// The same with the per-pair rows in bf16 (8-byte aligned), widened exactly to fp32.
+hipError_t launch_combine_bf16(const uint16_t* y_pair, const float* w, const float* y_shared,
+                               const float* shared_scale, const float* sgate, const float* residual, int T, int k,
+                               int H, float* out, hipStream_t s);
 // s[t] = 1 / (1 + exp(-(g . x_t))), one wave per token
 hipError_t launch_shared_gate(const float* x, int T, int H, const float* g, float* s, hipStream_t st);
 hipError_t launch_dequant(const void* blocks, int qtype, int64_t n_weights, float* out, hipStream_t s);

@@ -204,10 +204,18 @@ void set_ffn_ws(moe::FfnArgs& a, char* base, const FfnWorkspace& w) {
 }
 
 struct ForwardWorkspace {
-    size_t route, ffn, xq, xd, tab, sg, total;
+    size_t route, ffn, xq, xd, tab, sg, yp, total;
+    bool yp_bf16;   // yp holds bf16 per-pair outputs (else fp32); used with MOE_FFN_PAIR_BF16
 };
 
-ForwardWorkspace forward_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
+// ffn_flags of the layer calls: a path selector, optionally with MOE_FFN_PAIR_BF16.
+bool split_ffn_flags(uint32_t flags, uint32_t& sel, bool& pair_ws) {
+    pair_ws = (flags & MOE_FFN_PAIR_BF16) != 0;
+    sel = flags & ~(uint32_t)MOE_FFN_PAIR_BF16;
+    return sel == MOE_FFN_AUTO || sel == MOE_FFN_DECODE || sel == MOE_FFN_INT8;
+}
+
+ForwardWorkspace forward_ws_layout(const moe_layer* L, int T, int k, uint32_t path, bool pair_ws) {
     ForwardWorkspace w{};
     size_t off = 0;
     w.route = off;
@@ -222,6 +230,9 @@ ForwardWorkspace forward_ws_layout(const moe_layer* L, int T, int k, uint32_t pa
     off += moe::kDecRouteTabBytes;
     w.sg = off;   // shared-expert gate values of the separate stages
     off += align_up((size_t)T * sizeof(float), 256);
+    w.yp = off;   // the per-pair outputs when the caller does not take them
+    w.yp_bf16 = ffn_ws_layout(L, T, k, path).mfma;
+    if (pair_ws) off += align_up((size_t)T * k * L->hidden * (w.yp_bf16 ? 2 : 4), 256);
     w.total = off;
     return w;
 }
@@ -315,19 +326,25 @@ moe_status forward_impl(const moe_layer* L, const float* logits, const float* x,
         return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: shared_gate must be 16-byte aligned, residual 4-byte aligned");
     if (residual && (residual == y_pair || residual == y_shared))
         return fail(MOE_ERR_INVALID_ARGUMENT, "epilogue: residual must not alias y_pair or y_shared");
-    if (!logits || !x || !out || !y_pair) return fail(MOE_ERR_INVALID_ARGUMENT, "logits, x, y_pair or out is NULL");
+    uint32_t sel = 0;
+    bool pair_ws = false;
+    if (!split_ffn_flags(ffn_flags, sel, pair_ws))
+        return fail(MOE_ERR_INVALID_ARGUMENT,
+                    "ffn_flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8, optionally with "
+                    "MOE_FFN_PAIR_BF16",
+                    ffn_flags);
+    if (!logits || !x || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "logits, x or out is NULL");
+    if (!y_pair && !pair_ws) return fail(MOE_ERR_INVALID_ARGUMENT, "y_pair is NULL (allowed with MOE_FFN_PAIR_BF16)");
+    if (pair_ws) y_pair = nullptr;   // not touched
     if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(out, 4) || !aligned(y_pair, 4) ||
         (y_shared && !aligned(y_shared, 4)) || (shared_scale && !aligned(shared_scale, 4)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned, the other fp32 arrays 4-byte aligned");
     if (route_flags & ~(uint32_t)MOE_ROUTE_RENORM)
         return fail(MOE_ERR_INVALID_ARGUMENT, "route_flags = 0x%x: only MOE_ROUTE_RENORM is defined", route_flags);
-    if (ffn_flags != MOE_FFN_AUTO && ffn_flags != MOE_FFN_DECODE && ffn_flags != MOE_FFN_INT8)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "ffn_flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8",
-                    ffn_flags);
     if (!r || !r->idx || !r->w || !r->count || !r->offset || !r->pair || !r->active || !r->n_active)
         return fail(MOE_ERR_INVALID_ARGUMENT, "moe_routing or one of its arrays is NULL");
-    const uint32_t path = resolve_path(ffn_flags, T);
-    const ForwardWorkspace wl = forward_ws_layout(L, T, k, path);
+    const uint32_t path = resolve_path(sel, T);
+    const ForwardWorkspace wl = forward_ws_layout(L, T, k, path, pair_ws);
     if (!workspace || ws_bytes < wl.total)
         return fail(MOE_ERR_WORKSPACE, "forward workspace: %zu bytes given, %zu needed", ws_bytes, wl.total);
     if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
@@ -382,7 +399,18 @@ moe_status forward_impl(const moe_layer* L, const float* logits, const float* x,
     a.xq = (int8_t*)(ws + wl.xq);
     a.xd = (float*)(ws + wl.xd);
     set_ffn_ws(a, ws + wl.ffn, ffn_ws_layout(L, T, k, path));
-    a.y_pair = y_pair;
+    // the per-pair outputs: the caller's y_pair, or with MOE_FFN_PAIR_BF16 the
+    // workspace (bf16 on the MFMA GEMMs, fp32 on the other stages)
+    float* yp32 = y_pair;
+    uint16_t* yp16 = nullptr;
+    if (pair_ws) {
+        if (wl.yp_bf16)
+            yp16 = (uint16_t*)(ws + wl.yp);
+        else
+            yp32 = (float*)(ws + wl.yp);
+    }
+    a.y_pair = yp32;
+    a.y_pair_bf16 = yp16;
     a.y_shared = y_shared;
     hipError_t e;
     if (path == MOE_FFN_INT8) {
@@ -412,10 +440,10 @@ moe_status forward_impl(const moe_layer* L, const float* logits, const float* x,
         e = moe::launch_shared_gate(x, T, L->hidden, sgate_w, sg, stream);
         if (e != hipSuccess) return from_hip(e, "moe_forward: shared-expert gate launch");
     }
-    return finish(from_hip(moe::launch_combine(y_pair, r->w, L->has_shared ? y_shared : nullptr, shared_scale, sg,
-                                               residual, T, k, L->hidden, out, stream),
-                           "moe_forward: combine launch"),
-                  stream, "moe_forward");
+    const float* ysh = L->has_shared ? y_shared : nullptr;
+    e = yp16 ? moe::launch_combine_bf16(yp16, r->w, ysh, shared_scale, sg, residual, T, k, L->hidden, out, stream)
+             : moe::launch_combine(yp32, r->w, ysh, shared_scale, sg, residual, T, k, L->hidden, out, stream);
+    return finish(from_hip(e, "moe_forward: combine launch"), stream, "moe_forward");
 }
 
 }  // namespace
@@ -531,8 +559,10 @@ moe_status moe_expert_ffn_q(const moe_layer* L, const moe_routing* r, int32_t T,
 }
 
 size_t moe_forward_workspace_bytes(const moe_layer* L, int32_t T, int32_t k, uint32_t ffn_flags) {
-    if (!L || T < 1 || k < 1) return 0;
-    return forward_ws_layout(L, T, k, resolve_path(ffn_flags, T)).total;
+    uint32_t sel = 0;
+    bool pair_ws = false;
+    if (!L || T < 1 || k < 1 || !split_ffn_flags(ffn_flags, sel, pair_ws)) return 0;
+    return forward_ws_layout(L, T, k, resolve_path(sel, T), pair_ws).total;
 }
 
 moe_status moe_forward(const moe_layer* L, const float* logits, const float* x, int32_t T, int32_t k,
@@ -640,10 +670,14 @@ moe_status moe_forward_noalloc(const moe_layer* L, const float* logits, const fl
                                float* y_shared, const float* shared_scale, float* out, hipStream_t stream) {
     moe_status st = validate_layer(L, T, k, y_shared);
     if (st != MOE_OK) return st;
-    if (ffn_flags != MOE_FFN_AUTO && ffn_flags != MOE_FFN_DECODE && ffn_flags != MOE_FFN_INT8)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "ffn_flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8",
+    uint32_t sel = 0;
+    bool pair_ws = false;
+    if (!split_ffn_flags(ffn_flags, sel, pair_ws))
+        return fail(MOE_ERR_INVALID_ARGUMENT,
+                    "ffn_flags = 0x%x: use MOE_FFN_AUTO, MOE_FFN_DECODE or MOE_FFN_INT8, optionally with "
+                    "MOE_FFN_PAIR_BF16",
                     ffn_flags);
-    const size_t need = forward_ws_layout(L, T, k, resolve_path(ffn_flags, T)).total;
+    const size_t need = forward_ws_layout(L, T, k, resolve_path(sel, T), pair_ws).total;
     if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
         return fail(MOE_ERR_WORKSPACE,
                     "moe_forward_noalloc: T = %d, k = %d needs %zu bytes of workspace; its static scratch holds %zu "

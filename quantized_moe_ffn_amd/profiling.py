@@ -35,11 +35,17 @@ _DECODE = _COMMON + ("qblock.h", "decode_fused.hip")
 _INT8 = _COMMON + ("quant.hip", "ffn_mfma.hip", "ffn_int8.hip", "ffn_decode.hip")
 
 
+# A workload run with MOE_FFN_PAIR_BF16 is recorded under its name with this suffix.
+PAIR_BF16_SUFFIX = "+pair_bf16"
+
+
 def kernel_files(workload: str | None = None):
     """The library sources a workload's kernels are built from (all sources when None)."""
     if workload is None:
         return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
     from quantized_moe_ffn_amd import synth
+    if workload.endswith(PAIR_BF16_SUFFIX):
+        workload = workload[:-len(PAIR_BF16_SUFFIX)]
     return sorted(_INT8 if synth.WORKLOADS[workload].int8_path else _DECODE)
 
 

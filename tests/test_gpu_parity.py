@@ -379,6 +379,84 @@ def test_int8_determinism_and_batch_invariance():
     assert np.array_equal(c, a[rows])
 
 
+# --------------------------------------------------------------------------- MOE_FFN_PAIR_BF16
+
+def _bf16_rne(a):
+    """fp32 -> bf16 rounded to nearest, ties to even, widened back to fp32 (finite values)."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _pair_bf16_pair(m, dl, logits, x, k, flags):
+    """The layer call with and without MOE_FFN_PAIR_BF16 on the same inputs.  The flagged
+    call gets a y_pair buffer full of a sentinel, which it must leave alone."""
+    ref = _run_layer(m, dl, logits, x, k, flags)
+    lg = torch.from_numpy(np.ascontiguousarray(logits)).to(DEV)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    bufs = m.LayerBuffers(dl.layer, x.shape[0], k, flags | m.MOE_FFN_PAIR_BF16, device=DEV)
+    bufs.y_pair.fill_(7.0)
+    m.forward(dl.layer, lg, xt, k, bufs=bufs, flags=flags | m.MOE_FFN_PAIR_BF16)
+    m.moe_check_device_errors()
+    assert bool((bufs.y_pair == 7.0).all())
+    assert torch.equal(bufs.routing.idx, ref.routing.idx) and torch.equal(bufs.routing.pair, ref.routing.pair)
+    if ref.y_shared is not None:
+        assert torch.equal(bufs.y_shared, ref.y_shared)
+    return ref, bufs
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", dict(hidden=768, inter=512, n_experts=40, top_k=4, tokens=130, shared=True)),
+    ("tiny", dict(hidden=2560, inter=512, n_experts=16, top_k=2, tokens=40, qt_gate=oracle.Q5_K,
+                  qt_up=oracle.Q5_K, qt_down=oracle.Q5_K)),
+    ("prefill_chunk", {}),
+])
+def test_pair_bf16_int8_mfma_is_the_combine_of_rounded_pairs(name, over):
+    """On the int8 MFMA GEMMs the flagged layer call's out equals, bit for bit, the fp32
+    combine (moe_combine) of the same call's fp32 per-pair outputs rounded to bf16 (nearest
+    even) on the host; and out stays within the int8 path's tolerance of the oracle (checked
+    with the unflagged call's y_pair, which the existing tests hold to the oracle)."""
+    import types
+    m = qm()
+    _say("pair bf16, int8 MFMA", name, over)
+    dl, w = _layer(name, **over)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=11)
+    ref, bufs = _pair_bf16_pair(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8)
+    yb = torch.from_numpy(_bf16_rne(ref.y_pair.cpu().numpy())).to(DEV)
+    out_ref = torch.empty_like(ref.out)
+    m.moe_combine(yb, ref.routing.w, out_ref, ref.y_shared)
+    m.moe_check_device_errors()
+    assert torch.equal(bufs.out, out_ref)
+    # the rounding moves out by at most 2^-8 sum_j |w_j y_j| per element, plus the fp32
+    # roundings of the two k + 1 step fmaf chains
+    T, k, H = x.shape[0], w.top_k, w.hidden
+    wy = (ref.routing.w.double().reshape(T, k, 1) * ref.y_pair.double().reshape(T, k, H)).abs().sum(1)
+    mag = wy + (ref.y_shared.double().abs() if ref.y_shared is not None else 0.0)
+    bound = wy * 2.0 ** -8 + mag * (k + 2) * 2.0 ** -23
+    assert bool(((bufs.out.double() - ref.out.double()).abs() <= bound).all())
+    mixed = types.SimpleNamespace(routing=bufs.routing, y_pair=ref.y_pair, y_shared=bufs.y_shared, out=bufs.out)
+    _check_layer(m, dl, w, logits, x, mixed, 1, TOL_INT8)
+
+
+@pytest.mark.parametrize("name,T,flags,over", [
+    ("sage_decode", 1, 0, {}),                                         # two-kernel decode layer
+    ("flash_next_decode", 2, 0, {}),                                   # with the shared expert
+    ("tiny", 16, 1, dict(hidden=512, inter=256, n_experts=8, top_k=2)),   # general decode stages
+    ("tiny", 20, 2, dict(hidden=512, inter=256, n_experts=8, top_k=2, qt_down=oracle.Q8_0)),  # int8, no MFMA
+])
+def test_pair_bf16_leaves_the_fp32_paths_unchanged(name, T, flags, over):
+    """Off the MFMA GEMMs the per-pair outputs stay fp32 (in the workspace, or in LDS in the
+    two-kernel decode layer): the flagged call gives the same out bits."""
+    m = qm()
+    _say("pair bf16, fp32 paths", name, T, flags, over)
+    dl, w = _layer(name, tokens=T, **over)
+    from quantized_moe_ffn_amd import layers
+    logits, x = layers.inputs_np(w, seed=12)
+    ref, bufs = _pair_bf16_pair(m, dl, logits, x, w.top_k, flags)
+    assert torch.equal(bufs.out, ref.out)
+
+
 def test_integer_exact_layer_is_bitwise():
     """Gate weights all 1/8, up row i all (i mod 4), down row o all (o mod 3), x = 1 (H = I = 256):
     g = 32 (so silu(g) = g in fp32), h_i = 8192 (i mod 4), y_o = (o mod 3) * 8192 * 384.  Every

@@ -322,3 +322,34 @@ def test_forward_router_checks_its_arguments_before_any_device_call():
     assert "w_router" in qm.moe_last_error()
     assert lib.moe_forward_router(ctypes.byref(L), P(4096), P(4096), P(4096), *args, P(1 << 20), fwd - 1, None) == 3
     assert "forward workspace" in qm.moe_last_error()
+
+
+def test_pair_bf16_flag_sizes_the_workspace_and_is_checked_before_any_device_call():
+    """MOE_FFN_PAIR_BF16 grows the layer call's workspace by the per-pair outputs: bf16 on
+    the int8 MFMA GEMMs, fp32 on the other paths.  Without it y_pair is required; unknown
+    flag bits, and the flag on moe_expert_ffn_q, are refused before anything is enqueued."""
+    lib = qm.load_library()
+    au = lambda n: (n + 255) // 256 * 256
+    L = _layer(H=2048, I=512, E=256)
+    T, k, f = 4096, 8, qm.MOE_FFN_PAIR_BF16
+    for sel, per in ((qm.MOE_FFN_INT8, 2), (qm.MOE_FFN_DECODE, 4)):
+        base = lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, sel)
+        assert lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, sel | f) - base == au(T * k * 2048 * per)
+    L8 = _layer(H=512, I=256, E=8, qd=qm.MOE_Q8_0)     # int8 path without the MFMA GEMMs
+    base = lib.moe_forward_workspace_bytes(ctypes.byref(L8), 20, 2, qm.MOE_FFN_INT8)
+    assert lib.moe_forward_workspace_bytes(ctypes.byref(L8), 20, 2, qm.MOE_FFN_INT8 | f) - base == au(20 * 2 * 512 * 4)
+    for bad in (3, 32, f | 4):
+        assert lib.moe_forward_workspace_bytes(ctypes.byref(L), T, k, bad) == 0
+    r = _routing_null()
+    P = ctypes.c_void_p
+    ws = lib.moe_forward_workspace_bytes(ctypes.byref(L), 1, k, 1 | f)
+    args = (ctypes.byref(L), P(4096), P(4096), 1, k, 1)
+    assert lib.moe_forward(*args, 1, ctypes.byref(r), None, None, None, P(16384), P(1 << 20), ws, None) == 1
+    assert "y_pair" in qm.moe_last_error()
+    assert lib.moe_forward(*args, 32, ctypes.byref(r), P(8192), None, None, P(16384), P(1 << 20), ws, None) == 1
+    assert "ffn_flags" in qm.moe_last_error()
+    assert lib.moe_forward_noalloc(*args, 2 | 64, ctypes.byref(r), None, None, None, P(16384), None) == 1
+    assert "ffn_flags" in qm.moe_last_error()
+    assert lib.moe_expert_ffn_q(ctypes.byref(L), ctypes.byref(r), 1, k, P(4096), None, None, 1 | f, P(8192), None,
+                                P(1 << 20), 1 << 20, None) == 1
+    assert "flags" in qm.moe_last_error()
