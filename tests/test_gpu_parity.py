@@ -350,6 +350,11 @@ def test_int8_prefill_chunk_full(name):
          qt_down=oracle.Q5_K),                                                       # Q5_K, 32-token tiles
     dict(hidden=768, inter=512, n_experts=10, top_k=3, tokens=24, qt_gate=oracle.Q5_1, qt_up=oracle.Q5_1,
          qt_down=oracle.Q5_1, shared=True),                                          # Q5_1 experts: in-register path
+    # past 256 pairs the layer call routes and quantises in one launch and the bucket scan writes
+    # the tile list: eight and sixteen keys per lane, shared-expert tiles, a token count not a
+    # multiple of four
+    dict(hidden=512, inter=256, n_experts=512, top_k=10, tokens=41, shared=True),
+    dict(hidden=256, inter=256, n_experts=1024, top_k=4, tokens=83),
 ])
 @pytest.mark.parametrize("fused", [True, False])
 def test_int8_ragged_shapes(over, fused):
