@@ -2,7 +2,9 @@
 tight serving loops) against moe_forward with a caller-owned workspace, through
 the C ABI.  The same kernels run on the same inputs, so the outputs must agree bit
 for bit; two calls in a row, the second smaller, check that the shared static
-scratch keeps no state that a later call depends on."""
+scratch keeps no state that a later call depends on.  With MOE_FFN_PAIR_BF16 the
+per-pair outputs live in the scratch too, and y_pair (filled with NaN) stays
+untouched by both calls."""
 import numpy as np
 import pytest
 
@@ -42,6 +44,8 @@ def _outputs(m, dl, w, logits, x, flags, noalloc):
     ("sage_decode", 1, 8, 2),            # two-kernel decode layer
     ("flash_next_decode", 1, 3, 1),      # with the shared expert, Q8_0 down
     ("sage_decode", 2, 300, 40),         # int8 MFMA path
+    ("sage_decode", 2 | 16, 200, 40),    # MOE_FFN_PAIR_BF16: bf16 per-pair outputs in the scratch
+    ("flash_next_decode", 1 | 16, 3, 1), # the flag on the decode layer: y_pair left untouched
 ])
 def test_noalloc_equals_forward_bitwise(name, flags, t1, t2):
     m = _qm()
