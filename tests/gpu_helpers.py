@@ -58,3 +58,10 @@ def oracle_shared(dl, hb, tokens, x, mode):
 # (oracle.int8_pair_candidates) and the best match against it.
 int8_pair_candidates = oracle.int8_pair_candidates
 best_candidate_err = oracle.best_candidate_err
+
+
+def bf16_rne(a):
+    """fp32 -> bf16 rounded to nearest, ties to even, widened back to fp32 (finite values)."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)

@@ -17,7 +17,7 @@ import pytest
 import oracle
 from quantized_moe_ffn_amd import synth
 
-from tests.gpu_helpers import TOL_DECODE, TOL_INT8, normwise_err, oracle_pairs, oracle_shared
+from tests.gpu_helpers import TOL_DECODE, TOL_INT8, bf16_rne, normwise_err, oracle_pairs, oracle_shared
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -135,4 +135,26 @@ def test_epilogue_is_gate_as_scale_plus_residual_bitwise(name, T, over, mode, fu
     bufs.out.copy_(rt)
     m.forward(dl.layer, lg, xt, w.top_k, bufs=bufs, flags=flags, fused=fused, residual=bufs.out, shared_gate=gw)
     m.moe_check_device_errors()
+    assert torch.equal(bufs.out, expect)
+
+
+def test_epilogue_on_the_bf16_hand_off_bitwise():
+    """With MOE_FFN_PAIR_BF16 on the int8 MFMA GEMMs (shared expert, gate and residual), the
+    layer call's out equals moe_combine_ep of the unflagged call's y_pair rounded to bf16 on the
+    host, with the same gate values and residual, bit for bit."""
+    m = qm()
+    name, T, over, _ = CASES[3]
+    _say("epilogue on the bf16 hand-off", name, T)
+    w, dl, logits, x, gate_w, resid = _case(name, T, over, seed=33)
+    lg, xt, gw, rt = _dev(logits), _dev(x), _dev(gate_w), _dev(resid)
+    plain = m.forward(dl.layer, lg, xt, w.top_k, flags=m.MOE_FFN_INT8)
+    s = torch.empty(T, dtype=torch.float32, device=DEV)
+    m.moe_shared_gate(xt, gw, s)
+    expect = torch.empty_like(plain.out)
+    m.moe_combine_ep(_dev(bf16_rne(plain.y_pair.cpu().numpy())), plain.routing.w, expect, plain.y_shared, None, s, rt)
+    flags = m.MOE_FFN_INT8 | m.MOE_FFN_PAIR_BF16
+    bufs = m.LayerBuffers(dl.layer, T, w.top_k, flags, device=DEV)
+    m.forward(dl.layer, lg, xt, w.top_k, bufs=bufs, flags=flags, residual=rt, shared_gate=gw)
+    m.moe_check_device_errors()
+    assert torch.equal(bufs.y_shared, plain.y_shared)
     assert torch.equal(bufs.out, expect)

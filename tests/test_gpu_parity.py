@@ -12,7 +12,7 @@ import pytest
 import oracle
 from quantized_moe_ffn_amd import synth
 
-from tests.gpu_helpers import TOL_DECODE, TOL_INT8, TOL_W, normwise_err, oracle_pairs, oracle_shared
+from tests.gpu_helpers import TOL_DECODE, TOL_INT8, TOL_W, bf16_rne, normwise_err, oracle_pairs, oracle_shared
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -386,13 +386,6 @@ def test_int8_determinism_and_batch_invariance():
 
 # --------------------------------------------------------------------------- MOE_FFN_PAIR_BF16
 
-def _bf16_rne(a):
-    """fp32 -> bf16 rounded to nearest, ties to even, widened back to fp32 (finite values)."""
-    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32)
-
-
 def _pair_bf16_pair(m, dl, logits, x, k, flags):
     """The layer call with and without MOE_FFN_PAIR_BF16 on the same inputs.  The flagged
     call gets a y_pair buffer full of a sentinel, which it must leave alone."""
@@ -428,7 +421,7 @@ def test_pair_bf16_int8_mfma_is_the_combine_of_rounded_pairs(name, over):
     from quantized_moe_ffn_amd import layers
     logits, x = layers.inputs_np(w, seed=11)
     ref, bufs = _pair_bf16_pair(m, dl, logits, x, w.top_k, m.MOE_FFN_INT8)
-    yb = torch.from_numpy(_bf16_rne(ref.y_pair.cpu().numpy())).to(DEV)
+    yb = torch.from_numpy(bf16_rne(ref.y_pair.cpu().numpy())).to(DEV)
     out_ref = torch.empty_like(ref.out)
     m.moe_combine(yb, ref.routing.w, out_ref, ref.y_shared)
     m.moe_check_device_errors()
