@@ -509,18 +509,22 @@ def test_fused_equals_separate_calls_bitwise_for_routing():
     assert torch.equal(a.routing.w, b.routing.w)
 
 
-def test_graph_replay_matches_eager():
-    """A captured stack of decode layers replays correctly, with eager work between replays."""
+@pytest.mark.parametrize("T,flags", [(1, 1), (300, 2), (300, 2 | 16)])
+def test_graph_replay_matches_eager(T, flags):
+    """A captured stack of layers replays correctly, with eager work between replays: the
+    two-kernel decode layer, and the int8 path (routing and quantisation in one launch, the
+    tile list from the bucket scan), also with the bf16 hand-off of MOE_FFN_PAIR_BF16."""
     m = qm()
     from quantized_moe_ffn_amd import layers
-    w = synth.WORKLOADS["sage_decode"]
+    _say("graph replay T=%d flags=%d" % (T, flags))
+    w = synth.Workload(**{**synth.WORKLOADS["sage_decode"].__dict__, "tokens": T})
     stack = [layers.make_layer(w, seed=9, index=l, device=DEV) for l in range(3)]
     ins = [layers.inputs_np(w, seed=9, index=l) for l in range(3)]
     lgs = [torch.from_numpy(a).to(DEV) for a, _ in ins]
     xs = [torch.from_numpy(b).to(DEV) for _, b in ins]
-    bufs = [m.LayerBuffers(dl.layer, 1, w.top_k, m.MOE_FFN_DECODE, device=DEV) for dl in stack]
+    bufs = [m.LayerBuffers(dl.layer, T, w.top_k, flags, device=DEV) for dl in stack]
     for l in range(3):
-        m.forward(stack[l].layer, lgs[l], xs[l], w.top_k, bufs[l], flags=m.MOE_FFN_DECODE)
+        m.forward(stack[l].layer, lgs[l], xs[l], w.top_k, bufs[l], flags=flags)
     torch.cuda.synchronize()
     eager = [b.out.clone() for b in bufs]
     g = torch.cuda.CUDAGraph()
@@ -529,7 +533,7 @@ def test_graph_replay_matches_eager():
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             for l in range(3):
-                m.forward(stack[l].layer, lgs[l], xs[l], w.top_k, bufs[l], flags=m.MOE_FFN_DECODE)
+                m.forward(stack[l].layer, lgs[l], xs[l], w.top_k, bufs[l], flags=flags)
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(3):
         for b in bufs:
