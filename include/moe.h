@@ -313,7 +313,9 @@ moe_status moe_forward_router(const moe_layer* L, const float* x, const float* w
  * moe_forward, without workspace/ws_bytes.  Rejects (MOE_ERR_WORKSPACE, nothing
  * enqueued) a call whose moe_forward_workspace_bytes exceeds the array: every
  * decode batch fits, and int8-path batches up to about a thousand tokens of a
- * hidden-2048 / top-8 / intermediate-512 layer.  Calls no allocating routine.
+ * hidden-2048 / top-8 / intermediate-512 layer (about two hundred with
+ * MOE_FFN_PAIR_BF16, whose per-pair outputs then take room in the array too).
+ * Calls no allocating routine.
  * Every call on one GPU uses that GPU's one array: calls that overlap in time
  * on one GPU (other streams, other host threads) race and give wrong results;
  * serialise them.  The array needs no clearing: each call writes every byte of
