@@ -27,8 +27,8 @@
 // Work.  A tile is (expert, 32*MTILES tokens of its bucket).  Gate/up:
 // workgroups of 8 waves take (tile, 256 rows of I); each wave owns 32 rows and
 // runs them through gate, then up (so SiLU(gate)*up and the requantisation of
-// h happen in registers).  Down: workgroups take (tile, 256 or 1024 rows of H),
-// each wave 32 rows per round.  The tile's int8 activations, their per-256
+// h happen in registers).  Down: workgroups of 4 waves take (tile, 128 or 512
+// rows of H), each wave 32 rows per round.  The tile's int8 activations, their per-256
 // scales and per-32 sums sit in LDS for the whole K loop; weights stream from
 // global memory into registers one 256-block ahead of use.  Work items are
 // laid out (expert, token tile, row block) and dealt to the 8 XCDs in
@@ -524,19 +524,24 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     }
 }
 
-constexpr int kDownRoundsMax = 4;  // 256-row rounds per down workgroup (large batches)
+constexpr int kDownRoundsMax = 4;  // 128-row rounds per down workgroup (large batches)
+// Waves of a down workgroup.  Four (not eight) let a CU hold three workgroups,
+// so each SIMD runs three waves instead of two: the down tile's LDS footprint
+// (~39 KB at 64 tokens) allows it, and its registers stay within 168.
+constexpr int kDownWaves = 4;
 
 // PAIR16: the per-pair outputs go to y_pair_bf16 as bf16 (nearest even), not to y_pair.
 template <int MTILES, int QD, bool PAIR16>
-__global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
+__global__ void __launch_bounds__(kDownWaves * kWave, MTILES == 1 ? 4 : 3) down_mfma_kernel(MfmaArgs a) {
     constexpr int MT = 32 * MTILES;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int s_src[MT], s_out[MT];
     __shared__ __attribute__((aligned(16))) float s_sc[MT];
 
     const int H = a.H, I = a.I, nsb = I / 256;
+    constexpr int RR = 32 * kDownWaves;  // output rows per round: 32 per wave
     const int R = a.down_rounds;
-    const int NB = (H / 256 + R - 1) / R;
+    const int NB = (H / RR + R - 1) / R;
     int u, ob;
     if (!work_item(a.n_tiles, NB, u, ob)) return;
     const int e = a.tile_e[u], m0 = a.tile_m0[u];
@@ -556,9 +561,9 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
     const QMat D = shared ? a.sdown : a.down;
     const int64_t eo = shared ? 0 : (int64_t)e;
     const int r0 = ob * R;
-    const int nr = min(R, H / 256 - r0);
-    const uint8_t* base = D.data + eo * D.expert_bytes + (int64_t)(r0 * 256 + wave * 32 + n) * D.row_bytes;
-    const int64_t round_stride = 256 * D.row_bytes;
+    const int nr = min(R, H / RR - r0);
+    const uint8_t* base = D.data + eo * D.expert_bytes + (int64_t)(r0 * RR + wave * 32 + n) * D.row_bytes;
+    const int64_t round_stride = (int64_t)RR * D.row_bytes;
     const int npairs = a.T * a.k;
 
     v16f acc[MTILES];
@@ -576,7 +581,7 @@ __global__ void __launch_bounds__(kMThreads) down_mfma_kernel(MfmaArgs a) {
         block_mma<MTILES, QD>(br, b, T, acc);
         if (b == nsb - 1) {
             apply_row_scale<MTILES>(T, acc);
-            const int o = (r0 + r) * 256 + wave * 32 + n;
+            const int o = (r0 + r) * RR + wave * 32 + n;
 #pragma unroll
             for (int mt = 0; mt < MTILES; ++mt) {
 #pragma unroll
@@ -646,6 +651,26 @@ int max_tiles(int T, int k, int E, int has_shared, int mt) {
 
 unsigned grid_for(int works) { return (unsigned)((works + kXcds - 1) / kXcds * kXcds); }
 
+template <int MTILES, int QD>
+hipError_t launch_down(const MfmaArgs& a, int maxt, hipStream_t s) {
+    constexpr int RR = 32 * kDownWaves;
+    // rounds of RR output rows per down workgroup: four amortise the tile's LDS
+    // load over 512 rows when there are work items to spare; small batches (a
+    // few tokens per expert, few tiles) take one round so that the grid covers
+    // the CUs
+    MfmaArgs d = a;
+    const int rounds_all = a.H / RR;
+    d.down_rounds =
+        (int64_t)maxt * ((rounds_all + kDownRoundsMax - 1) / kDownRoundsMax) >= 1024 ? kDownRoundsMax : 1;
+    const int nb_down = (rounds_all + d.down_rounds - 1) / d.down_rounds;
+    const dim3 gd(grid_for(maxt * nb_down));
+    if (a.y_pair_bf16)
+        down_mfma_kernel<MTILES, QD, true><<<gd, kDownWaves * kWave, tile_lds_bytes<MTILES>(a.I), s>>>(d);
+    else
+        down_mfma_kernel<MTILES, QD, false><<<gd, kDownWaves * kWave, tile_lds_bytes<MTILES>(a.I), s>>>(d);
+    return hipGetLastError();
+}
+
 template <int MTILES, int QG, int QD>
 hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     constexpr int MT = 32 * MTILES;
@@ -664,19 +689,7 @@ hipError_t launch_mfma_path(const MfmaArgs& a, hipStream_t s) {
     const size_t lds_gu = std::max(tile_lds_bytes<MTILES>(a.H), (size_t)MT * kHStride * sizeof(float));
     gateup_mfma_kernel<MTILES, QG><<<grid_for(maxt * (a.I / 256)), kMThreads, lds_gu, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // rounds of 256 output rows per down workgroup: four amortise the tile's LDS
-    // load over 1,024 rows when there are work items to spare; small batches (a
-    // few tokens per expert, few tiles) take one round so that the grid covers
-    // the CUs
-    MfmaArgs d = a;
-    d.down_rounds = (int64_t)maxt * ((a.H / 256 + kDownRoundsMax - 1) / kDownRoundsMax) >= 1024 ? kDownRoundsMax : 1;
-    const int nb_down = (a.H / 256 + d.down_rounds - 1) / d.down_rounds;
-    const dim3 gd(grid_for(maxt * nb_down));
-    if (a.y_pair_bf16)
-        down_mfma_kernel<MTILES, QD, true><<<gd, kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(d);
-    else
-        down_mfma_kernel<MTILES, QD, false><<<gd, kMThreads, tile_lds_bytes<MTILES>(a.I), s>>>(d);
-    return hipGetLastError();
+    return launch_down<MTILES, QD>(a, maxt, s);
 }
 
 template <int MTILES, int QG>

@@ -88,7 +88,7 @@ struct MfmaArgs {
     int32_t* tile_e;
     int32_t* tile_m0;
     int32_t* n_tiles;
-    int down_rounds;               // 256-row rounds per down workgroup (set by the launcher)
+    int down_rounds;               // 128-row rounds per down workgroup (set by the launcher)
     int xs_ready;                  // xs already holds the per-32 sums of xq (written with the codes)
     int tiles_ready;               // tile_e / tile_m0 / n_tiles already hold the tile list
     uint16_t* y_pair_bf16;         // non-null: y_pair is written here as bf16 (nearest even) instead
