@@ -294,18 +294,24 @@ __device__ __forceinline__ void load_tile(const int8_t* __restrict__ q, const fl
         const int c = tid % per_row, m0 = tid / per_row;
         if (m0 < rows_per_pass) {
             for (int mb = m0; mb < MT; mb += kBatch * rows_per_pass) {
+                // every load of the batch is issued before any is used: rows past
+                // the bucket load row 0 and store zeros (a select at the store,
+                // not a branch after each load, which would wait for it)
                 uint4 v[kBatch];
+                bool pad[kBatch];
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i) {
                     const int m = min(mb + i * rows_per_pass, MT - 1);
                     const int src = s_src[m];
+                    pad[i] = src < 0;
                     v[i] = *reinterpret_cast<const uint4*>(q + (int64_t)max(src, 0) * K + 16 * c);
-                    if (src < 0) v[i] = make_uint4(0, 0, 0, 0);
                 }
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i) {
                     const int m = mb + i * rows_per_pass;
-                    if (m < MT) *reinterpret_cast<uint4*>(lds_a + m * lda + 16 * c) = v[i];
+                    const uint32_t keep = pad[i] ? 0u : ~0u;
+                    const uint4 w = make_uint4(v[i].x & keep, v[i].y & keep, v[i].z & keep, v[i].w & keep);
+                    if (m < MT) *reinterpret_cast<uint4*>(lds_a + m * lda + 16 * c) = w;
                 }
             }
         }
@@ -326,16 +332,36 @@ __device__ __forceinline__ void load_tile(const int8_t* __restrict__ q, const fl
         for (int b = 0; b < nsb; ++b) xd_s[b * MT + tid] *= inv;
     }
     __syncthreads();
-    // per-32 values X*xd/s as fp16 hi/lo pairs: [m][0 .. K/32) hi, [m][K/32 .. 2K/32) lo
-    const int k32 = K / 32;
-    for (int idx = tid; idx < MT * k32; idx += nthr) {
-        const int m = idx / k32, c = idx - m * k32;
+    // per-32 values X*xd/s as fp16 hi/lo pairs: [m][0 .. K/32) hi, [m][K/32 .. 2K/32) lo.
+    // A thread takes the eight sums of one 256-block of one row (one 16-byte
+    // load; K/32 is a multiple of 8 and the rows start 16-byte aligned), all
+    // scaled by that block's xd/s.
+    const int k32 = K / 32, k256 = K / 256;
+    for (int idx = tid; idx < MT * k256; idx += nthr) {
+        const int m = idx / k256, b = idx - m * k256;
         const int src = s_src[m];
-        const float xv = src >= 0 ? (float)qs[(int64_t)src * k32 + c] : 0.0f;
-        const float v = xv * xd_s[(c >> 3) * MT + m];
-        const _Float16 vh = (_Float16)v;
-        xs_s[m * xs_ld + c] = __builtin_bit_cast(uint16_t, vh);
-        xs_s[m * xs_ld + k32 + c] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)vh));
+        const uint4 raw = *reinterpret_cast<const uint4*>(qs + (int64_t)max(src, 0) * k32 + 8 * b);
+        const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float sc = xd_s[b * MT + m];
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int16_t sv = (int16_t)(rw[t >> 1] >> (16 * (t & 1)));
+            const float xv = src >= 0 ? (float)sv : 0.0f;
+            const float v = xv * sc;
+            const _Float16 vh = (_Float16)v;
+            const uint32_t bh = __builtin_bit_cast(uint16_t, vh);
+            const uint32_t bl = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)vh));
+            if (t & 1) {
+                hi[t >> 1] |= bh << 16;
+                lo[t >> 1] |= bl << 16;
+            } else {
+                hi[t >> 1] = bh;
+                lo[t >> 1] = bl;
+            }
+        }
+        *reinterpret_cast<uint4*>(xs_s + m * xs_ld + 8 * b) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(xs_s + m * xs_ld + k32 + 8 * b) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
 }
 
