@@ -563,6 +563,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave, MTILES == 1 ? 4 : 3) down_
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int s_src[MT], s_out[MT];
     __shared__ __attribute__((aligned(16))) float s_sc[MT];
+    __shared__ __attribute__((aligned(16))) int s_off[MT];  // element offset of the row's output, -1 past the bucket
 
     const int H = a.H, I = a.I, nsb = I / 256;
     constexpr int RR = 32 * kDownWaves;  // output rows per round: 32 per wave
@@ -574,6 +575,13 @@ __global__ void __launch_bounds__(kDownWaves * kWave, MTILES == 1 ? 4 : 3) down_
     const bool shared = (e == a.E);
     tile_rows<MT>(a, e, m0, true, s_src, s_out);
     __syncthreads();
+    const int npairs = a.T * a.k;
+    // a tile is all routed pairs (rows of y_pair) or all shared-expert tokens
+    // (rows T*k + t, stored as rows t of y_shared)
+    if (threadIdx.x < MT) {
+        const int orow = s_out[threadIdx.x];
+        s_off[threadIdx.x] = orow >= 0 ? (orow - (shared ? npairs : 0)) * H : -1;
+    }
 
     int8_t* lds_a;
     float* hd_s;
@@ -590,7 +598,6 @@ __global__ void __launch_bounds__(kDownWaves * kWave, MTILES == 1 ? 4 : 3) down_
     const int nr = min(R, H / RR - r0);
     const uint8_t* base = D.data + eo * D.expert_bytes + (int64_t)(r0 * RR + wave * 32 + n) * D.row_bytes;
     const int64_t round_stride = (int64_t)RR * D.row_bytes;
-    const int npairs = a.T * a.k;
 
     v16f acc[MTILES];
 #pragma unroll
@@ -610,21 +617,33 @@ __global__ void __launch_bounds__(kDownWaves * kWave, MTILES == 1 ? 4 : 3) down_
             const int o = (r0 + r) * RR + wave * 32 + n;
 #pragma unroll
             for (int mt = 0; mt < MTILES; ++mt) {
+                // the output offsets of the lane's 16 rows (C layout: four runs
+                // of four consecutive rows), read together
+                int off[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int orow = s_out[c_row(mt, v, h)];
-                    if (orow >= 0) {
-                        if (orow < npairs) {
-                            if constexpr (PAIR16)
-                                a.y_pair_bf16[(uint32_t)(orow * H + o)] =
-                                    __builtin_bit_cast(uint16_t, (__bf16)acc[mt][v]);
-                            else
-                                a.y_pair[(uint32_t)(orow * H + o)] = acc[mt][v];
-                        } else
-                            a.y_shared[(uint32_t)((orow - npairs) * H + o)] = acc[mt][v];
-                    }
-                    acc[mt][v] = 0.0f;
+                for (int g = 0; g < 4; ++g) {
+                    const int4 o4 = *reinterpret_cast<const int4*>(s_off + mt * 32 + 8 * g + 4 * h);
+                    off[4 * g + 0] = o4.x;
+                    off[4 * g + 1] = o4.y;
+                    off[4 * g + 2] = o4.z;
+                    off[4 * g + 3] = o4.w;
                 }
+                if (shared) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (off[v] >= 0) a.y_shared[(uint32_t)(off[v] + o)] = acc[mt][v];
+                } else if constexpr (PAIR16) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (off[v] >= 0)
+                            a.y_pair_bf16[(uint32_t)(off[v] + o)] = __builtin_bit_cast(uint16_t, (__bf16)acc[mt][v]);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (off[v] >= 0) a.y_pair[(uint32_t)(off[v] + o)] = acc[mt][v];
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
             }
         }
     };
