@@ -842,6 +842,156 @@ __global__ void __launch_bounds__(kK2MaxThreads) dec_down_kernel(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Expert-grouped decode FFN: batches past the two-kernel layer (T*k > 64) on
+// fp32 activations.  The int8 path's tile list with kGrpTok pairs per tile
+// (tiles of one expert's bucket, then the shared expert's token tiles) drives
+// two kernels: a workgroup of the gate/up kernel streams a tile of the
+// expert's rows once and applies it to the tile's tokens (the shared-expert
+// body of K1 above), and a workgroup of the down kernel does the same with the
+// tile's h rows, writing y_pair / y_shared for the combine.  An expert shared
+// by several tokens of the batch is read once per tile of two of them, where
+// the two-kernel layer reads it once per (token, rank) pair.
+// ---------------------------------------------------------------------------
+struct GroupTiles {
+    const int32_t* tile_e;
+    const int32_t* tile_m0;
+    const int32_t* n_tiles;
+    const int32_t* offset;
+    const int32_t* pair;
+};
+
+// Pairs per tile of the expert-grouped kernels.  Two keep a wave's activation
+// slices (32 floats per token) and its weight slices within ~120 VGPRs, so a
+// SIMD holds four waves; four tokens per tile took 205-276 VGPRs.
+constexpr int kGrpTok = 2;
+
+// The tile's tokens (t < nt) and h rows; false (uniform across the workgroup)
+// when the tile is past the list, empty, or its bucket entries are corrupt.
+__device__ __forceinline__ bool group_tile(const DecArgs& a, const GroupTiles& g, int y, int& e, bool& shared,
+                                           int& nt, int (&tok)[kGrpTok], int (&hrow)[kGrpTok]) {
+    if (y >= *g.n_tiles) return false;
+    e = g.tile_e[y];
+    const int m0 = g.tile_m0[y];
+    const int P = a.T * a.k;
+    shared = e == a.E;
+    if (shared) {
+        nt = min(kGrpTok, a.T - m0);
+        if (m0 < 0 || nt <= 0) return false;
+#pragma unroll
+        for (int t = 0; t < kGrpTok; ++t) {
+            tok[t] = m0 + min(t, nt - 1);
+            hrow[t] = P + tok[t];
+        }
+        return true;
+    }
+    if (e < 0 || e >= a.E) {
+        if (threadIdx.x == 0) raise_error(kErrExpertRange);
+        return false;
+    }
+    const int p0 = g.offset[e], p1 = g.offset[e + 1];
+    if (p0 < 0 || p1 < p0 || p1 > P || m0 < 0) {
+        if (threadIdx.x == 0) raise_error(kErrPairRange);
+        return false;
+    }
+    nt = min(kGrpTok, p1 - p0 - m0);
+    if (nt <= 0) return false;
+#pragma unroll
+    for (int t = 0; t < kGrpTok; ++t) {
+        const int p = g.pair[p0 + m0 + min(t, nt - 1)];
+        if (p < 0 || p >= P) {
+            if (threadIdx.x == 0) raise_error(kErrPairRange);
+            return false;
+        }
+        tok[t] = p / a.k;
+        hrow[t] = p;
+    }
+    return true;
+}
+
+template <int NB, int PASSES, int QG>
+__global__ void __launch_bounds__((K1Shape<NB, PASSES>::THREADS)) dec_gateup_grouped_kernel(DecArgs a, GroupTiles g) {
+    using S = K1Shape<NB, PASSES>;
+    constexpr int TT = kGrpTok;
+    __shared__ float s_part[S::IN_WAVE ? 1 : (2 * TT * S::P * S::GROUPS)];
+    int e, nt, tok[TT], hrow[TT];
+    bool shared;
+    if (!group_tile(a, g, blockIdx.y, e, shared, nt, tok, hrow)) return;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int sl = ((wave % S::W) * kWave + lane) % S::SLICES;
+    const int clo = kslice_col_lo<QG>(sl), chi = kslice_col_hi<QG>(sl);
+    float4 xl4[TT][4], xh4[TT][4];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) load_x_slice<TT>(a, tok[t], clo, chi, xl4[t], xh4[t]);
+    dec_gateup_body<NB, PASSES, TT, QG>(a, shared ? a.sgate : a.gate, shared ? a.sup : a.up, shared ? 0 : e, nt,
+                                        hrow, xl4, xh4, s_part);
+}
+
+// Down: four waves, each PS passes of RP = 64/NS rows (NS lanes per row), all
+// of its weight loads in flight before the tile's h slices are read.
+constexpr int kGrpDownWaves = 4;
+
+template <int QD, int NS, int PS>
+__global__ void __launch_bounds__(kGrpDownWaves * kWave) dec_down_grouped_kernel(DecArgs a, GroupTiles g) {
+    constexpr int RP = kWave / NS;
+    constexpr int TT = kGrpTok;
+    int e, nt, tok[TT], hrow[TT];
+    bool shared;
+    if (!group_tile(a, g, blockIdx.y, e, shared, nt, tok, hrow)) return;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int rr = lane / NS, sl = lane % NS;
+    const SliceKit kit = kslice_kit<QD>(sl);
+    const int c_lo = kslice_col_lo<QD>(sl), c_hi = kslice_col_hi<QD>(sl);
+    const QMat D = shared ? a.sdown : a.down;
+    const uint8_t* Db = D.data + (int64_t)(shared ? 0 : e) * D.expert_bytes + kslice_block_off<QD>(sl);
+    const int o0 = (blockIdx.x * kGrpDownWaves + wave) * RP * PS;
+    KSlice rk[PS];
+#pragma unroll
+    for (int pp = 0; pp < PS; ++pp) {
+        const int o = o0 + pp * RP + rr;
+        kslice_load<QD>(Db + (int64_t)(o < a.H ? o : a.H - 1) * D.row_bytes, sl, rk[pp]);
+    }
+    float4 hl4[TT][4], hh4[TT][4];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const float4* pl = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[t] * a.I + c_lo);
+        const float4* ph = reinterpret_cast<const float4*>(a.h + (int64_t)hrow[t] * a.I + c_hi);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            hl4[t][v] = pl[v];
+            hh4[t][v] = ph[v];
+        }
+    }
+    float hl[TT][16], hh[TT][16], shl[TT], shh[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        unpack_f4<TT>(hl4[t], hl[t]);
+        unpack_f4<TT>(hh4[t], hh[t]);
+        shl[t] = shh[t] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            shl[t] += hl[t][j];
+            shh[t] += hh[t][j];
+        }
+    }
+#pragma unroll
+    for (int pp = 0; pp < PS; ++pp) {
+        const int o = o0 + pp * RP + rr;
+        float acc[TT];
+        kslice_dot<QD, TT>(rk[pp], kit, nt, hl, hh, shl, shh, acc);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            acc[t] = segment_sum<NS>(acc[t]);
+            if (t < nt && sl == NS - 1 && o < a.H) {
+                if (shared)
+                    a.y_shared[(int64_t)tok[t] * a.H + o] = acc[t];
+                else
+                    a.y_pair[(int64_t)hrow[t] * a.H + o] = acc[t];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 namespace {
@@ -1002,6 +1152,90 @@ hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s) {
     if (a.down.qtype == kQ5_K) return launch_k2_q<kQ5_K>(a, s);
     if (a.down.qtype == kQ5_1) return launch_k2_q<kQ5_1>(a, s);
     return launch_k2_q<kQ8_0>(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// The expert-grouped path's launcher.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kGrpPasses = 2;     // gate/up rows per wave (row passes)
+constexpr int kGrpDownPasses = 2; // down row passes per wave
+
+int grp_max_tiles(int T, int k, int E, int has_shared) {
+    const int P = T * k;
+    return (P + kGrpTok - 1) / kGrpTok + (E < P ? E : P) + (has_shared ? (T + kGrpTok - 1) / kGrpTok : 0);
+}
+
+template <int NB, int QG>
+hipError_t launch_grp_gateup(const DecArgs& a, const GroupTiles& g, int maxt, hipStream_t s) {
+    using S = K1Shape<NB, kGrpPasses>;
+    const dim3 grid((a.I + S::ROWS - 1) / S::ROWS, maxt);
+    dec_gateup_grouped_kernel<NB, kGrpPasses, QG><<<grid, S::THREADS, 0, s>>>(a, g);
+    return hipGetLastError();
+}
+
+template <int QD>
+hipError_t launch_grp_down(const DecArgs& a, const GroupTiles& g, int maxt, hipStream_t s) {
+    constexpr int NS = 16, RO = kGrpDownWaves * (kWave / NS) * kGrpDownPasses;
+    const dim3 grid((a.H + RO - 1) / RO, maxt);
+    dec_down_grouped_kernel<QD, NS, kGrpDownPasses><<<grid, kGrpDownWaves * kWave, 0, s>>>(a, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Shapes of the expert-grouped path: H = 2,048 or 2,560; Q4_K or Q5_K gate/up
+// (the same for both); Q4_K, Q5_K or Q8_0 down with I = 512; batches past the
+// two-kernel layer (T*k > 64).
+bool dec_grouped_supported(int T, int k, int H, int I, int qg, int qu, int qd) {
+    if (T < 1 || T * k <= kDecMaxPairs) return false;
+    if (!(qg == kQ4_K || qg == kQ5_K) || qu != qg) return false;
+    if (!(qd == kQ4_K || qd == kQ5_K || qd == kQ8_0)) return false;
+    return (H == 2048 || H == 2560) && I == 512;
+}
+
+size_t dec_grouped_tiles_bytes(int T, int k, int E, int has_shared) {
+    return 2 * sizeof(int32_t) * (size_t)grp_max_tiles(T, k, E, has_shared) + 256;
+}
+
+hipError_t launch_dec_grouped(const FfnArgs& f, hipStream_t s) {
+    const int maxt = grp_max_tiles(f.T, f.k, f.E, f.has_shared);
+    const size_t half = (dec_grouped_tiles_bytes(f.T, f.k, f.E, f.has_shared) - 256) / 2;
+    int32_t* tile_e = f.tiles;
+    int32_t* tile_m0 = f.tiles + half / sizeof(int32_t);
+    int32_t* n_tiles = f.tiles + 2 * (half / sizeof(int32_t));
+    const TileList tl{tile_e, tile_m0, n_tiles, kGrpTok, maxt, f.T, f.has_shared};
+    mfma_tiles_kernel<<<1, 1024, 0, s>>>(f.count, f.E, f.T * f.k, tl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    DecArgs a{};
+    a.x = f.x;
+    a.gate = f.gate;
+    a.up = f.up;
+    a.down = f.down;
+    a.sgate = f.sgate;
+    a.sup = f.sup;
+    a.sdown = f.sdown;
+    a.has_shared = f.has_shared;
+    a.T = f.T;
+    a.E = f.E;
+    a.k = f.k;
+    a.H = f.H;
+    a.I = f.I;
+    a.h = f.h;
+    a.y_pair = f.y_pair;
+    a.y_shared = f.y_shared;
+    const GroupTiles g{tile_e, tile_m0, n_tiles, f.offset, f.pair};
+    if (f.H == 2048)
+        e = f.gate.qtype == kQ5_K ? launch_grp_gateup<8, kQ5_K>(a, g, maxt, s) : launch_grp_gateup<8, kQ4_K>(a, g, maxt, s);
+    else
+        e = f.gate.qtype == kQ5_K ? launch_grp_gateup<10, kQ5_K>(a, g, maxt, s)
+                                  : launch_grp_gateup<10, kQ4_K>(a, g, maxt, s);
+    if (e != hipSuccess) return e;
+    if (f.down.qtype == kQ5_K) return launch_grp_down<kQ5_K>(a, g, maxt, s);
+    if (f.down.qtype == kQ8_0) return launch_grp_down<kQ8_0>(a, g, maxt, s);
+    return launch_grp_down<kQ4_K>(a, g, maxt, s);
 }
 
 }  // namespace moe

@@ -340,6 +340,11 @@ hipError_t launch_down(const FfnArgs& a, int hmode, hipStream_t s) {
 }
 
 hipError_t launch_ffn_decode(const FfnArgs& a, hipStream_t s) {
+    // batches past the two-kernel layer: the expert-grouped kernels when the
+    // shape is theirs (the caller gave them their tile-list workspace)
+    if (a.tiles && ((uintptr_t)a.x % 16) == 0 &&
+        dec_grouped_supported(a.T, a.k, a.H, a.I, a.gate.qtype, a.up.qtype, a.down.qtype))
+        return launch_dec_grouped(a, s);
     hipError_t e = launch_gateup(a, 0, s);
     if (e != hipSuccess) return e;
     return launch_down(a, 0, s);

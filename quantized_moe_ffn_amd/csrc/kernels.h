@@ -123,6 +123,12 @@ constexpr int kDecRouteTabBytes = 4096;
 bool dec_fused_supported(int T, int k, int H, int I, int qg, int qu, int qd);
 hipError_t launch_dec_fused(const DecArgs& a, hipStream_t s);
 
+// The expert-grouped decode FFN (batches past the two-kernel layer): tile list
+// (in f.tiles, dec_grouped_tiles_bytes), gate/up, down; y_pair / y_shared out.
+bool dec_grouped_supported(int T, int k, int H, int I, int qg, int qu, int qd);
+size_t dec_grouped_tiles_bytes(int T, int k, int E, int has_shared);
+hipError_t launch_dec_grouped(const FfnArgs& f, hipStream_t s);
+
 // The int8 path's other two prologue stages, carried by the routing launches of
 // a layer call: quantisation of x (launch_quantize_act's rule and outputs) and,
 // with tiles.mt > 0, the MFMA tile list (written from the bucket counts).

@@ -158,6 +158,7 @@ moe::QMat to_qmat(const moe_qmatrix& m) {
 struct FfnWorkspace {
     size_t h, hq, hd, xs, hs, tiles, total;
     bool mfma;
+    bool grouped;   // decode path, expert-grouped kernels: tiles holds their tile list
 };
 
 // The int8 path runs as grouped int8 MFMA GEMMs for k-quant experts (Q4_K or
@@ -171,9 +172,15 @@ FfnWorkspace ffn_ws_layout(const moe_layer* L, int T, int k, uint32_t path) {
     const size_t rows = (size_t)T * k + (L->has_shared ? T : 0);
     FfnWorkspace w{};
     w.mfma = path == MOE_FFN_INT8 && int8_uses_mfma(L) && moe::mfma_rows_fit(T, k, L->hidden, L->inter);
+    w.grouped = path == MOE_FFN_DECODE && moe::dec_grouped_supported(T, k, L->hidden, L->inter, L->gate.qtype,
+                                                                      L->up.qtype, L->down.qtype);
     size_t off = 0;
     w.h = 0;
     if (!w.mfma) off += align_up(rows * L->inter * sizeof(float), 256);
+    if (w.grouped) {
+        w.tiles = off;
+        off += align_up(moe::dec_grouped_tiles_bytes(T, k, L->n_experts, L->has_shared ? 1 : 0), 256);
+    }
     w.hq = off;
     w.hd = off;
     if (path == MOE_FFN_INT8) {
@@ -200,7 +207,7 @@ void set_ffn_ws(moe::FfnArgs& a, char* base, const FfnWorkspace& w) {
     a.hd = (float*)(base + w.hd);
     a.xs = w.mfma ? (int16_t*)(base + w.xs) : nullptr;
     a.hs = w.mfma ? (int16_t*)(base + w.hs) : nullptr;
-    a.tiles = w.mfma ? (int32_t*)(base + w.tiles) : nullptr;
+    a.tiles = (w.mfma || w.grouped) ? (int32_t*)(base + w.tiles) : nullptr;
 }
 
 struct ForwardWorkspace {

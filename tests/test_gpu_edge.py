@@ -247,3 +247,53 @@ def test_plain_softmax_and_shared_scale_through_the_layer(T, path, fused):
     e = normwise_err(bufs.out.cpu().numpy(), out)
     _say("  plain softmax + shared scale, out err max %.3e" % e.max())
     assert e.max() <= tol
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name,T,over", [
+    ("sage_decode", 9, {}),                                  # T*k = 72: just past the two-kernel layer
+    ("sage_decode", 40, {}),                                 # 320 pairs: routed through the bucket kernels
+    ("sage_decode", 64, dict(n_experts=16)),                 # ~32 pairs per expert: eight tiles of four each
+    ("sage_decode_q5k", 16, {}),                             # Q5_K experts
+    ("flash_next_decode", 12, dict(n_experts=64)),           # shared expert (three token tiles), Q8_0 down, H 2560
+])
+def test_decode_batches_past_eight_tokens_expert_grouped(name, T, over, fused):
+    """Decode batches past the two-kernel layer (T*k > 64) on the expert-grouped kernels:
+    each tile of four pairs of one expert streams that expert's rows once.  Against the
+    oracle, on the layer call (fused) and the separate calls."""
+    m = qm()
+    _say("decode batch, expert-grouped", name, T, over, fused)
+    from quantized_moe_ffn_amd import layers
+    w = synth.Workload(**{**synth.WORKLOADS[name].__dict__, **over, "tokens": T})
+    dl = layers.make_layer(w, seed=19, index=0, device=DEV)
+    logits, x = layers.inputs_np(w, seed=19)
+    _check(m, dl, w, logits, x, m.MOE_FFN_DECODE, fused, TOL_DECODE)
+
+
+@pytest.mark.parametrize("name,T,over", [
+    ("sage_decode", 24, {}),
+    ("sage_decode_q5k", 12, {}),
+])
+def test_expert_grouped_rows_equal_the_two_kernel_layer_bitwise(name, T, over):
+    """On the Sage-like shape (H 2,048: a row's 64 slices in one wave; Q4_K or Q5_K down) a
+    token's per-pair outputs and layer output on the expert-grouped kernels equal, bit for
+    bit, those of the two-kernel layer run on that token alone: both take the same per-lane
+    slices, the same per-token dot products and lane sums in the same order, and the
+    combine in slot order.  (The Q8_0 dot and the five-wave rows of H 2,560 are compiled
+    with other fused multiply-adds in the two kernels' instances and agree to a few ulps;
+    those shapes are checked against the oracle above.)"""
+    m = qm()
+    _say("expert-grouped vs two-kernel layer", name, T, over)
+    from quantized_moe_ffn_amd import layers
+    w = synth.Workload(**{**synth.WORKLOADS[name].__dict__, **over, "tokens": T})
+    dl = layers.make_layer(w, seed=20, index=0, device=DEV)
+    logits, x = layers.inputs_np(w, seed=20)
+    big = _forward(m, dl, logits, x, w.top_k, m.MOE_FFN_DECODE, True)
+    k = w.top_k
+    for t in (0, T // 2, T - 1):
+        one = _forward(m, dl, logits[t:t + 1], x[t:t + 1], k, m.MOE_FFN_DECODE, True)
+        assert torch.equal(big.routing.idx[t], one.routing.idx[0]), t
+        assert torch.equal(big.y_pair[t * k:(t + 1) * k].view(torch.int32), one.y_pair.view(torch.int32)), t
+        if w.shared:
+            assert torch.equal(big.y_shared[t].view(torch.int32), one.y_shared[0].view(torch.int32)), t
+        assert torch.equal(big.out[t].view(torch.int32), one.out[0].view(torch.int32)), t
