@@ -76,8 +76,11 @@ typedef enum moe_status {
  * Q4_K and Q5_K banks must be 16-byte aligned, Q5_1 banks 8-byte aligned,
  * Q8_0 banks 2-byte aligned.  The two-kernel decode layer takes gate/up in
  * any of the four formats (one format for both) with down in any of them;
- * the int8 MFMA GEMMs take Q4_K or Q5_K gate/up with Q4_K or Q5_K down; other
- * mixes run on the general kernels of the chosen path. */
+ * the int8 MFMA GEMMs take Q4_K or Q5_K gate/up with Q4_K or Q5_K down; past
+ * eight tokens (T*k > 64) the decode path's expert-grouped kernels take Q4_K or
+ * Q5_K gate/up with Q4_K, Q5_K or Q8_0 down at H = 2048 or 2560, I = 512
+ * (16-byte aligned x); other mixes run on the general kernels of the chosen
+ * path. */
 enum { MOE_Q5_1 = 7, MOE_Q8_0 = 8, MOE_Q4_K = 12, MOE_Q5_K = 13 };
 
 /* moe_route_topk flags */
