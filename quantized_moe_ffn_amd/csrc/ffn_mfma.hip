@@ -45,6 +45,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -149,8 +150,9 @@ __device__ __forceinline__ void load_block(const uint8_t* blk, int h, BlockRegs&
 // and flipping bit 7 of every byte (the two's complement of the sum minus
 // 128).  The 16*sc*X_j it takes away comes back through the min-term MFMA,
 // whose weight side becomes 16*d*sc_j - dmin*m_j.
-template <int MTILES, int QT>
+template <int MTILES, int QT, bool RANK1>
 __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const TileLds& T, v16f (&out)[MTILES]) {
+    static_assert(MTILES == 1 || MTILES == 2, "tiles of 32 or 64 rows");
     constexpr int MT = 32 * MTILES;
     const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 31, h = lane >> 5;
@@ -234,19 +236,39 @@ __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const Tile
         }
     }
 
-    // main term: out += (acc_l + 8 acc_h) * d * xd
+    // main term: out += (acc_l + 8 acc_h) * (d * xd).  RANK1: the products
+    // d * xd of the lane's row and the tile's rows come from one rank-1 MFMA
+    // (v_mfma_f32_32x32x1f32: two 32x32 blocks, K = 1; block mt takes xd of its
+    // 32 rows from lanes 32*mt .. 32*mt + 31 and d of row n from lane n + 32*mt,
+    // and returns d * xd, rounded once, in the C layout of registers
+    // 16*mt .. 16*mt + 15; with one tile, block 1 repeats block 0, unused).
+    // Otherwise each lane multiplies them itself, reading xd from LDS.
     const float d = q4k_d(hd);
+    if constexpr (RANK1) {
+        const float xa = T.xd[b * MT + (MTILES == 2 ? lane : n)];
+        const v32f z32 = {};
+        const v32f dx = __builtin_amdgcn_mfma_f32_32x32x1f32(xa, d, z32, 0, 0, 0);
 #pragma unroll
-    for (int mt = 0; mt < MTILES; ++mt) {
+        for (int mt = 0; mt < MTILES; ++mt) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 x4 = *reinterpret_cast<const float4*>(T.xd + b * MT + mt * 32 + 8 * g + 4 * h);
-            const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int v = 4 * g + r;
+            for (int v = 0; v < 16; ++v) {
                 const int sm = accl[mt][v] + (acch[mt][v] << 3);
-                out[mt][v] = fmaf((float)sm, d * xv[r], out[mt][v]);
+                out[mt][v] = fmaf((float)sm, dx[16 * mt + v], out[mt][v]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MTILES; ++mt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 x4 = *reinterpret_cast<const float4*>(T.xd + b * MT + mt * 32 + 8 * g + 4 * h);
+                const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int v = 4 * g + r;
+                    const int sm = accl[mt][v] + (acch[mt][v] << 3);
+                    out[mt][v] = fmaf((float)sm, d * xv[r], out[mt][v]);
+                }
             }
         }
     }
@@ -459,7 +481,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     };
     const int steps = 2 * nsb;
     auto step = [&](const BlockRegs& br, int sx) {
-        block_mma<MTILES, QG>(br, sx >= nsb ? sx - nsb : sx, T, acc);
+        block_mma<MTILES, QG, true>(br, sx >= nsb ? sx - nsb : sx, T, acc);
         if (sx == nsb - 1) {
             apply_row_scale<MTILES>(T, acc);
 #pragma unroll
@@ -611,7 +633,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave, MTILES == 1 ? 4 : 3) down_
     const int steps = nr * nsb;
     auto step = [&](const BlockRegs& br, int sx) {
         const int r = sx / nsb, b = sx - r * nsb;
-        block_mma<MTILES, QD>(br, b, T, acc);
+        block_mma<MTILES, QD, false>(br, b, T, acc);
         if (b == nsb - 1) {
             apply_row_scale<MTILES>(T, acc);
             const int o = (r0 + r) * RR + wave * 32 + n;
