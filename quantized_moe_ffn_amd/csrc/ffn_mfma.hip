@@ -150,7 +150,14 @@ __device__ __forceinline__ void load_block(const uint8_t* blk, int h, BlockRegs&
 // and flipping bit 7 of every byte (the two's complement of the sum minus
 // 128).  The 16*sc*X_j it takes away comes back through the min-term MFMA,
 // whose weight side becomes 16*d*sc_j - dmin*m_j.
-template <int MTILES, int QT, bool RANK1>
+// How a block's products d*xd (the lane's row d against the tile rows' xd) are formed.
+enum DxMode : int {
+    kDxLanes = 0,      // each lane multiplies them, reading xd from LDS
+    kDxRank1Pair = 1,  // one v_mfma_f32_32x32x1f32 for both 32-row tiles (32 result registers)
+    kDxRank1Tile = 2,  // one v_mfma_f32_32x32x2f32 per tile (16 result registers)
+};
+
+template <int MTILES, int QT, int DX>
 __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const TileLds& T, v16f (&out)[MTILES]) {
     static_assert(MTILES == 1 || MTILES == 2, "tiles of 32 or 64 rows");
     constexpr int MT = 32 * MTILES;
@@ -236,15 +243,29 @@ __device__ __forceinline__ void block_mma(const BlockRegs& br, int b, const Tile
         }
     }
 
-    // main term: out += (acc_l + 8 acc_h) * (d * xd).  RANK1: the products
-    // d * xd of the lane's row and the tile's rows come from one rank-1 MFMA
-    // (v_mfma_f32_32x32x1f32: two 32x32 blocks, K = 1; block mt takes xd of its
-    // 32 rows from lanes 32*mt .. 32*mt + 31 and d of row n from lane n + 32*mt,
-    // and returns d * xd, rounded once, in the C layout of registers
-    // 16*mt .. 16*mt + 15; with one tile, block 1 repeats block 0, unused).
-    // Otherwise each lane multiplies them itself, reading xd from LDS.
+    // main term: out += (acc_l + 8 acc_h) * (d * xd).  The products d * xd
+    // form an outer product, which a rank-1 MFMA returns in the C layout of
+    // the int32 accumulators, each product one fp32 multiply rounded once (the
+    // bits of the lane's own d * xd).  kDxRank1Pair: v_mfma_f32_32x32x1f32, two
+    // 32x32 blocks with K = 1; block mt takes xd of its 32 rows from lanes
+    // 32*mt .. 32*mt + 31 and d of row n from lane n + 32*mt, into registers
+    // 16*mt .. 16*mt + 15 (with one tile, block 1 repeats block 0, unused).
+    // kDxRank1Tile: v_mfma_f32_32x32x2f32 per tile, K = 2 with the second K
+    // slice (lanes 32..63) zero, so only 16 result registers are live at once.
     const float d = q4k_d(hd);
-    if constexpr (RANK1) {
+    if constexpr (DX == kDxRank1Tile) {
+        const v16f z16 = {};
+#pragma unroll
+        for (int mt = 0; mt < MTILES; ++mt) {
+            const float xa = h ? 0.0f : T.xd[b * MT + mt * 32 + n];
+            const v16f dx = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, h ? 0.0f : d, z16, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int sm = accl[mt][v] + (acch[mt][v] << 3);
+                out[mt][v] = fmaf((float)sm, dx[v], out[mt][v]);
+            }
+        }
+    } else if constexpr (DX == kDxRank1Pair) {
         const float xa = T.xd[b * MT + (MTILES == 2 ? lane : n)];
         const v32f z32 = {};
         const v32f dx = __builtin_amdgcn_mfma_f32_32x32x1f32(xa, d, z32, 0, 0, 0);
@@ -481,7 +502,7 @@ __global__ void __launch_bounds__(kMThreads) gateup_mfma_kernel(MfmaArgs a) {
     };
     const int steps = 2 * nsb;
     auto step = [&](const BlockRegs& br, int sx) {
-        block_mma<MTILES, QG, true>(br, sx >= nsb ? sx - nsb : sx, T, acc);
+        block_mma<MTILES, QG, kDxRank1Pair>(br, sx >= nsb ? sx - nsb : sx, T, acc);
         if (sx == nsb - 1) {
             apply_row_scale<MTILES>(T, acc);
 #pragma unroll
@@ -633,7 +654,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave, MTILES == 1 ? 4 : 3) down_
     const int steps = nr * nsb;
     auto step = [&](const BlockRegs& br, int sx) {
         const int r = sx / nsb, b = sx - r * nsb;
-        block_mma<MTILES, QD, false>(br, b, T, acc);
+        block_mma<MTILES, QD, MTILES == 2 ? kDxRank1Tile : kDxLanes>(br, b, T, acc);
         if (b == nsb - 1) {
             apply_row_scale<MTILES>(T, acc);
             const int o = (r0 + r) * RR + wave * 32 + n;
